@@ -1,0 +1,194 @@
+// CPU oracle for the submanifold sparse 3D convolution.
+//
+// TEST INFRASTRUCTURE. Only the tests, the package entry's smoke check and the
+// benchmark's CPU-baseline leg load this code. It is deliberately plain and slow,
+// and it shares no code, header, table or constant with the HIP library.
+//
+// What it computes, and where the pages define it:
+//   * The operator: a spatial hash of the active voxels; for every kernel
+//     position the neighbour features are gathered, multiplied by that
+//     position's weights and added into the output of the voxel -- "Running
+//     TRELLIS.2 on a Mac (1/3)", section "Swapping out the CUDA libraries one at
+//     a time", sparse 3D convolution paragraph. The same sum as a gather-GEMM over
+//     a neighbour table built once per resolution level -- "Porting TRELLIS.2
+//     From Python to Rust and Metal", section V.
+//   * Output only at active sites ("submanifold"; features stay sparse) --
+//     mlx-diffuser TRELLIS guide, section "Why it fits better on a Mac".
+//   * Coordinates are (b, x, y, z) integer rows; features are [N, C] rows --
+//     startup packet (page 5), section 5, parity fixture table, rows B-D.
+//   * Weights are tap-major [Kvol = 27, C_in, C_out], reshaped from the on-disk
+//     (C_out, Kd, Kh, Kw, C_in) layout, so tap k = 9*Kd + 3*Kh + Kw -- startup
+//     packet, section 5 (conv conventions table and notes) and section 8.
+//
+// Readings where the pages are silent (each also listed in the design notes):
+//   * Kd, Kh, Kw run along x, y, z in the order the coordinates list them, and
+//     tap (Kd, Kh, Kw) reads the voxel at (x + Kd - 1, y + Kh - 1, z + Kw - 1):
+//     cross-correlation, the same as a dense 3x3x3 convolution with zero padding
+//     of 1 evaluated at the active sites. Agreement with TRELLIS's own sign
+//     convention is "parity unpinned": no TRELLIS layer or fixture is available.
+//   * Neighbours exist only inside the same batch index b; a neighbour outside
+//     [0, 2^16) on any axis does not exist (zero padding).
+//   * Every coordinate component must lie in [0, 2^16); a repeated coordinate
+//     is an error (a sparse tensor's coordinates form a set).
+//
+// Arithmetic: inputs are widened exactly to double by the caller; every output
+// y[i, co] = sum over k = 0..26 with nbr[i][k] >= 0, then over ci = 0..C_in-1,
+// of W[k, ci, co] * x[nbr[i][k], ci], accumulated in double in exactly that
+// (k, ci) order and never rounded.
+#include <algorithm>
+#include <climits>
+#include <cstdint>
+#include <cstring>
+#include <unordered_map>
+#include <vector>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+namespace {
+
+constexpr int kOk = 0;
+constexpr int kErrInvalid = -1;
+constexpr int kErrCoordRange = -2;
+constexpr int kErrDuplicate = -3;
+
+constexpr int64_t kAxisLimit = int64_t(1) << 16;
+
+// Plain positional packing of (b, x, y, z), 16 bits each.
+inline uint64_t pack_key(int64_t b, int64_t x, int64_t y, int64_t z) {
+  return (((uint64_t(b) * kAxisLimit + uint64_t(x)) * kAxisLimit + uint64_t(y)) * kAxisLimit) +
+         uint64_t(z);
+}
+
+inline bool in_range(int64_t v) { return v >= 0 && v < kAxisLimit; }
+
+struct Table {
+  std::unordered_map<uint64_t, int32_t> map;
+  std::vector<int32_t> coords;  // copy of the caller's [n, 4] rows
+  int64_t n = 0;
+};
+
+// Tap k -> offset (dx, dy, dz), each in {-1, 0, 1}.
+inline void tap_offset(int k, int& dx, int& dy, int& dz) {
+  dx = k / 9 - 1;
+  dy = (k / 3) % 3 - 1;
+  dz = k % 3 - 1;
+}
+
+}  // namespace
+
+extern "C" {
+
+// Builds the coordinate -> row map, inserting rows in caller order. Returns 0,
+// -2 for a component outside [0, 2^16), -3 for a repeated coordinate, -1 for
+// bad arguments. On success *out receives a handle for oc_free.
+int oc_build(const int32_t* coords, int64_t n, void** out) {
+  if (out == nullptr || n < 0 || (n > 0 && coords == nullptr) || n > INT32_MAX) return kErrInvalid;
+  *out = nullptr;
+  Table* t = new Table;
+  t->n = n;
+  t->coords.assign(coords, coords + 4 * n);
+  t->map.reserve(size_t(n) * 2 + 1);
+  for (int64_t i = 0; i < n; ++i) {
+    const int32_t* c = coords + 4 * i;
+    if (!in_range(c[0]) || !in_range(c[1]) || !in_range(c[2]) || !in_range(c[3])) {
+      delete t;
+      return kErrCoordRange;
+    }
+    auto ins = t->map.emplace(pack_key(c[0], c[1], c[2], c[3]), int32_t(i));
+    if (!ins.second) {
+      delete t;
+      return kErrDuplicate;
+    }
+  }
+  *out = t;
+  return kOk;
+}
+
+void oc_free(void* h) { delete static_cast<Table*>(h); }
+
+// idx[q] = row of query coordinate q, or -1 if it is not active (including
+// queries with a component outside [0, 2^16)).
+int oc_lookup(const void* h, const int32_t* q, int64_t nq, int32_t* idx) {
+  const Table* t = static_cast<const Table*>(h);
+  if (t == nullptr || nq < 0 || (nq > 0 && (q == nullptr || idx == nullptr))) return kErrInvalid;
+  for (int64_t i = 0; i < nq; ++i) {
+    const int32_t* c = q + 4 * i;
+    int32_t r = -1;
+    if (in_range(c[0]) && in_range(c[1]) && in_range(c[2]) && in_range(c[3])) {
+      auto it = t->map.find(pack_key(c[0], c[1], c[2], c[3]));
+      if (it != t->map.end()) r = it->second;
+    }
+    idx[i] = r;
+  }
+  return kOk;
+}
+
+// nbr[i * 27 + k] = row of the voxel at (b_i, x_i + dx_k, y_i + dy_k, z_i + dz_k),
+// or -1 when that voxel is not active or lies outside [0, 2^16).
+int oc_kernel_map(const void* h, int32_t* nbr) {
+  const Table* t = static_cast<const Table*>(h);
+  if (t == nullptr || (t->n > 0 && nbr == nullptr)) return kErrInvalid;
+  const int64_t n = t->n;
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; ++i) {
+    const int32_t* c = t->coords.data() + 4 * i;
+    for (int k = 0; k < 27; ++k) {
+      int dx, dy, dz;
+      tap_offset(k, dx, dy, dz);
+      const int64_t x = int64_t(c[1]) + dx, y = int64_t(c[2]) + dy, z = int64_t(c[3]) + dz;
+      int32_t r = -1;
+      if (in_range(x) && in_range(y) && in_range(z)) {
+        auto it = t->map.find(pack_key(c[0], x, y, z));
+        if (it != t->map.end()) r = it->second;
+      }
+      nbr[i * 27 + k] = r;
+    }
+  }
+  return kOk;
+}
+
+// y[r, co] for each requested row r (rows == NULL: every row 0..n-1, and y is
+// [n, c_out]; otherwise y is [nrows, c_out] in the order of `rows`).
+// x is [n, c_in] and w is [27, c_in, c_out], both double, row-major.
+int oc_forward(const int32_t* nbr, int64_t n, const int64_t* rows, int64_t nrows,
+               const double* x, const double* w, int c_in, int c_out, double* y) {
+  if (n < 0 || c_in <= 0 || c_out <= 0) return kErrInvalid;
+  const int64_t m = rows ? nrows : n;
+  if (m < 0) return kErrInvalid;
+  if (m > 0 && (nbr == nullptr || x == nullptr || w == nullptr || y == nullptr)) return kErrInvalid;
+  for (int64_t q = 0; q < (rows ? nrows : 0); ++q)
+    if (rows[q] < 0 || rows[q] >= n) return kErrInvalid;
+#pragma omp parallel
+  {
+    std::vector<double> acc(static_cast<size_t>(c_out));
+#pragma omp for schedule(dynamic, 64)
+    for (int64_t q = 0; q < m; ++q) {
+      const int64_t i = rows ? rows[q] : q;
+      std::fill(acc.begin(), acc.end(), 0.0);
+      for (int k = 0; k < 27; ++k) {
+        const int32_t j = nbr[i * 27 + k];
+        if (j < 0) continue;
+        const double* xr = x + int64_t(j) * c_in;
+        const double* wk = w + int64_t(k) * c_in * c_out;
+        for (int ci = 0; ci < c_in; ++ci) {
+          const double xv = xr[ci];
+          const double* wr = wk + int64_t(ci) * c_out;
+          for (int co = 0; co < c_out; ++co) acc[size_t(co)] += wr[co] * xv;
+        }
+      }
+      std::memcpy(y + q * c_out, acc.data(), sizeof(double) * size_t(c_out));
+    }
+  }
+  return kOk;
+}
+
+int oc_num_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
+
+}  // extern "C"

@@ -1,0 +1,325 @@
+"""Pins for the CPU oracle, checked against things other than itself.
+
+Each test compares the oracle with an independent fact: a hand-worked example,
+a library routine (torch's dense conv3d in float64), a dense brute force, a
+closed form, or an invariant the definition implies. They run without a GPU.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gen import workloads as W
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def tap_offsets():
+    # d_k for k = 9*Kd + 3*Kh + Kw, component = K - 1 (written from the tap
+    # numbering, independently of the oracle's own helper).
+    return np.array([(a - 1, b - 1, c - 1) for a in range(3) for b in range(3) for c in range(3)])
+
+
+# --------------------------------------------------------------------------
+# hand-worked example
+# --------------------------------------------------------------------------
+def load_hand_example():
+    rows, nb = [], {}
+    section = None
+    with open(os.path.join(GOLDEN, "hand_example.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            if line in ("coords_features_y", "neighbours"):
+                section = line
+                continue
+            parts = line.split()
+            if section == "coords_features_y":
+                rows.append([int(v) for v in parts])
+            else:
+                nb[int(parts[0])] = {int(p.split(":")[0]): int(p.split(":")[1]) for p in parts[1:]}
+    a = np.array(rows, dtype=np.int64)
+    return a[:, :4].astype(np.int32), a[:, 4].astype(np.float64), a[:, 5].astype(np.float64), nb
+
+
+def test_hand_example_map_and_values():
+    coords, feat, y_exp, nb = load_hand_example()
+    nbr = oracle.kernel_map(coords)
+    expected = np.full((len(coords), 27), -1, dtype=np.int32)
+    for i, d in nb.items():
+        for k, j in d.items():
+            expected[i, k] = j
+    np.testing.assert_array_equal(nbr, expected)
+    w = (np.arange(27, dtype=np.float64) + 1.0).reshape(27, 1, 1)
+    y = oracle.forward(nbr, feat.reshape(-1, 1), w)
+    np.testing.assert_array_equal(y[:, 0], y_exp)
+
+
+# --------------------------------------------------------------------------
+# kernel map against brute force and a dense look-up table
+# --------------------------------------------------------------------------
+def brute_force_map(coords):
+    c = coords.astype(np.int64)
+    n = len(c)
+    nbr = np.full((n, 27), -1, dtype=np.int32)
+    d = c[None, :, 1:] - c[:, None, 1:]                   # [i, j, 3]: p_j - p_i
+    same_b = c[None, :, 0] == c[:, None, 0]
+    close = same_b & (np.abs(d) <= 1).all(axis=2)
+    ii, jj = np.nonzero(close)
+    dd = d[ii, jj]
+    k = 9 * (dd[:, 0] + 1) + 3 * (dd[:, 1] + 1) + (dd[:, 2] + 1)
+    nbr[ii, k] = jj
+    return nbr
+
+
+def lut_map(coords, D, B):
+    lut = np.full((B, D, D, D), -1, dtype=np.int32)
+    c = coords.astype(np.int64)
+    lut[c[:, 0], c[:, 1], c[:, 2], c[:, 3]] = np.arange(len(c), dtype=np.int32)
+    nbr = np.full((len(c), 27), -1, dtype=np.int32)
+    for k, (dx, dy, dz) in enumerate(tap_offsets()):
+        q = c[:, 1:] + np.array([dx, dy, dz])
+        ok = ((q >= 0) & (q < D)).all(axis=1)
+        nbr[ok, k] = lut[c[ok, 0], q[ok, 0], q[ok, 1], q[ok, 2]]
+    return nbr
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_map_brute_force_random(seed):
+    rng = np.random.default_rng(seed)
+    coords = W.random_sparse(rng, 1500, D=12, B=2)
+    coords = coords[rng.permutation(len(coords))]
+    np.testing.assert_array_equal(oracle.kernel_map(coords), brute_force_map(coords))
+
+
+def test_map_brute_force_tiny_config():
+    wl = W.make("T", with_values=False)
+    np.testing.assert_array_equal(oracle.kernel_map(wl.coords), brute_force_map(wl.coords))
+    wl = W.make("T", seed_offset=100, order="shuffled", with_values=False)
+    np.testing.assert_array_equal(oracle.kernel_map(wl.coords), brute_force_map(wl.coords))
+
+
+@pytest.mark.parametrize("name", ["S", "W", "L", "X"])
+def test_map_lut_configs(name):
+    wl = W.make(name, with_values=False)
+    nbr = oracle.kernel_map(wl.coords)
+    np.testing.assert_array_equal(nbr, lut_map(wl.coords, wl.D, wl.B))
+
+
+def test_map_invariants():
+    wl = W.make("S", seed_offset=100, order="shuffled", with_values=False)
+    nbr = oracle.kernel_map(wl.coords)
+    n = wl.n
+    np.testing.assert_array_equal(nbr[:, 13], np.arange(n))
+    # mirror symmetry: nbr[i][k] = j  <=>  nbr[j][26-k] = i
+    ii, kk = np.nonzero(nbr >= 0)
+    jj = nbr[ii, kk]
+    np.testing.assert_array_equal(nbr[jj, 26 - kk], ii)
+    # per-offset counts: |A intersect (A - d_k)| with Python sets
+    A = set(map(tuple, wl.coords.tolist()))
+    for k, (dx, dy, dz) in enumerate(tap_offsets()):
+        expect = sum((b, x + dx, y + dy, z + dz) in A for (b, x, y, z) in A)
+        assert int((nbr[:, k] >= 0).sum()) == expect
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 5, 7])
+def test_map_full_cube_closed_form(n):
+    coords = W.full_cube(n, origin=(3, 4, 5))
+    nbr = oracle.kernel_map(coords)
+    assert int((nbr >= 0).sum()) == (3 * n - 2) ** 3
+    deg = (nbr >= 0).sum(axis=1)
+    # interior 27, face 18, edge 12, corner 8 (n >= 2)
+    if n >= 2:
+        counts = {27: (n - 2) ** 3, 18: 6 * (n - 2) ** 2, 12: 12 * (n - 2), 8: 8}
+        got = {int(v): int((deg == v).sum()) for v in np.unique(deg)}
+        assert got == {k: v for k, v in counts.items() if v}
+
+
+def test_lookup_against_dict():
+    rng = np.random.default_rng(7)
+    coords = W.random_sparse(rng, 3000, D=40, B=3)
+    t = oracle.Table(coords)
+    d = {tuple(r): i for i, r in enumerate(coords.tolist())}
+    np.testing.assert_array_equal(t.lookup(coords), np.arange(len(coords)))
+    q = rng.integers(-2, 42, size=(20000, 4)).astype(np.int32)
+    q[:, 0] = rng.integers(0, 4, size=20000)
+    exp = np.array([d.get(tuple(r), -1) for r in q.tolist()], dtype=np.int32)
+    np.testing.assert_array_equal(t.lookup(q), exp)
+
+
+def test_errors_and_empty():
+    assert oracle.build_status(np.array([[0, 1, 2, 3], [0, 1, 2, 3]], np.int32)) == oracle.ERR_DUPLICATE
+    assert oracle.build_status(np.array([[0, -1, 2, 3]], np.int32)) == oracle.ERR_COORD_RANGE
+    assert oracle.build_status(np.array([[0, 1, 65536, 3]], np.int32)) == oracle.ERR_COORD_RANGE
+    assert oracle.build_status(np.array([[65535, 65535, 65535, 65535]], np.int32)) == oracle.OK
+    nbr = oracle.kernel_map(np.zeros((0, 4), np.int32))
+    assert nbr.shape == (0, 27)
+    y = oracle.forward(nbr, np.zeros((0, 4)), np.zeros((27, 4, 3)))
+    assert y.shape == (0, 3)
+    # neighbours at the top of the coordinate range do not wrap around
+    c = np.array([[0, 65535, 65535, 65535], [0, 0, 0, 0], [0, 65534, 65535, 65535]], np.int32)
+    nbr = oracle.kernel_map(c)
+    assert (nbr[0] >= 0).sum() == 2 and nbr[0, 4] == 2
+    assert (nbr[1] >= 0).sum() == 1
+
+
+# --------------------------------------------------------------------------
+# feature sum against dense 3x3x3 convolution (zero padding 1)
+# --------------------------------------------------------------------------
+def dense_inputs(coords, x, B, D):
+    dense = np.zeros((B, x.shape[1], D, D, D))
+    c = coords.astype(np.int64)
+    dense[c[:, 0], :, c[:, 1], c[:, 2], c[:, 3]] = x
+    return dense
+
+
+def torch_dense_conv(coords, x, w, B, D):
+    dense = torch.from_numpy(dense_inputs(coords, x, B, D))
+    # Wt[co, ci, a, b, c] = W[9a + 3b + c, ci, co]; spatial dims (D, H, W) = (x, y, z)
+    wt = torch.from_numpy(np.ascontiguousarray(w.reshape(3, 3, 3, w.shape[1], w.shape[2])
+                                               .transpose(4, 3, 0, 1, 2)))
+    out = torch.nn.functional.conv3d(dense, wt, padding=1).numpy()
+    c = coords.astype(np.int64)
+    return out[c[:, 0], :, c[:, 1], c[:, 2], c[:, 3]]
+
+
+def naive_dense_conv(coords, x, w, B, D):
+    """Dense zero-padded 3x3x3 cross-correlation, looping over the 27 shifts of
+    a padded grid (no hashing, no neighbour lists)."""
+    dense = dense_inputs(coords, x, B, D)
+    pad = np.zeros((B, x.shape[1], D + 2, D + 2, D + 2))
+    pad[:, :, 1:-1, 1:-1, 1:-1] = dense
+    out = np.zeros((B, w.shape[2], D, D, D))
+    for a in range(3):
+        for b in range(3):
+            for cc in range(3):
+                sh = pad[:, :, a:a + D, b:b + D, cc:cc + D]            # in[p + (a-1, b-1, c-1)]
+                out += np.einsum("icxyz,io->ocxyz", sh.transpose(1, 0, 2, 3, 4),
+                                 w[9 * a + 3 * b + cc]).transpose(1, 0, 2, 3, 4)
+    c = coords.astype(np.int64)
+    return out[c[:, 0], :, c[:, 1], c[:, 2], c[:, 3]]
+
+
+def rel_err(a, b):
+    return np.abs(a - b).max() / max(np.abs(b).max(), 1e-300)
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_forward_vs_dense_conv(seed):
+    rng = np.random.default_rng(100 + seed)
+    D, B, ci, co = 9, 2, 3, 5
+    coords = W.random_sparse(rng, 300, D=D, B=B)
+    coords = coords[rng.permutation(len(coords))]
+    x = rng.standard_normal((len(coords), ci))
+    w = rng.standard_normal((27, ci, co))
+    y = oracle.conv(coords, x, w)[1]
+    assert rel_err(y, torch_dense_conv(coords, x, w, B, D)) < 1e-12
+    assert rel_err(y, naive_dense_conv(coords, x, w, B, D)) < 1e-12
+
+
+def test_forward_vs_dense_conv_tiny_config():
+    wl = W.make("T")
+    y = oracle.conv(wl.coords, wl.x, wl.w)[1]
+    ref = torch_dense_conv(wl.coords, wl.x.astype(np.float64), wl.w.astype(np.float64), 1, wl.D)
+    assert rel_err(y, ref) < 1e-12
+
+
+@pytest.mark.parametrize("k", [0, 4, 13, 22, 26])
+def test_single_tap(k):
+    rng = np.random.default_rng(k)
+    D, ci, co = 8, 4, 3
+    coords = W.random_sparse(rng, 200, D=D)
+    x = rng.standard_normal((len(coords), ci))
+    w = np.zeros((27, ci, co))
+    w[k] = rng.standard_normal((ci, co))
+    nbr, y = oracle.conv(coords, x, w)
+    j = nbr[:, k]
+    exp = np.where((j >= 0)[:, None], x[np.maximum(j, 0)] @ w[k], 0.0)
+    np.testing.assert_allclose(y, exp, rtol=1e-13, atol=1e-13)
+    assert rel_err(y, torch_dense_conv(coords, x, w, 1, D)) < 1e-12
+
+
+# --------------------------------------------------------------------------
+# exact special cases and invariances
+# --------------------------------------------------------------------------
+def test_identity_kernel_exact():
+    wl = W.make("S", seed_offset=100, order="shuffled")
+    x = wl.x.astype(np.float64)
+    w = np.zeros((27, wl.c_in, wl.c_in))
+    w[13] = np.eye(wl.c_in)
+    y = oracle.conv(wl.coords, x, w)[1]
+    np.testing.assert_array_equal(y, x)
+
+
+def test_isolated_voxel():
+    rng = np.random.default_rng(3)
+    coords = np.array([[0, 10, 10, 10], [0, 20, 20, 20], [1, 10, 10, 11]], np.int32)
+    x = rng.standard_normal((3, 6))
+    w = rng.standard_normal((27, 6, 4))
+    y = oracle.conv(coords, x, w)[1]
+    for i in range(3):
+        exp = [sum(x[i, c] * w[13, c, o] for c in range(6)) for o in range(4)]
+        np.testing.assert_allclose(y[i], exp, rtol=1e-14, atol=1e-14)
+
+
+def test_translation_invariance_exact():
+    wl = W.make("T", seed_offset=200, order="shuffled")
+    nbr, y = oracle.conv(wl.coords, wl.x, wl.w)
+    shifted = wl.coords + np.array([0, 1000, 3, 777], np.int32)
+    nbr2, y2 = oracle.conv(shifted, wl.x, wl.w)
+    np.testing.assert_array_equal(nbr2, nbr)
+    np.testing.assert_array_equal(y2, y)
+
+
+def test_permutation_exact():
+    wl = W.make("T", seed_offset=100)
+    nbr, y = oracle.conv(wl.coords, wl.x, wl.w)
+    pi = np.random.default_rng(5).permutation(wl.n)
+    inv = np.argsort(pi)
+    nbr2, y2 = oracle.conv(wl.coords[pi], wl.x[pi], wl.w)
+    np.testing.assert_array_equal(y2, y[pi])
+    exp = np.where(nbr[pi] >= 0, inv[np.maximum(nbr[pi], 0)], -1)
+    np.testing.assert_array_equal(nbr2, exp)
+
+
+def test_batch_isolation_exact():
+    rng = np.random.default_rng(11)
+    a = W.random_sparse(rng, 400, D=10)
+    b = a.copy()
+    b[:, 0] = 1                                   # same places, second object
+    c = W.random_sparse(rng, 300, D=10)
+    c[:, 0] = 2
+    coords = np.concatenate([a, b, c])
+    x = rng.standard_normal((len(coords), 3))
+    w = rng.standard_normal((27, 3, 2))
+    nbr, y = oracle.conv(coords, x, w)
+    off = 0
+    for part in (a, b, c):
+        n = len(part)
+        nb_p, y_p = oracle.conv(part, x[off:off + n], w)
+        np.testing.assert_array_equal(y[off:off + n], y_p)
+        np.testing.assert_array_equal(nbr[off:off + n], np.where(nb_p >= 0, nb_p + off, -1))
+        off += n
+
+
+def test_linearity():
+    wl = W.make("T")
+    rng = np.random.default_rng(9)
+    x1 = rng.standard_normal((wl.n, wl.c_in))
+    x2 = rng.standard_normal((wl.n, wl.c_in))
+    w = wl.w.astype(np.float64)
+    nbr = oracle.kernel_map(wl.coords)
+    lhs = oracle.forward(nbr, 0.75 * x1 - 2.5 * x2, w)
+    rhs = 0.75 * oracle.forward(nbr, x1, w) - 2.5 * oracle.forward(nbr, x2, w)
+    assert rel_err(lhs, rhs) < 1e-12
+
+
+def test_rows_subset_matches_full():
+    wl = W.make("S", seed_offset=100)
+    nbr = oracle.kernel_map(wl.coords)
+    rows = np.random.default_rng(1).choice(wl.n, 500, replace=False)
+    full = oracle.forward(nbr, wl.x, wl.w)
+    np.testing.assert_array_equal(oracle.forward(nbr, wl.x, wl.w, rows=rows), full[rows])
