@@ -1,0 +1,266 @@
+#!/usr/bin/env python3
+"""Benchmark of the submanifold sparse 3D convolution hot path on one MI355X.
+
+One step = the whole path over one synthetic voxel set: build_hash (Morton
+sort + open-addressing table), build_kernel_map (27 neighbours per voxel),
+pack_weights and the gather-GEMM (forward_packed). Inputs are resident in HBM
+before the timed region. Prints ONE JSON line.
+
+    python bench.py [--steps K] [--warmup W] [--config L] [--gpus 1]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 matrix peak
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fwd_mfma.json")
+GEMM_SOURCE = os.path.join(ROOT, "submanifold_sparse_conv_amd", "csrc", "gemm_mfma.hip")
+
+WORKLOAD_NAMES = {
+    "T": "16^3 sphere shell (radius 6, thickness 1), C 8->8 fp32",
+    "S": "64^3 union of 3 ellipsoid shells (thickness 2), C 64->64 bf16",
+    "W": "64^3 x 4 objects, ellipsoid shells, C 1024->1024 bf16",
+    "L": "256^3 thickened fBm level set (thickness 2), C 128->128 bf16",
+    "X": "512^3 x 2 objects, Gaussian blobs + holed sheets, C 64->32 bf16",
+}
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--config", default="L", choices=list(WORKLOAD_NAMES))
+    p.add_argument("--also", default="S", help="extra configs measured forward-only, comma list ('' = none)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=8.0, help="target wall time of the oracle forward sample")
+    p.add_argument("--gemm-reps", type=int, default=50)
+    return p.parse_args()
+
+
+def sha_of(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def to_device(wl, torch):
+    dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    c = torch.from_numpy(wl.coords).cuda()
+    x = torch.from_numpy(wl.x).cuda().to(dt)
+    w = torch.from_numpy(wl.w).cuda().to(dt)
+    return c, x, w
+
+
+class Path:
+    """Pre-allocated buffers and one step of the hot path."""
+
+    def __init__(self, sc, torch, coords, x, w):
+        self.sc, self.torch = sc, torch
+        self.coords, self.x, self.w = coords, x, w
+        n = int(coords.shape[0])
+        L = sc._lib.lib()
+        self.hws = sc.Workspace(L.tr_sparseconv_hash_workspace_bytes(n), coords.device)
+        self.kws = sc.Workspace(L.tr_sparseconv_kmap_workspace_bytes(n), coords.device)
+        self.nbr = torch.empty((n, 27), dtype=torch.int32, device=coords.device)
+        self.y = torch.empty((n, int(w.shape[2])), dtype=x.dtype, device=x.device)
+        self.h = self.m = self.wp = None
+
+    def step(self, ev=None):
+        sc = self.sc
+        if ev is not None:
+            ev[0].record()
+        self.h = sc.build_hash(self.coords, check_status=False, workspace=self.hws)
+        if ev is not None:
+            ev[1].record()
+        self.m = sc.build_kernel_map(self.h, nbr=self.nbr, workspace=self.kws)
+        if ev is not None:
+            ev[2].record()
+        self.wp = sc.pack_weights(self.w)
+        if ev is not None:
+            ev[3].record()
+        sc.forward_packed(self.m, self.x, self.wp, out=self.y)
+        if ev is not None:
+            ev[4].record()
+
+
+def pairs_of(nbr_t):
+    return int((nbr_t >= 0).sum().item())
+
+
+def measure_forward_only(sc, torch, path, reps):
+    """Back-to-back gather-GEMM launches between two events (steady state)."""
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for _ in range(3):
+        sc.forward_packed(path.m, path.x, path.wp, out=path.y)
+    torch.cuda.synchronize()
+    s.record()
+    for _ in range(reps):
+        sc.forward_packed(path.m, path.x, path.wp, out=path.y)
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / reps
+
+
+def cpu_baseline(wl, target_s):
+    """The oracle (plain C++, unordered_map + fp64 direct sum) on the host
+    cores: full map build and kernel map, fp64 forward on a timed random
+    sample of rows, scaled to all rows."""
+    import oracle
+    t0 = time.perf_counter()
+    table = oracle.Table(wl.coords)
+    t1 = time.perf_counter()
+    nbr = table.kernel_map()
+    t2 = time.perf_counter()
+    rng = np.random.default_rng(12345)
+    probe = rng.choice(wl.n, size=min(wl.n, 2000), replace=False)
+    tp = time.perf_counter()
+    oracle.forward(nbr, wl.x, wl.w, rows=probe)
+    rate = len(probe) / max(time.perf_counter() - tp, 1e-9)
+    k = int(min(wl.n, max(2000, rate * target_s)))
+    rows = rng.choice(wl.n, size=k, replace=False)
+    t3 = time.perf_counter()
+    oracle.forward(nbr, wl.x, wl.w, rows=rows)
+    t4 = time.perf_counter()
+    t_fwd_all = (t4 - t3) * wl.n / k
+    total = (t1 - t0) + (t2 - t1) + t_fwd_all
+    return {
+        "value": wl.n / total,
+        "unit": "voxels/s",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": (f"full unordered_map build ({t1 - t0:.2f} s, serial) and kernel map "
+                   f"({t2 - t1:.2f} s) over all {wl.n} voxels; fp64 forward over {k} random rows "
+                   f"({t4 - t3:.2f} s) scaled to all rows ({t_fwd_all:.2f} s)"),
+    }
+
+
+def traffic_entry():
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current gather-GEMM source; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha256") != sha_of(GEMM_SOURCE):
+        return None
+    return t.get("bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); multi-GPU "
+              "sharding of this path is described in DESIGN.md but not built.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import submanifold_sparse_conv_amd as sc
+    from gen import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    wl = W.make(args.config)
+    coords, x, w = to_device(wl, torch)
+    path = Path(sc, torch, coords, x, w)
+    for _ in range(args.warmup):
+        path.step()
+    torch.cuda.synchronize()
+    M = pairs_of(path.nbr)
+    assert bool((path.nbr[:, 13] == torch.arange(wl.n, device=dev, dtype=torch.int32)).all())
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        path.step(evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    ph = np.array([[evs[i][j].elapsed_time(evs[i][j + 1]) for j in range(4)] for i in range(args.steps)])
+    t_hash, t_map, t_pack, t_gemm = ph.mean(axis=0)
+    assert bool(torch.isfinite(path.y.float()).all())
+
+    flops = 2.0 * wl.c_in * wl.c_out * M
+    gemm_tflops = flops / (t_gemm * 1e-3) / 1e12
+    t_gemm_ss = measure_forward_only(sc, torch, path, args.gemm_reps)
+
+    P = int(16)
+    while P < 2 * wl.n:
+        P *= 2
+    hash_bytes = 16 * wl.n + 12 * wl.n + 16 * P
+    map_bytes = 12 * wl.n + 16 * P + 108 * wl.n + 4 * wl.n
+    traffic = traffic_entry()
+
+    out = {
+        "metric": "sparse-conv voxels/s (whole path: hash + kernel map + gather-GEMM)",
+        "value": wl.n / (ms_step * 1e-3),
+        "unit": "voxels/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if wl.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD_NAMES[args.config], "n_voxels": wl.n, "pairs_M": M,
+                   "c_in": wl.c_in, "c_out": wl.c_out, "grid": wl.D, "batch": wl.B, "seed": wl.seed},
+        "phases_ms": {"build_hash": t_hash, "build_kernel_map": t_map, "pack_weights": t_pack,
+                      "gather_gemm": t_gemm},
+        "forward": {"voxels_per_s_steady": wl.n / (t_gemm_ss * 1e-3), "ms_steady": t_gemm_ss,
+                    "effective_tflops": flops / (t_gemm_ss * 1e-3) / 1e12,
+                    "frac_bf16_peak": flops / (t_gemm_ss * 1e-3) / 1e12 / PEAK_BF16_TFLOPS},
+        "hash_map_hbm": {"algorithmic_bytes": hash_bytes + map_bytes,
+                         "gbs": (hash_bytes + map_bytes) / ((t_hash + t_map) * 1e-3) / 1e9,
+                         "frac": (hash_bytes + map_bytes) / ((t_hash + t_map) * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                         "map_only_gbs": map_bytes / (t_map * 1e-3) / 1e9},
+        "roofline": {"kernel": "fwd_mfma (gather-GEMM)", "bound": "mfma", "achieved": gemm_tflops,
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": gemm_tflops / PEAK_BF16_TFLOPS,
+                     "traffic": traffic},
+    }
+    extra = {}
+    for name in [a for a in args.also.split(",") if a and a != args.config]:
+        wl2 = W.make(name)
+        c2, x2, w2 = to_device(wl2, torch)
+        p2 = Path(sc, torch, c2, x2, w2)
+        for _ in range(2):
+            p2.step()
+        torch.cuda.synchronize()
+        M2 = pairs_of(p2.nbr)
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(10)]
+        for i in range(10):
+            p2.step(ev[i])
+        torch.cuda.synchronize()
+        st = np.array([[ev[i][j].elapsed_time(ev[i][j + 1]) for j in range(4)] for i in range(10)]).mean(0)
+        tss = measure_forward_only(sc, torch, p2, args.gemm_reps)
+        f2 = 2.0 * wl2.c_in * wl2.c_out * M2
+        extra[name] = {"workload": WORKLOAD_NAMES[name], "n_voxels": wl2.n, "pairs_M": M2,
+                       "ms_path": float(st.sum()), "voxels_per_s_path": wl2.n / (st.sum() * 1e-3),
+                       "gemm_ms_steady": tss, "voxels_per_s_forward": wl2.n / (tss * 1e-3),
+                       "effective_tflops": f2 / (tss * 1e-3) / 1e12}
+        del p2, c2, x2, w2
+    if extra:
+        out["also"] = extra
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

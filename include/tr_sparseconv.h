@@ -1,0 +1,179 @@
+/* tr_sparseconv.h -- C ABI of the submanifold sparse 3D convolution library
+ * (gfx950 / MI355X, HIP).
+ *
+ * The operation. For a set of N active voxels with integer coordinates
+ * (b, x, y, z), features x[N, C_in] and tap-major weights w[27, C_in, C_out],
+ * the library computes, for every active voxel i and output channel co,
+ *
+ *     y[i, co] = sum over taps k (0..26) whose neighbour j = nbr[i][k] is active,
+ *                sum over ci of  w[k, ci, co] * x[j, ci]
+ *
+ * and writes output rows only at the active voxels. The pages define it as a
+ * spatial hash of the active voxels followed, per kernel position, by a gather
+ * of neighbour features, a product with that position's weights and a sum into
+ * the output ("Running TRELLIS.2 on a Mac (1/3)", section "Swapping out the CUDA
+ * libraries one at a time", sparse 3D convolution paragraph); as a neighbour
+ * table built once per resolution level and a gather-GEMM over it with
+ * half-precision inputs and single-precision accumulation ("Porting TRELLIS.2
+ * From Python to Rust and Metal", section V); with features kept sparse rather
+ * than materialised on a dense grid (mlx-diffuser TRELLIS guide, section "Why it
+ * fits better on a Mac").
+ *
+ * Conventions.
+ *  - Coordinates: int32 rows (b, x, y, z), each component in [0, 65536)
+ *    (startup packet, page 5, section 5, fixture table row B).
+ *  - Features: row-major [N, C] (same table, rows C-D). Row i of every per-voxel
+ *    array (x, y, nbr) belongs to coordinate row i as the caller gave it.
+ *  - Weights: tap-major [27, C_in, C_out] (startup packet, section 5 conv
+ *    conventions and section 8), tap k = 9*Kd + 3*Kh + Kw.
+ *  - Tap k reads the voxel at (x + Kd - 1, y + Kh - 1, z + Kw - 1) in the same
+ *    object b: cross-correlation, equal to a dense 3x3x3 convolution with zero
+ *    padding 1 evaluated at the active sites. A neighbour outside [0, 65536) on
+ *    any axis does not exist.
+ *
+ * Memory and streams. Every tensor pointer is a DEVICE pointer owned by the
+ * caller, who must keep it alive while a handle that refers to it is in use.
+ * `stream` is a hipStream_t (NULL = the null stream). Work is enqueued on it;
+ * only tr_sparseconv_build_hash (one small read-back) and tr_sparseconv_status
+ * wait for the device. Handles are small host structs; destroying one frees
+ * that struct only, never device memory.
+ *
+ * Errors. Every int-returning call returns TR_SC_OK (0) or a negative
+ * tr_sc_status. A failed call enqueues nothing further and records a message
+ * for tr_sparseconv_last_error() (thread-local). Problems that only the device
+ * can see after the read-back (duplicate coordinates, a full table) are kept in
+ * a status word inside the hash workspace and returned by tr_sparseconv_status.
+ */
+#ifndef TR_SPARSECONV_H
+#define TR_SPARSECONV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  TR_SC_OK = 0,
+  TR_SC_ERR_INVALID_ARG = -1, /* null pointer, negative size, bad handle      */
+  TR_SC_ERR_COORD_RANGE = -2, /* a coordinate component outside [0, 65536)    */
+  TR_SC_ERR_DUPLICATE = -3,   /* the same (b, x, y, z) given twice            */
+  TR_SC_ERR_CAPACITY = -4,    /* hash table ran out of slots                  */
+  TR_SC_ERR_WORKSPACE = -5,   /* workspace smaller than the *_workspace_bytes */
+  TR_SC_ERR_UNSUPPORTED = -6, /* dtype / channel count the library lacks      */
+  TR_SC_ERR_HIP = -7          /* a HIP runtime call failed                    */
+} tr_sc_status;
+
+typedef enum { TR_SC_F32 = 0, TR_SC_BF16 = 1 } tr_sc_dtype;
+
+typedef struct tr_sc_hash tr_sc_hash; /* coordinate hash (opaque)  */
+typedef struct tr_sc_kmap tr_sc_kmap; /* kernel map (opaque)       */
+
+/* Library version, (major << 16) | minor. */
+int tr_sparseconv_version(void);
+
+/* ------------------------------------------------------------------------
+ * Coordinate hash.
+ * The "spatial hash of the active voxels" of the definition above. The voxels
+ * are sorted along a Morton (Z-order) curve and inserted into an
+ * open-addressing table in the workspace.
+ * ------------------------------------------------------------------------ */
+
+/* Bytes of device workspace tr_sparseconv_build_hash needs for n voxels
+ * (0 for n < 0). */
+size_t tr_sparseconv_hash_workspace_bytes(int64_t n);
+
+/* coords    device int32 [n, 4] (b, x, y, z); read during this call only.
+ * n         number of voxels, 0 <= n <= 2^30 (n = 0 is valid: empty hash).
+ * workspace device buffer of >= tr_sparseconv_hash_workspace_bytes(n) bytes,
+ *           256-byte aligned; it holds the table and must outlive the handle.
+ * out       receives a new handle (release with tr_sparseconv_hash_destroy).
+ * Returns TR_SC_ERR_COORD_RANGE if any component is outside [0, 65536); this
+ * is found by the device and read back once, so the call waits for the work
+ * enqueued before it on `stream`. Duplicate coordinates are reported by
+ * tr_sparseconv_status. */
+int tr_sparseconv_build_hash(const int32_t* coords, int64_t n, void* workspace,
+                             size_t ws_bytes, void* stream, tr_sc_hash** out);
+
+/* Device-found errors of the build, read from the workspace status word:
+ * TR_SC_OK, TR_SC_ERR_DUPLICATE or TR_SC_ERR_CAPACITY. Synchronises `stream`. */
+int tr_sparseconv_status(const tr_sc_hash* h, void* stream);
+
+/* Number of voxels the hash was built over. */
+int64_t tr_sparseconv_hash_size(const tr_sc_hash* h);
+
+/* Test hook. q: device int32 [nq, 4] queries; idx: device int32 [nq] receives
+ * the caller row of each query, or -1 when it is not an active voxel (also for
+ * components outside [0, 65536)). */
+int tr_sparseconv_hash_lookup(const tr_sc_hash* h, const int32_t* q, int64_t nq,
+                              int32_t* idx, void* stream);
+
+/* Test hook. perm: device int32 [n] receives the caller row at each position
+ * of the Morton order (stable: equal keys cannot occur in a valid set). */
+int tr_sparseconv_hash_sorted_rows(const tr_sc_hash* h, int32_t* perm, void* stream);
+
+void tr_sparseconv_hash_destroy(tr_sc_hash* h);
+
+/* ------------------------------------------------------------------------
+ * Kernel map (the neighbour table, built once per resolution level and reused
+ * by every layer at that level -- "Porting TRELLIS.2 ...", section V).
+ * ------------------------------------------------------------------------ */
+
+/* Bytes of device workspace tr_sparseconv_build_kernel_map needs. */
+size_t tr_sparseconv_kmap_workspace_bytes(int64_t n);
+
+/* h         hash from tr_sparseconv_build_hash (its workspace must stay alive).
+ * nbr       device int32 [n, 27] output: nbr[i*27 + k] = caller row of the
+ *           neighbour of voxel i at tap k, or -1. nbr[i*27 + 13] = i.
+ *           Owned by the caller; the kernel map reads it in every forward.
+ * workspace device buffer >= tr_sparseconv_kmap_workspace_bytes(n) bytes
+ *           (per-voxel neighbour masks in Morton order); must outlive the handle.
+ * out       receives a new handle (release with tr_sparseconv_kmap_destroy). */
+int tr_sparseconv_build_kernel_map(const tr_sc_hash* h, int32_t* nbr, void* workspace,
+                                   size_t ws_bytes, void* stream, tr_sc_kmap** out);
+
+void tr_sparseconv_kmap_destroy(tr_sc_kmap* m);
+
+/* ------------------------------------------------------------------------
+ * Forward: the gather-GEMM over the kernel map.
+ * ------------------------------------------------------------------------ */
+
+/* Bytes of device workspace tr_sparseconv_forward needs (the packed weights,
+ * see tr_sparseconv_pack_weights below). */
+size_t tr_sparseconv_forward_workspace_bytes(int c_in, int c_out, int dtype);
+
+/* m      kernel map of the voxel set.
+ * x      device [n, c_in] features, dtype `dtype`.
+ * w      device [27, c_in, c_out] weights, dtype `dtype`.
+ * y      device [n, c_out] output, dtype `dtype`; every element is written.
+ * dtype  TR_SC_BF16: bf16 inputs, fp32 accumulation, output rounded to bf16
+ *        (nearest, ties to even); needs c_in % 8 == 0 and c_out % 8 == 0.
+ *        TR_SC_F32: fp32 inputs, fp32 accumulation and output; any c >= 1.
+ * No atomics: the result is the same bit for bit on every call. x and y must
+ * not overlap. */
+int tr_sparseconv_forward(const tr_sc_kmap* m, const void* x, const void* w, void* y,
+                          int c_in, int c_out, int dtype, void* workspace,
+                          size_t ws_bytes, void* stream);
+
+/* The two halves of tr_sparseconv_forward, for callers that reuse one set of
+ * weights across many calls (a layer applied to many inputs):
+ *
+ * tr_sparseconv_pack_weights: wp (device, >= tr_sparseconv_packed_weights_bytes
+ * bytes, 16-byte aligned, caller-owned) receives w [27, c_in, c_out] re-laid
+ * out for the matrix cores (bf16: [27, c_out, c_in]; f32: unchanged copy).
+ * tr_sparseconv_forward_packed: as tr_sparseconv_forward, reading the packed
+ * weights. Same argument rules and errors as tr_sparseconv_forward. */
+size_t tr_sparseconv_packed_weights_bytes(int c_in, int c_out, int dtype);
+int tr_sparseconv_pack_weights(const void* w, int c_in, int c_out, int dtype, void* wp,
+                               size_t wp_bytes, void* stream);
+int tr_sparseconv_forward_packed(const tr_sc_kmap* m, const void* x, const void* wp, void* y,
+                                 int c_in, int c_out, int dtype, void* stream);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char* tr_sparseconv_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TR_SPARSECONV_H */

@@ -1,0 +1,265 @@
+"""Submanifold sparse 3D convolution on MI355X (gfx950): Python binding.
+
+Thin marshalling over the C ABI in include/tr_sparseconv.h (same names without
+the `tr_sparseconv_` prefix). Every step of the computation runs in the HIP
+library; torch only provides device memory and the current stream.
+
+    h = build_hash(coords)          # int32 [N, 4] (b, x, y, z) on the GPU
+    m = build_kernel_map(h)         # m.nbr: int32 [N, 27]
+    y = forward(m, x, w)            # x [N, C_in], w [27, C_in, C_out] -> [N, C_out]
+"""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import _lib
+from ._lib import TrSparseConvError, check  # noqa: F401
+
+__all__ = ["build_hash", "build_kernel_map", "forward", "pack_weights", "forward_packed",
+           "status", "hash_lookup", "hash_sorted_rows", "HashTable", "KernelMap", "PackedWeights",
+           "TrSparseConvError", "version", "forward_workspace_bytes", "Workspace"]
+
+_DTYPES = {torch.float32: _lib.F32, torch.bfloat16: _lib.BF16}
+
+
+def version() -> tuple[int, int]:
+    v = _lib.lib().tr_sparseconv_version()
+    return v >> 16, v & 0xFFFF
+
+
+def _stream(device: torch.device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _ptr(t: torch.Tensor | None) -> ctypes.c_void_p:
+    return ctypes.c_void_p(t.data_ptr() if t is not None and t.numel() else None)
+
+
+class Workspace:
+    """Device bytes starting at a 256-byte boundary. Reusable across builds
+    (pass it as `workspace=`) when it is large enough."""
+
+    def __init__(self, nbytes: int, device):
+        self.nbytes = int(nbytes)
+        self.buf = torch.empty(max(self.nbytes, 1) + 256, dtype=torch.uint8, device=device)
+        self.ptr = ctypes.c_void_p(self.buf.data_ptr() + (-self.buf.data_ptr()) % 256)
+
+
+def _workspace(nbytes: int, device, given: "Workspace | None" = None) -> Workspace:
+    if given is not None:
+        if given.nbytes < nbytes:
+            raise ValueError(f"workspace of {given.nbytes} bytes, {nbytes} needed")
+        return given
+    return Workspace(nbytes, device)
+
+
+def _require(t: torch.Tensor, name: str, dtype=None, ndim=None):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+class HashTable:
+    """Coordinate hash (tr_sparseconv_build_hash). Keeps its workspace alive."""
+
+    def __init__(self, coords: torch.Tensor, check_status: bool = True,
+                 workspace: Workspace | None = None):
+        _require(coords, "coords", torch.int32, 2)
+        if coords.shape[1] != 4:
+            raise ValueError(f"coords must be [N, 4], got {tuple(coords.shape)}")
+        L = _lib.lib()
+        self.device = coords.device
+        self.n = int(coords.shape[0])
+        self._ws = _workspace(L.tr_sparseconv_hash_workspace_bytes(self.n), self.device, workspace)
+        h = ctypes.c_void_p()
+        with torch.cuda.device(self.device):
+            check(L.tr_sparseconv_build_hash(_ptr(coords), self.n, self._ws.ptr, self._ws.nbytes,
+                                             _stream(self.device), ctypes.byref(h)))
+        self._h = h
+        if check_status:
+            self.check_status()
+
+    @property
+    def handle(self) -> ctypes.c_void_p:
+        return self._h
+
+    def status(self) -> int:
+        with torch.cuda.device(self.device):
+            return _lib.lib().tr_sparseconv_status(self._h, _stream(self.device))
+
+    def check_status(self) -> None:
+        check(self.status())
+
+    def lookup(self, q: torch.Tensor) -> torch.Tensor:
+        _require(q, "queries", torch.int32, 2)
+        idx = torch.empty(q.shape[0], dtype=torch.int32, device=self.device)
+        with torch.cuda.device(self.device):
+            check(_lib.lib().tr_sparseconv_hash_lookup(self._h, _ptr(q), int(q.shape[0]), _ptr(idx),
+                                                       _stream(self.device)))
+        return idx
+
+    def sorted_rows(self) -> torch.Tensor:
+        perm = torch.empty(self.n, dtype=torch.int32, device=self.device)
+        with torch.cuda.device(self.device):
+            check(_lib.lib().tr_sparseconv_hash_sorted_rows(self._h, _ptr(perm), _stream(self.device)))
+        return perm
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and _lib._lib is not None:
+            _lib._lib.tr_sparseconv_hash_destroy(h)
+            self._h = None
+
+
+class KernelMap:
+    """Neighbour table (tr_sparseconv_build_kernel_map); `nbr` is int32 [N, 27]."""
+
+    def __init__(self, h: HashTable, nbr: torch.Tensor | None = None,
+                 workspace: Workspace | None = None):
+        L = _lib.lib()
+        self.hash = h                      # its workspace holds the Morton order
+        self.device = h.device
+        self.n = h.n
+        if nbr is None:
+            nbr = torch.empty((self.n, 27), dtype=torch.int32, device=self.device)
+        else:
+            _require(nbr, "nbr", torch.int32, 2)
+            if tuple(nbr.shape) != (self.n, 27):
+                raise ValueError(f"nbr must be [{self.n}, 27]")
+        self.nbr = nbr
+        self._ws = _workspace(L.tr_sparseconv_kmap_workspace_bytes(self.n), self.device, workspace)
+        m = ctypes.c_void_p()
+        with torch.cuda.device(self.device):
+            check(L.tr_sparseconv_build_kernel_map(h.handle, _ptr(self.nbr), self._ws.ptr,
+                                                   self._ws.nbytes, _stream(self.device),
+                                                   ctypes.byref(m)))
+        self._m = m
+        self._fws = {}
+
+    @property
+    def handle(self) -> ctypes.c_void_p:
+        return self._m
+
+    def forward_workspace(self, c_in: int, c_out: int, dtype: int) -> Workspace:
+        key = (c_in, c_out, dtype)
+        if key not in self._fws:
+            nbytes = _lib.lib().tr_sparseconv_forward_workspace_bytes(c_in, c_out, dtype)
+            self._fws[key] = Workspace(nbytes, self.device)
+        return self._fws[key]
+
+    def __del__(self):
+        m = getattr(self, "_m", None)
+        if m is not None and _lib._lib is not None:
+            _lib._lib.tr_sparseconv_kmap_destroy(m)
+            self._m = None
+
+
+def build_hash(coords: torch.Tensor, check_status: bool = True,
+               workspace: Workspace | None = None) -> HashTable:
+    return HashTable(coords, check_status=check_status, workspace=workspace)
+
+
+def build_kernel_map(h: HashTable, nbr: torch.Tensor | None = None,
+                     workspace: Workspace | None = None) -> KernelMap:
+    return KernelMap(h, nbr=nbr, workspace=workspace)
+
+
+class PackedWeights:
+    """Weights re-laid out for the gather-GEMM (tr_sparseconv_pack_weights)."""
+
+    def __init__(self, w: torch.Tensor):
+        if w.dtype not in _DTYPES:
+            raise ValueError(f"unsupported dtype {w.dtype}")
+        _require(w, "w", w.dtype, 3)
+        if w.shape[0] != 27:
+            raise ValueError(f"w must be [27, C_in, C_out], got {tuple(w.shape)}")
+        self.dtype = w.dtype
+        self.c_in, self.c_out = int(w.shape[1]), int(w.shape[2])
+        dt = _DTYPES[w.dtype]
+        L = _lib.lib()
+        self._ws = Workspace(L.tr_sparseconv_packed_weights_bytes(self.c_in, self.c_out, dt), w.device)
+        with torch.cuda.device(w.device):
+            check(L.tr_sparseconv_pack_weights(_ptr(w), self.c_in, self.c_out, dt, self._ws.ptr,
+                                               self._ws.nbytes, _stream(w.device)))
+
+
+def pack_weights(w: torch.Tensor) -> PackedWeights:
+    return PackedWeights(w)
+
+
+def _check_x(m, x, c_in, dtype):
+    if x.dtype != dtype:
+        raise ValueError(f"x is {x.dtype}, weights are {dtype}")
+    _require(x, "x", dtype, 2)
+    if int(x.shape[0]) != m.n or int(x.shape[1]) != c_in:
+        raise ValueError(f"x must be [{m.n}, {c_in}], got {tuple(x.shape)}")
+
+
+def _out(out, n, c_out, x):
+    if out is None:
+        return torch.empty((n, c_out), dtype=x.dtype, device=x.device)
+    _require(out, "out", x.dtype, 2)
+    if tuple(out.shape) != (n, c_out):
+        raise ValueError(f"out must be [{n}, {c_out}]")
+    return out
+
+
+def forward_packed(m: KernelMap, x: torch.Tensor, wp: PackedWeights,
+                   out: torch.Tensor | None = None) -> torch.Tensor:
+    """forward() with weights packed once by pack_weights()."""
+    _check_x(m, x, wp.c_in, wp.dtype)
+    out = _out(out, m.n, wp.c_out, x)
+    with torch.cuda.device(x.device):
+        check(_lib.lib().tr_sparseconv_forward_packed(m.handle, _ptr(x), wp._ws.ptr, _ptr(out),
+                                                      wp.c_in, wp.c_out, _DTYPES[wp.dtype],
+                                                      _stream(x.device)))
+    return out
+
+
+def status(h: HashTable) -> int:
+    return h.status()
+
+
+def hash_lookup(h: HashTable, q: torch.Tensor) -> torch.Tensor:
+    return h.lookup(q)
+
+
+def hash_sorted_rows(h: HashTable) -> torch.Tensor:
+    return h.sorted_rows()
+
+
+def forward_workspace_bytes(c_in: int, c_out: int, dtype: torch.dtype) -> int:
+    return int(_lib.lib().tr_sparseconv_forward_workspace_bytes(c_in, c_out, _DTYPES[dtype]))
+
+
+def forward(m: KernelMap, x: torch.Tensor, w: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """y[N, C_out] = submanifold 3x3x3 convolution of x[N, C_in] with w[27, C_in, C_out]."""
+    if x.dtype not in _DTYPES:
+        raise ValueError(f"unsupported dtype {x.dtype}")
+    _require(x, "x", x.dtype, 2)
+    _require(w, "w", x.dtype, 3)
+    n, c_in = int(x.shape[0]), int(x.shape[1])
+    if n != m.n:
+        raise ValueError(f"x has {n} rows, kernel map has {m.n}")
+    if w.shape[0] != 27 or w.shape[1] != c_in:
+        raise ValueError(f"w must be [27, {c_in}, C_out], got {tuple(w.shape)}")
+    c_out = int(w.shape[2])
+    if out is None:
+        out = torch.empty((n, c_out), dtype=x.dtype, device=x.device)
+    else:
+        _require(out, "out", x.dtype, 2)
+        if tuple(out.shape) != (n, c_out):
+            raise ValueError(f"out must be [{n}, {c_out}]")
+    dt = _DTYPES[x.dtype]
+    ws = m.forward_workspace(c_in, c_out, dt)
+    with torch.cuda.device(x.device):
+        check(_lib.lib().tr_sparseconv_forward(m.handle, _ptr(x), _ptr(w), _ptr(out), c_in, c_out, dt,
+                                               ws.ptr, ws.nbytes, _stream(x.device)))
+    return out

@@ -1,0 +1,359 @@
+// C ABI of the library (declared in include/tr_sparseconv.h): argument checks,
+// workspace layout, launches. No device memory is allocated here; every buffer
+// comes from the caller.
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "common.h"
+#include "launch.h"
+#include "tr_sparseconv.h"
+
+using namespace trsc;
+
+namespace {
+
+constexpr uint32_t kHashMagic = 0x48534354u;  // "TCSH"
+constexpr uint32_t kKmapMagic = 0x4D4B4354u;  // "TCKM"
+constexpr int64_t kMaxN = int64_t(1) << 30;  // table capacity 2^31 slots at most
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* where) {
+  return fail(TR_SC_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+uint32_t table_capacity(int64_t n) {  // power of two >= 4n (at most 2^31 >= 2n), at least 16
+  uint64_t p = 16;
+  while (p < uint64_t(4 * n) && p < (uint64_t(1) << 31)) p <<= 1;
+  return uint32_t(p);
+}
+
+int log2_u64(uint64_t v) {
+  int r = 0;
+  while ((uint64_t(1) << (r + 1)) <= v) ++r;
+  return r;
+}
+
+// Hash workspace: header | keys[2][n] | rows[2][n] | radix counts | digit
+// totals | OR/AND partials | slots[P].
+struct HashLayout {
+  size_t hdr, keys0, keys1, rows0, rows1, counts, totals, parts, slots, total;
+  uint32_t cap;
+};
+
+HashLayout hash_layout(int64_t n) {
+  HashLayout l{};
+  const size_t un = size_t(n);
+  size_t o = 0;
+  l.hdr = o;
+  o += align_up(sizeof(HashHeader), 256);
+  l.keys0 = o;
+  o += align_up(un * 8, 256);
+  l.keys1 = o;
+  o += align_up(un * 8, 256);
+  l.rows0 = o;
+  o += align_up(un * 4, 256);
+  l.rows1 = o;
+  o += align_up(un * 4, 256);
+  l.counts = o;
+  o += align_up(size_t(sort_blocks(n)) * 256 * 4, 256);
+  l.totals = o;
+  o += 256 * 4;
+  l.parts = o;
+  o += align_up(size_t(pack_partials(n)) * 16, 256);
+  l.cap = table_capacity(n);
+  l.slots = o;
+  o += size_t(l.cap) * sizeof(Slot);
+  l.total = o;
+  return l;
+}
+
+}  // namespace
+
+struct tr_sc_hash {
+  uint32_t magic;
+  int64_t n;
+  HashHeader* hdr;
+  TableRef table;
+  const uint64_t* skeys;  // sorted keys
+  const int32_t* srows;   // sorted position -> caller row
+};
+
+struct tr_sc_kmap {
+  uint32_t magic;
+  int64_t n;
+  const int32_t* nbr;
+  const int32_t* srows;
+  const uint32_t* mask;
+};
+
+extern "C" {
+
+int tr_sparseconv_version(void) { return (0 << 16) | 1; }
+
+const char* tr_sparseconv_last_error(void) { return g_last_error.c_str(); }
+
+size_t tr_sparseconv_hash_workspace_bytes(int64_t n) {
+  if (n < 0 || n > kMaxN) return 0;
+  return hash_layout(n).total;
+}
+
+int tr_sparseconv_build_hash(const int32_t* coords, int64_t n, void* workspace, size_t ws_bytes,
+                             void* stream, tr_sc_hash** out) {
+  if (out == nullptr) return fail(TR_SC_ERR_INVALID_ARG, "build_hash: out is NULL");
+  *out = nullptr;
+  if (n < 0 || n > kMaxN) return fail(TR_SC_ERR_INVALID_ARG, "build_hash: n = %lld out of [0, 2^30]", (long long)n);
+  if (n > 0 && coords == nullptr) return fail(TR_SC_ERR_INVALID_ARG, "build_hash: coords is NULL");
+  if (workspace == nullptr) return fail(TR_SC_ERR_INVALID_ARG, "build_hash: workspace is NULL");
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+    return fail(TR_SC_ERR_INVALID_ARG, "build_hash: workspace not 256-byte aligned");
+  if (reinterpret_cast<uintptr_t>(coords) % 16 != 0)
+    return fail(TR_SC_ERR_INVALID_ARG, "build_hash: coords not 16-byte aligned");
+  const HashLayout l = hash_layout(n);
+  if (ws_bytes < l.total)
+    return fail(TR_SC_ERR_WORKSPACE, "build_hash: workspace %zu bytes < %zu needed", ws_bytes, l.total);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  HashHeader* hdr = reinterpret_cast<HashHeader*>(ws + l.hdr);
+  uint64_t* keys[2] = {reinterpret_cast<uint64_t*>(ws + l.keys0), reinterpret_cast<uint64_t*>(ws + l.keys1)};
+  int32_t* rows[2] = {reinterpret_cast<int32_t*>(ws + l.rows0), reinterpret_cast<int32_t*>(ws + l.rows1)};
+  uint32_t* counts = reinterpret_cast<uint32_t*>(ws + l.counts);
+  uint32_t* totals = reinterpret_cast<uint32_t*>(ws + l.totals);
+  unsigned long long* parts = reinterpret_cast<unsigned long long*>(ws + l.parts);
+  Slot* slots = reinterpret_cast<Slot*>(ws + l.slots);
+
+  hipError_t e = launch_pack(coords, n, keys[0], rows[0], parts, hdr, st);
+  if (e != hipSuccess) return hip_fail(e, "build_hash: pack");
+  // One read-back: the range flag and which key bits vary (they set the number
+  // of radix passes).
+  HashHeader host{};
+  e = hipMemcpyAsync(&host, hdr, sizeof(HashHeader), hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return hip_fail(e, "build_hash: read-back");
+  if (host.flags & kFlagCoordRange)
+    return fail(TR_SC_ERR_COORD_RANGE, "build_hash: a coordinate component is outside [0, 65536)");
+
+  int cur = 0;
+  if (n > 1) {
+    const uint64_t vary = host.or_bits ^ host.and_bits;
+    uint8_t pos[64];
+    int nv = 0;
+    for (int b = 0; b < 64; ++b)
+      if ((vary >> b) & 1u) pos[nv++] = uint8_t(b);
+    for (int p0 = 0; p0 < nv; p0 += 8) {
+      DigitSel sel{};
+      sel.nbits = nv - p0 < 8 ? nv - p0 : 8;
+      for (int j = 0; j < sel.nbits; ++j) sel.pos[j] = pos[p0 + j];
+      e = launch_sort_pass(keys[cur], rows[cur], keys[cur ^ 1], rows[cur ^ 1], n, sel, counts, totals, st);
+      if (e != hipSuccess) return hip_fail(e, "build_hash: sort");
+      cur ^= 1;
+    }
+  }
+  const uint32_t shift = uint32_t(64 - log2_u64(uint64_t(l.cap)));
+  e = launch_insert(keys[cur], rows[cur], n, slots, l.cap - 1, shift, hdr, st);
+  if (e != hipSuccess) return hip_fail(e, "build_hash: insert");
+
+  tr_sc_hash* h = new tr_sc_hash;
+  h->magic = kHashMagic;
+  h->n = n;
+  h->hdr = hdr;
+  h->table = TableRef{slots, l.cap - 1, shift};
+  h->skeys = keys[cur];
+  h->srows = rows[cur];
+  *out = h;
+  return TR_SC_OK;
+}
+
+int tr_sparseconv_status(const tr_sc_hash* h, void* stream) {
+  if (h == nullptr || h->magic != kHashMagic) return fail(TR_SC_ERR_INVALID_ARG, "status: bad hash handle");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  uint32_t flags = 0;
+  hipError_t e = hipMemcpyAsync(&flags, &h->hdr->flags, sizeof(flags), hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return hip_fail(e, "status");
+  if (flags & kFlagCoordRange) return fail(TR_SC_ERR_COORD_RANGE, "status: coordinate out of range");
+  if (flags & kFlagDuplicate) return fail(TR_SC_ERR_DUPLICATE, "status: duplicate coordinates");
+  if (flags & kFlagCapacity) return fail(TR_SC_ERR_CAPACITY, "status: hash table full");
+  return TR_SC_OK;
+}
+
+int64_t tr_sparseconv_hash_size(const tr_sc_hash* h) {
+  if (h == nullptr || h->magic != kHashMagic) return -1;
+  return h->n;
+}
+
+int tr_sparseconv_hash_lookup(const tr_sc_hash* h, const int32_t* q, int64_t nq, int32_t* idx,
+                              void* stream) {
+  if (h == nullptr || h->magic != kHashMagic) return fail(TR_SC_ERR_INVALID_ARG, "hash_lookup: bad hash handle");
+  if (nq < 0) return fail(TR_SC_ERR_INVALID_ARG, "hash_lookup: nq < 0");
+  if (nq > 0 && (q == nullptr || idx == nullptr)) return fail(TR_SC_ERR_INVALID_ARG, "hash_lookup: NULL buffer");
+  if (reinterpret_cast<uintptr_t>(q) % 16 != 0)
+    return fail(TR_SC_ERR_INVALID_ARG, "hash_lookup: queries not 16-byte aligned");
+  hipError_t e = launch_lookup(h->table, h->hdr, q, nq, idx, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "hash_lookup");
+  return TR_SC_OK;
+}
+
+int tr_sparseconv_hash_sorted_rows(const tr_sc_hash* h, int32_t* perm, void* stream) {
+  if (h == nullptr || h->magic != kHashMagic) return fail(TR_SC_ERR_INVALID_ARG, "hash_sorted_rows: bad hash handle");
+  if (h->n == 0) return TR_SC_OK;
+  if (perm == nullptr) return fail(TR_SC_ERR_INVALID_ARG, "hash_sorted_rows: perm is NULL");
+  hipError_t e = hipMemcpyAsync(perm, h->srows, size_t(h->n) * 4, hipMemcpyDeviceToDevice,
+                                static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "hash_sorted_rows");
+  return TR_SC_OK;
+}
+
+void tr_sparseconv_hash_destroy(tr_sc_hash* h) {
+  if (h != nullptr && h->magic == kHashMagic) {
+    h->magic = 0;
+    delete h;
+  }
+}
+
+size_t tr_sparseconv_kmap_workspace_bytes(int64_t n) {
+  if (n < 0 || n > kMaxN) return 0;
+  return align_up(size_t(n) * 4, 256) + 256;
+}
+
+int tr_sparseconv_build_kernel_map(const tr_sc_hash* h, int32_t* nbr, void* workspace, size_t ws_bytes,
+                                   void* stream, tr_sc_kmap** out) {
+  if (out == nullptr) return fail(TR_SC_ERR_INVALID_ARG, "build_kernel_map: out is NULL");
+  *out = nullptr;
+  if (h == nullptr || h->magic != kHashMagic) return fail(TR_SC_ERR_INVALID_ARG, "build_kernel_map: bad hash handle");
+  if (workspace == nullptr) return fail(TR_SC_ERR_INVALID_ARG, "build_kernel_map: workspace is NULL");
+  if (h->n > 0 && nbr == nullptr) return fail(TR_SC_ERR_INVALID_ARG, "build_kernel_map: nbr is NULL");
+  const size_t need = tr_sparseconv_kmap_workspace_bytes(h->n);
+  if (ws_bytes < need)
+    return fail(TR_SC_ERR_WORKSPACE, "build_kernel_map: workspace %zu bytes < %zu needed", ws_bytes, need);
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+    return fail(TR_SC_ERR_INVALID_ARG, "build_kernel_map: workspace not 256-byte aligned");
+  uint32_t* mask = static_cast<uint32_t*>(workspace);
+  hipError_t e = launch_kmap(h->skeys, h->srows, h->n, h->table, h->hdr, nbr, mask,
+                             static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "build_kernel_map");
+  tr_sc_kmap* m = new tr_sc_kmap;
+  m->magic = kKmapMagic;
+  m->n = h->n;
+  m->nbr = nbr;
+  m->srows = h->srows;
+  m->mask = mask;
+  *out = m;
+  return TR_SC_OK;
+}
+
+void tr_sparseconv_kmap_destroy(tr_sc_kmap* m) {
+  if (m != nullptr && m->magic == kKmapMagic) {
+    m->magic = 0;
+    delete m;
+  }
+}
+
+size_t tr_sparseconv_packed_weights_bytes(int c_in, int c_out, int dtype) {
+  if (c_in <= 0 || c_out <= 0) return 0;
+  const size_t elems = size_t(27) * size_t(c_in) * size_t(c_out);
+  if (dtype == TR_SC_BF16) return align_up(elems * 2, 256);
+  if (dtype == TR_SC_F32) return align_up(elems * 4, 256);
+  return 0;
+}
+
+size_t tr_sparseconv_forward_workspace_bytes(int c_in, int c_out, int dtype) {
+  if (dtype == TR_SC_F32) return 0;  // the fp32 path reads w in place
+  return tr_sparseconv_packed_weights_bytes(c_in, c_out, dtype);
+}
+
+namespace {
+
+int check_channels(const char* who, int c_in, int c_out, int dtype) {
+  if (c_in <= 0 || c_out <= 0) return fail(TR_SC_ERR_INVALID_ARG, "%s: c_in = %d, c_out = %d", who, c_in, c_out);
+  if (dtype != TR_SC_F32 && dtype != TR_SC_BF16) return fail(TR_SC_ERR_UNSUPPORTED, "%s: dtype %d", who, dtype);
+  if (dtype == TR_SC_BF16 && (c_in % 8 != 0 || c_out % 8 != 0))
+    return fail(TR_SC_ERR_UNSUPPORTED, "%s: bf16 needs c_in and c_out multiples of 8 (got %d, %d)", who, c_in,
+                c_out);
+  return TR_SC_OK;
+}
+
+bool misaligned16(const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 != 0; }
+
+// Launches the gather-GEMM of an already validated call.
+int run_forward(const char* who, const tr_sc_kmap* m, const void* x, const void* wp, void* y, int c_in,
+                int c_out, int dtype, hipStream_t st) {
+  if (x == nullptr || wp == nullptr || y == nullptr) return fail(TR_SC_ERR_INVALID_ARG, "%s: NULL tensor", who);
+  if (int64_t(m->n) * c_out >= (int64_t(1) << 40) || int64_t(m->n) * c_in >= (int64_t(1) << 40))
+    return fail(TR_SC_ERR_UNSUPPORTED, "%s: tensor too large", who);
+  ConvArgs a{m->nbr, m->srows, m->mask, m->n, x, wp, y, c_in, c_out};
+  hipError_t e;
+  if (dtype == TR_SC_F32) {
+    e = launch_forward_simple_f32(a, st);
+  } else {
+    if (misaligned16(x) || misaligned16(y) || misaligned16(wp))
+      return fail(TR_SC_ERR_INVALID_ARG, "%s: bf16 x, y and packed weights must be 16-byte aligned", who);
+    e = launch_forward_mfma_bf16(a, wp, st);
+  }
+  if (e != hipSuccess) return hip_fail(e, who);
+  return TR_SC_OK;
+}
+
+}  // namespace
+
+int tr_sparseconv_pack_weights(const void* w, int c_in, int c_out, int dtype, void* wp, size_t wp_bytes,
+                               void* stream) {
+  const int c = check_channels("pack_weights", c_in, c_out, dtype);
+  if (c != TR_SC_OK) return c;
+  if (w == nullptr || wp == nullptr) return fail(TR_SC_ERR_INVALID_ARG, "pack_weights: NULL pointer");
+  const size_t need = tr_sparseconv_packed_weights_bytes(c_in, c_out, dtype);
+  if (wp_bytes < need) return fail(TR_SC_ERR_WORKSPACE, "pack_weights: %zu bytes < %zu needed", wp_bytes, need);
+  if (misaligned16(wp)) return fail(TR_SC_ERR_INVALID_ARG, "pack_weights: wp not 16-byte aligned");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (dtype == TR_SC_BF16)
+    e = launch_pack_weights(w, wp, c_in, c_out, st);
+  else
+    e = hipMemcpyAsync(wp, w, size_t(27) * c_in * c_out * 4, hipMemcpyDeviceToDevice, st);
+  if (e != hipSuccess) return hip_fail(e, "pack_weights");
+  return TR_SC_OK;
+}
+
+int tr_sparseconv_forward_packed(const tr_sc_kmap* m, const void* x, const void* wp, void* y, int c_in,
+                                 int c_out, int dtype, void* stream) {
+  if (m == nullptr || m->magic != kKmapMagic)
+    return fail(TR_SC_ERR_INVALID_ARG, "forward_packed: bad kernel-map handle");
+  const int c = check_channels("forward_packed", c_in, c_out, dtype);
+  if (c != TR_SC_OK) return c;
+  if (m->n == 0) return TR_SC_OK;
+  return run_forward("forward_packed", m, x, wp, y, c_in, c_out, dtype, static_cast<hipStream_t>(stream));
+}
+
+int tr_sparseconv_forward(const tr_sc_kmap* m, const void* x, const void* w, void* y, int c_in, int c_out,
+                          int dtype, void* workspace, size_t ws_bytes, void* stream) {
+  if (m == nullptr || m->magic != kKmapMagic) return fail(TR_SC_ERR_INVALID_ARG, "forward: bad kernel-map handle");
+  const int c = check_channels("forward", c_in, c_out, dtype);
+  if (c != TR_SC_OK) return c;
+  const size_t need = tr_sparseconv_forward_workspace_bytes(c_in, c_out, dtype);
+  if (ws_bytes < need) return fail(TR_SC_ERR_WORKSPACE, "forward: workspace %zu bytes < %zu needed", ws_bytes, need);
+  if (need > 0 && workspace == nullptr) return fail(TR_SC_ERR_INVALID_ARG, "forward: workspace is NULL");
+  if (m->n == 0) return TR_SC_OK;
+  if (w == nullptr) return fail(TR_SC_ERR_INVALID_ARG, "forward: NULL tensor");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (dtype == TR_SC_F32) return run_forward("forward", m, x, w, y, c_in, c_out, dtype, st);
+  if (misaligned16(workspace)) return fail(TR_SC_ERR_INVALID_ARG, "forward: workspace not 16-byte aligned");
+  hipError_t e = launch_pack_weights(w, workspace, c_in, c_out, st);
+  if (e != hipSuccess) return hip_fail(e, "forward: pack");
+  return run_forward("forward", m, x, workspace, y, c_in, c_out, dtype, st);
+}
+
+}  // extern "C"

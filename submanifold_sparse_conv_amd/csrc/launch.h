@@ -1,0 +1,51 @@
+// Host-side launchers of the library's kernels (internal).
+#pragma once
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "common.h"
+
+namespace trsc {
+
+// Radix digit of one sort pass: bits key[pos[0]], ..., key[pos[nbits-1]],
+// least significant first. The positions are the bits that differ between keys.
+struct DigitSel {
+  uint8_t pos[8];
+  int32_t nbits;
+};
+
+int64_t sort_blocks(int64_t n);    // radix-sort workgroups (tiles) for n keys
+int64_t pack_partials(int64_t n);  // OR/AND partial pairs written by the packing pass
+hipError_t launch_pack(const int32_t* coords, int64_t n, uint64_t* keys, int32_t* rows,
+                       unsigned long long* part, HashHeader* hdr, hipStream_t st);
+hipError_t launch_sort_pass(const uint64_t* kin, const int32_t* vin, uint64_t* kout, int32_t* vout,
+                            int64_t n, const DigitSel& sel, uint32_t* counts, uint32_t* totals,
+                            hipStream_t st);
+hipError_t launch_insert(const uint64_t* keys, const int32_t* rows, int64_t n, Slot* slots,
+                         uint32_t cap_mask, uint32_t shift, HashHeader* hdr, hipStream_t st);
+hipError_t launch_lookup(const TableRef& t, const HashHeader* hdr, const int32_t* q, int64_t nq,
+                         int32_t* out, hipStream_t st);
+
+hipError_t launch_kmap(const uint64_t* skeys, const int32_t* srows, int64_t n, const TableRef& t,
+                       const HashHeader* hdr, int32_t* nbr, uint32_t* mask, hipStream_t st);
+
+// Forward kernels. `srows` is the Morton order (sorted position -> caller row),
+// `mask` the per-sorted-voxel 27-bit neighbour masks.
+struct ConvArgs {
+  const int32_t* nbr;   // [n, 27] caller order
+  const int32_t* srows; // [n]
+  const uint32_t* mask; // [n] Morton order
+  int64_t n;
+  const void* x;
+  const void* w;
+  void* y;
+  int c_in, c_out;
+};
+hipError_t launch_forward_simple_f32(const ConvArgs& a, hipStream_t st);
+hipError_t launch_forward_simple_bf16(const ConvArgs& a, hipStream_t st);
+// wp[k][co][ci] = w[k][ci][co] (bf16), the matrix-core operand layout.
+hipError_t launch_pack_weights(const void* w, void* wp, int c_in, int c_out, hipStream_t st);
+hipError_t launch_forward_mfma_bf16(const ConvArgs& a, const void* wp, hipStream_t st);
+
+}  // namespace trsc

@@ -1,0 +1,247 @@
+"""Parity of the HIP path with the CPU oracle, through the C ABI, on the GPU.
+
+Kernel maps and hash lookups are compared bit for bit. Features are compared
+element by element (every row at small sizes, sampled rows plus the ragged
+tail at the full workload sizes) with the max relative error of helpers.max_rel
+against 2e-2 (bf16) and 1e-4 (fp32).
+"""
+import functools
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gen import workloads as W
+from tests.helpers import TOL, max_rel, morton_keys_numpy, sample_rows, say
+
+pytestmark = pytest.mark.gpu
+
+sc = pytest.importorskip("submanifold_sparse_conv_amd")
+DEV = "cuda:0"
+TORCH_DT = {"f32": torch.float32, "bf16": torch.bfloat16}
+
+
+@functools.lru_cache(maxsize=None)
+def workload(name, off=0, order="raster"):
+    return W.make(name, seed_offset=off, order=order)
+
+
+@functools.lru_cache(maxsize=None)
+def oracle_map(name, off=0, order="raster"):
+    return oracle.kernel_map(workload(name, off, order).coords)
+
+
+def to_dev(wl):
+    dt = TORCH_DT[wl.dtype]
+    c = torch.from_numpy(wl.coords).to(DEV)
+    x = torch.from_numpy(wl.x).to(DEV).to(dt)   # exact: values are representable
+    w = torch.from_numpy(wl.w).to(DEV).to(dt)
+    return c, x, w
+
+
+def run_all(coords, x, w):
+    h = sc.build_hash(coords)
+    m = sc.build_kernel_map(h)
+    y = sc.forward(m, x, w)
+    torch.cuda.synchronize()
+    return h, m, y
+
+
+MAP_CASES = ([(n, 0, "raster") for n in W.CONFIG_ORDER]
+             + [(n, 100, "shuffled") for n in W.CONFIG_ORDER]
+             + [("T", 200, "shuffled"), ("S", 200, "raster")])
+
+
+@pytest.mark.parametrize("name,off,order", MAP_CASES)
+def test_kernel_map_bitexact(name, off, order):
+    wl = workload(name, off, order)
+    say(f"[kmap] config={name} seed={wl.seed} order={order} n={wl.n}")
+    h = sc.build_hash(torch.from_numpy(wl.coords).to(DEV))
+    m = sc.build_kernel_map(h)
+    nbr = m.nbr.cpu().numpy()
+    np.testing.assert_array_equal(nbr, oracle_map(name, off, order))
+
+
+@pytest.mark.parametrize("name,off,order", [(n, 100, "shuffled") for n in W.CONFIG_ORDER])
+def test_hash_lookup_bitexact(name, off, order):
+    wl = workload(name, off, order)
+    say(f"[lookup] config={name} seed={wl.seed} n={wl.n}")
+    h = sc.build_hash(torch.from_numpy(wl.coords).to(DEV))
+    rng = np.random.default_rng(wl.seed)
+    q = np.concatenate([
+        wl.coords,
+        np.stack([rng.integers(0, wl.B + 1, 100000), rng.integers(-1, wl.D + 2, 100000),
+                  rng.integers(-1, wl.D + 2, 100000), rng.integers(-1, wl.D + 2, 100000)], 1),
+    ]).astype(np.int32)
+    got = h.lookup(torch.from_numpy(q).to(DEV)).cpu().numpy()
+    ref = oracle.Table(wl.coords).lookup(q)
+    np.testing.assert_array_equal(got, ref)
+    np.testing.assert_array_equal(got[:wl.n], np.arange(wl.n))
+
+
+@pytest.mark.parametrize("name,off,order", [("S", 100, "shuffled"), ("X", 0, "raster"),
+                                            ("W", 100, "shuffled")])
+def test_morton_order_bitexact(name, off, order):
+    wl = workload(name, off, order)
+    say(f"[morton] config={name} seed={wl.seed} n={wl.n}")
+    h = sc.build_hash(torch.from_numpy(wl.coords).to(DEV))
+    perm = h.sorted_rows().cpu().numpy()
+    np.testing.assert_array_equal(perm, np.argsort(morton_keys_numpy(wl.coords), kind="stable"))
+
+
+FWD_CASES = ([(n, 0, "raster") for n in W.CONFIG_ORDER]
+             + [(n, 100, "shuffled") for n in W.CONFIG_ORDER]
+             + [("S", 200, "raster"), ("L", 200, "shuffled")])
+
+
+@pytest.mark.parametrize("name,off,order", FWD_CASES)
+def test_forward_parity(name, off, order):
+    wl = workload(name, off, order)
+    say(f"[forward] config={name} seed={wl.seed} order={order} n={wl.n} "
+        f"c={wl.c_in}->{wl.c_out} {wl.dtype}")
+    c, x, w = to_dev(wl)
+    _, m, y = run_all(c, x, w)
+    nbr = oracle_map(name, off, order)
+    np.testing.assert_array_equal(m.nbr.cpu().numpy(), nbr)
+    if wl.n <= 20000:
+        rows = np.arange(wl.n)
+    else:
+        rows = sample_rows(wl.n, 1500 if wl.c_in >= 1024 else 4000, wl.seed)
+    ref = oracle.forward(nbr, wl.x, wl.w, rows=rows)
+    got = y.float().cpu().numpy()[rows]
+    err = max_rel(got, ref)
+    say(f"    max_rel={err:.3e} (unfloored max abs {np.abs(got - ref).max():.3e}, "
+        f"normwise {np.abs(got - ref).max() / np.abs(ref).max():.3e})")
+    assert err <= TOL[wl.dtype]
+
+
+SMALL_SHAPES = [(8, 8, "f32"), (3, 5, "f32"), (8, 8, "bf16"), (16, 8, "bf16"), (64, 64, "bf16"),
+                (32, 96, "bf16"), (128, 128, "bf16"), (64, 32, "bf16"), (256, 64, "bf16")]
+
+
+@pytest.mark.parametrize("n", [1, 63, 64, 65, 257, 1000, 4097])
+@pytest.mark.parametrize("c_in,c_out,dtype", SMALL_SHAPES)
+def test_forward_small_all_rows(n, c_in, c_out, dtype):
+    rng = np.random.default_rng(n * 1000 + c_in + c_out)
+    coords = W.random_sparse(rng, n, D=14 if n > 500 else 7, B=2)
+    coords = coords[rng.permutation(n)]
+    wl = W.custom(coords, c_in, c_out, dtype, seed=n + c_in)
+    say(f"[small] n={n} c={c_in}->{c_out} {dtype}")
+    c, x, w = to_dev(wl)
+    _, m, y = run_all(c, x, w)
+    nbr, ref = oracle.conv(coords, wl.x, wl.w)
+    np.testing.assert_array_equal(m.nbr.cpu().numpy(), nbr)
+    assert max_rel(y.float().cpu().numpy(), ref) <= TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("c", [8, 64, 128])
+def test_identity_kernel_bitexact(dtype, c):
+    wl = workload("S", 100, "shuffled")
+    say(f"[identity] c={c} {dtype}")
+    dt = TORCH_DT[dtype]
+    xv, _ = W.make_values(wl.n, c, c, dtype, np.random.default_rng(c))
+    x = torch.from_numpy(xv).to(DEV).to(dt)
+    w = torch.zeros((27, c, c), dtype=dt, device=DEV)
+    w[13] = torch.eye(c, dtype=dt, device=DEV)
+    _, _, y = run_all(torch.from_numpy(wl.coords).to(DEV), x, w)
+    assert torch.equal(y.view(torch.int16) if dtype == "bf16" else y.view(torch.int32),
+                       x.view(torch.int16) if dtype == "bf16" else x.view(torch.int32))
+
+
+@pytest.mark.parametrize("name", ["S", "L"])
+def test_deterministic_bits(name):
+    wl = workload(name, 100, "shuffled")
+    say(f"[determinism] config={name}")
+    c, x, w = to_dev(wl)
+    _, m1, y1 = run_all(c, x, w)
+    _, m2, y2 = run_all(c, x, w)
+    assert torch.equal(m1.nbr, m2.nbr)
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+
+
+def test_translation_invariance():
+    wl = workload("S", 200, "raster")
+    say("[translation] config=S")
+    c, x, w = to_dev(wl)
+    _, m1, y1 = run_all(c, x, w)
+    shift = torch.tensor([0, 1000, 37, 60000], dtype=torch.int32, device=DEV)
+    _, m2, y2 = run_all(c + shift, x, w)
+    assert torch.equal(m1.nbr, m2.nbr)
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+
+
+def test_empty_and_single():
+    say("[edge] empty and single voxel")
+    c = torch.zeros((0, 4), dtype=torch.int32, device=DEV)
+    x = torch.zeros((0, 16), dtype=torch.bfloat16, device=DEV)
+    w = torch.zeros((27, 16, 8), dtype=torch.bfloat16, device=DEV)
+    h, m, y = run_all(c, x, w)
+    assert m.nbr.shape == (0, 27) and y.shape == (0, 8)
+    wl = W.custom(np.array([[3, 9, 9, 9]], np.int32), 16, 8, "bf16", seed=4)
+    cc, xx, ww = to_dev(wl)
+    _, m, y = run_all(cc, xx, ww)
+    assert m.nbr.cpu().numpy().tolist() == [[-1] * 13 + [0] + [-1] * 13]
+    ref = oracle.conv(wl.coords, wl.x, wl.w)[1]
+    assert max_rel(y.float().cpu().numpy(), ref) <= TOL["bf16"]
+
+
+def test_coordinate_extremes():
+    say("[edge] coordinates at 0 and 65535, the all-ones key")
+    top = 65535
+    pts = [[top, top, top, top], [top, top - 1, top, top], [top, top, top - 1, top - 1],
+           [0, 0, 0, 0], [0, 1, 1, 1], [0, 0, 0, 1], [top, 0, top, 0], [1, top, top, top]]
+    coords = np.array(pts, np.int32)
+    wl = W.custom(coords, 8, 8, "f32", seed=1)
+    c, x, w = to_dev(wl)
+    h, m, y = run_all(c, x, w)
+    nbr, ref = oracle.conv(coords, wl.x, wl.w)
+    np.testing.assert_array_equal(m.nbr.cpu().numpy(), nbr)
+    assert max_rel(y.cpu().numpy(), ref) <= TOL["f32"]
+    np.testing.assert_array_equal(h.lookup(c).cpu().numpy(), np.arange(len(pts)))
+
+
+def test_errors():
+    say("[edge] error codes")
+    dup = torch.tensor([[0, 1, 2, 3], [0, 5, 5, 5], [0, 1, 2, 3]], dtype=torch.int32, device=DEV)
+    with pytest.raises(sc.TrSparseConvError) as e:
+        sc.build_hash(dup)
+    assert e.value.code == -3
+    dup_top = torch.tensor([[65535] * 4, [65535] * 4], dtype=torch.int32, device=DEV)
+    with pytest.raises(sc.TrSparseConvError) as e:
+        sc.build_hash(dup_top)
+    assert e.value.code == -3
+    for bad in ([0, -1, 2, 3], [0, 1, 65536, 3], [70000, 1, 2, 3]):
+        c = torch.tensor([[0, 0, 0, 0], bad], dtype=torch.int32, device=DEV)
+        with pytest.raises(sc.TrSparseConvError) as e:
+            sc.build_hash(c)
+        assert e.value.code == -2
+    c = torch.tensor([[0, 0, 0, 0]], dtype=torch.int32, device=DEV)
+    m = sc.build_kernel_map(sc.build_hash(c))
+    with pytest.raises(sc.TrSparseConvError) as e:
+        sc.forward(m, torch.zeros((1, 12), dtype=torch.bfloat16, device=DEV),
+                   torch.zeros((27, 12, 8), dtype=torch.bfloat16, device=DEV))
+    assert e.value.code == -6
+
+
+@pytest.mark.parametrize("name", ["S", "X"])
+def test_forward_packed_matches_forward(name):
+    wl = workload(name, 100, "shuffled")
+    say(f"[packed] config={name}")
+    c, x, w = to_dev(wl)
+    h, m, y = run_all(c, x, w)
+    wp = sc.pack_weights(w)
+    y2 = sc.forward_packed(m, x, wp)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
+
+
+def test_forward_packed_f32():
+    wl = workload("T", 100, "shuffled")
+    say("[packed] config=T f32")
+    c, x, w = to_dev(wl)
+    h, m, y = run_all(c, x, w)
+    y2 = sc.forward_packed(m, x, sc.pack_weights(w))
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int32), y2.view(torch.int32))
