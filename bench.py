@@ -46,7 +46,22 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=8.0, help="target wall time of the oracle forward sample")
     p.add_argument("--gemm-reps", type=int, default=50)
+    p.add_argument("--copy-probe-mib", type=int, default=0,
+                   help="only run a plain device copy of this many MiB (counter calibration)")
     return p.parse_args()
+
+
+def copy_probe(mib):
+    """A plain device-to-device copy of known size, the reference that scales
+    the HBM byte counters (FETCH_SIZE / WRITE_SIZE) of the profiled kernels."""
+    import torch
+    n = mib * (1 << 20) // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_read": n * 4, "copy_probe_bytes_written": n * 4, "reps": 5}))
 
 
 def sha_of(path):
@@ -160,6 +175,9 @@ def traffic_entry():
 
 def main():
     args = parse()
+    if args.copy_probe_mib:
+        copy_probe(args.copy_probe_mib)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); multi-GPU "
               "sharding of this path is described in DESIGN.md but not built.", file=sys.stderr)

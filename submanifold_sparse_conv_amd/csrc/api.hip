@@ -266,7 +266,7 @@ void tr_sparseconv_kmap_destroy(tr_sc_kmap* m) {
 size_t tr_sparseconv_packed_weights_bytes(int c_in, int c_out, int dtype) {
   if (c_in <= 0 || c_out <= 0) return 0;
   const size_t elems = size_t(27) * size_t(c_in) * size_t(c_out);
-  if (dtype == TR_SC_BF16) return align_up(elems * 2, 256);
+  if (dtype == TR_SC_BF16) return size_t(packed_weight_elems(c_in, c_out)) * 2 + 256;  // + zero block
   if (dtype == TR_SC_F32) return align_up(elems * 4, 256);
   return 0;
 }

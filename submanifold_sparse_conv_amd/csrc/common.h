@@ -105,6 +105,15 @@ __device__ inline int32_t table_find(const TableRef& t, uint64_t key, int32_t sp
   return probe_from(t, key, s, load_slot(t.slots, s));
 }
 
+// Workgroup index -> work index such that each XCD (workgroups are dealt to
+// the 8 XCDs of the chip round-robin) gets one contiguous run of work items, so
+// neighbouring work (Morton-adjacent voxels) shares that XCD's L2.
+__device__ inline int xcd_remap(int bid, int grid) {
+  const int xcd = bid & 7, local = bid >> 3;
+  const int per = grid >> 3, rem = grid & 7;
+  return xcd * per + (xcd < rem ? xcd : rem) + local;
+}
+
 // ---------------------------------------------------------------------------
 // bf16 helpers (bit patterns in uint16_t).
 // ---------------------------------------------------------------------------

@@ -20,7 +20,10 @@
 // already in flight into registers.
 //
 // Weights are first re-laid out to [27][C_out][C_in] (input channels
-// contiguous), the operand order of the matrix instruction.
+// contiguous), the operand order of the matrix instruction, followed by a
+// 256-byte block of zeros.
+#include <cstdlib>
+
 #include "common.h"
 #include "launch.h"
 
@@ -53,43 +56,58 @@ __global__ __launch_bounds__(kThreads) void pack_weights(const uint16_t* __restr
   }
 }
 
-// Workgroup index -> tile index so that each XCD (workgroups are dealt to the
-// 8 XCDs round-robin) works through one contiguous run of tiles, keeping the
-// gathered rows of neighbouring tiles in its own L2.
-__device__ inline int xcd_tile(int bid, int grid) {
-  const int xcd = bid & 7, local = bid >> 3;
-  const int per = grid >> 3, rem = grid & 7;
-  return xcd * per + (xcd < rem ? xcd : rem) + local;
+// The 256 zero bytes after the packed weights: the copy source of absent
+// neighbours and of channels past c_in.
+__global__ void zero_block(uint16_t* z) {
+  reinterpret_cast<uint4*>(z)[threadIdx.x & 15] = make_uint4(0u, 0u, 0u, 0u);
 }
 
-template <int TM, int TN, int WM, int WN, int KC>
-__global__ __launch_bounds__(kThreads) void fwd_mfma(const int32_t* __restrict__ nbr,
+// Direct global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4):
+// lane l of the wave writes lds_base + 16 * l. `lds_base` must be wave-uniform.
+__device__ inline void copy16_to_lds(const void* g, void* lds_base) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(g),
+                                   (__attribute__((address_space(3))) void*)(lds_base), 16, 0, 0);
+}
+
+// Staged operand rows are 64 bf16 = 128 bytes = eight 16-byte chunks; chunk c
+// of row r sits at chunk position c ^ (r & 7), so eight consecutive rows read
+// at one logical chunk hit eight different bank groups.
+__device__ inline int swz(int row, int chunk) { return chunk ^ (row & 7); }
+
+__device__ inline void stage_barrier() {
+  __builtin_amdgcn_s_waitcnt(0x0F71);
+  asm volatile("s_barrier" ::: "memory");
+}
+
+template <int TM, int TN, int WM, int WN>
+__global__ __launch_bounds__(kThreads, 2) void fwd_mfma(const int32_t* __restrict__ nbr,
                                                      const int32_t* __restrict__ srows,
                                                      const uint32_t* __restrict__ vmask, int64_t n,
                                                      const uint16_t* __restrict__ x,
                                                      const uint16_t* __restrict__ wp,
+                                                     const uint16_t* __restrict__ zeros,
                                                      uint16_t* __restrict__ y, int c_in, int c_out,
                                                      int n_tiles_n) {
+  constexpr int KC = 64;                  // input channels per stage
+  constexpr int ROWB = KC * 2;            // bytes per staged row
   constexpr int WAVES_N = TN / WN;
   static_assert((TM / WM) * (TN / WN) == kThreads / 64, "four waves");
+  static_assert(TM % 8 == 0 && TN % 8 == 0, "8 rows per wave copy");
   constexpr int FM = WM / 16, FN = WN / 16;
-  constexpr int LDK = KC + 8;                          // padded LDS row (bf16 elements)
-  constexpr int CPR = KC / 8;                          // 16-byte chunks per staged row
-  constexpr int ACH = (TM * CPR + kThreads - 1) / kThreads;  // A chunks per thread
-  constexpr int BCH = (TN * CPR + kThreads - 1) / kThreads;  // B chunks per thread
-  constexpr int LDO = TN + 8;                          // padded output staging row
-  constexpr int STAGE = (TM + TN) * LDK;
-  constexpr int OUTS = TM * LDO;
-  constexpr int SMEM = STAGE > OUTS ? STAGE : OUTS;
-  __shared__ __attribute__((aligned(16))) uint16_t smem[SMEM];
+  constexpr int BUF = (TM + TN) * ROWB;   // bytes of one stage buffer
+  constexpr int OUTB = TM * TN * 2;       // output tile staged as bf16
+  // Two stage buffers as two distinct arrays: the compiler can then tell that
+  // the copies in flight into one do not alias the fragment reads of the other
+  // and does not wait for them. buf0 also stages the output tile.
+  __shared__ __attribute__((aligned(1024))) unsigned char buf0[BUF > OUTB ? BUF : OUTB];
+  __shared__ __attribute__((aligned(1024))) unsigned char buf1[BUF];
+  __shared__ __attribute__((aligned(1024))) unsigned char junk[1024];  // sink of the L2 touches
   __shared__ int32_t s_row[TM];
-  __shared__ int32_t s_src[27 * TM];  // gather source row per (active tap, tile row)
+  __shared__ int32_t s_src[27 * TM];      // gather source row per (active tap, tile row)
   __shared__ int32_t s_taps[27];
   __shared__ uint32_t s_mask;
-  uint16_t* sA = smem;
-  uint16_t* sB = smem + TM * LDK;
 
-  const int tile = xcd_tile(blockIdx.x, gridDim.x);
+  const int tile = xcd_remap(blockIdx.x, gridDim.x);
   const int64_t t0 = int64_t(tile / n_tiles_n) * TM;
   const int n0 = (tile % n_tiles_n) * TN;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -109,10 +127,7 @@ __global__ __launch_bounds__(kThreads) void fwd_mfma(const int32_t* __restrict__
   __syncthreads();
   const uint32_t tmask = s_mask;
   const int ntaps = __popc(tmask);
-  if (tid < 27) {
-    // position of tap tid in the compact list, if active
-    if ((tmask >> tid) & 1u) s_taps[__popc(tmask & ((1u << tid) - 1u))] = tid;
-  }
+  if (tid < 27 && ((tmask >> tid) & 1u)) s_taps[__popc(tmask & ((1u << tid) - 1u))] = tid;
   __syncthreads();
   for (int q = tid; q < TM * ntaps; q += kThreads) {
     const int r = q / ntaps, ti = q - r * ntaps;  // consecutive lanes read one row's taps
@@ -121,82 +136,121 @@ __global__ __launch_bounds__(kThreads) void fwd_mfma(const int32_t* __restrict__
   }
   __syncthreads();
 
+  const int nchunks = (c_in + KC - 1) / KC;
+  const int nstages = ntaps * nchunks;
+
+  // Issues the copies of stage st into `base`: each wave copy moves 8 staged
+  // rows (64 lanes x 16 bytes); lane l fills row 8i + l/8, chunk position
+  // l%8, i.e. logical chunk (l%8) ^ (row & 7).
+  auto issue_stage = [&](int st, unsigned char* base) {
+    const int ti = st / nchunks;
+    const int c0 = (st - ti * nchunks) * KC;
+    const int rl = lane >> 3;
+#pragma unroll
+    for (int i = wave; i < TM / 8; i += 4) {
+      const int row = i * 8 + rl;
+      const int c = c0 + swz(row, lane & 7) * 8;
+      const int32_t src = s_src[ti * TM + row];
+      const void* g = (src >= 0 && c < c_in) ? static_cast<const void*>(x + int64_t(src) * c_in + c)
+                                             : static_cast<const void*>(zeros);
+      copy16_to_lds(g, base + i * 1024);
+    }
+    const uint16_t* wk = wp + int64_t(s_taps[ti]) * c_out * c_in;
+#pragma unroll
+    for (int i = wave; i < TN / 8; i += 4) {
+      const int col = i * 8 + rl;
+      const int c = c0 + swz(col, lane & 7) * 8;
+      const void* g = (n0 + col < c_out && c < c_in)
+                          ? static_cast<const void*>(wk + int64_t(n0 + col) * c_in + c)
+                          : static_cast<const void*>(zeros);
+      copy16_to_lds(g, base + TM * ROWB + i * 1024);
+    }
+  };
+
+  // One 16-byte read per gathered row of stage st (each staged row is one
+  // 128-byte line), issued kAhead stages early so that the real copies find
+  // their lines in L2: every stage otherwise waits for its slowest lane, and
+  // some lane almost always misses. Each wave issues exactly one such read per
+  // stage (rows wave*TM/4 .. +TM/4), so "all but the last one" is vmcnt(1).
+  constexpr int kAhead = 4;
+  constexpr int RPW = TM / 4;
+  auto touch_stage = [&](int st) {
+    const int sst = st < nstages ? st : nstages - 1;
+    const int ti = sst / nchunks;
+    const int c = (sst - ti * nchunks) * KC;
+    const int row = wave * RPW + lane % RPW;
+    const int32_t src = s_src[ti * TM + row];
+    const void* g = (src >= 0 && c < c_in) ? static_cast<const void*>(x + int64_t(src) * c_in + c)
+                                           : static_cast<const void*>(zeros);
+    copy16_to_lds(g, junk);
+  };
+
   f32x4 acc[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int nchunks = (c_in + KC - 1) / KC;
-  const int nstages = ntaps * nchunks;
-  uint4 ra[ACH], rb[BCH];
-  // Global -> registers for stage st (tap s_taps[st / nchunks], chunk st % nchunks).
-  auto load_stage = [&](int st) {
-    const int ti = st / nchunks;
-    const int c0 = (st - ti * nchunks) * KC;
-    const uint16_t* wk = wp + int64_t(s_taps[ti]) * c_out * c_in;
+  auto compute_stage = [&](const unsigned char* bA) {
+    const unsigned char* bB = bA + TM * ROWB;
 #pragma unroll
-    for (int i = 0; i < ACH; ++i) {
-      const int q = tid + i * kThreads;
-      const int r = q / CPR, cc = q % CPR;
-      const int c = c0 + cc * 8;
-      ra[i] = make_uint4(0u, 0u, 0u, 0u);
-      if (q < TM * CPR) {
-        const int32_t src = s_src[ti * TM + r];
-        if (src >= 0 && c < c_in) ra[i] = *reinterpret_cast<const uint4*>(x + int64_t(src) * c_in + c);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < BCH; ++i) {
-      const int q = tid + i * kThreads;
-      const int col = q / CPR, cc = q % CPR;
-      const int co = n0 + col, c = c0 + cc * 8;
-      rb[i] = make_uint4(0u, 0u, 0u, 0u);
-      if (q < TN * CPR && co < c_out && c < c_in)
-        rb[i] = *reinterpret_cast<const uint4*>(wk + int64_t(co) * c_in + c);
-    }
-  };
-  auto store_stage = [&]() {
-#pragma unroll
-    for (int i = 0; i < ACH; ++i) {
-      const int q = tid + i * kThreads;
-      if (q < TM * CPR) *reinterpret_cast<uint4*>(sA + (q / CPR) * LDK + (q % CPR) * 8) = ra[i];
-    }
-#pragma unroll
-    for (int i = 0; i < BCH; ++i) {
-      const int q = tid + i * kThreads;
-      if (q < TN * CPR) *reinterpret_cast<uint4*>(sB + (q / CPR) * LDK + (q % CPR) * 8) = rb[i];
-    }
-  };
-
-  if (nstages > 0) load_stage(0);
-  for (int st = 0; st < nstages; ++st) {
-    store_stage();
-    __syncthreads();
-    if (st + 1 < nstages) load_stage(st + 1);  // in flight during the matrix work below
-#pragma unroll
-    for (int kk = 0; kk < KC; kk += 32) {
+    for (int kk = 0; kk < KC / 32; ++kk) {
+      const int chunk = kk * 4 + (lane >> 4);
       bf16x8 af[FM], bfr[FN];
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
-        af[i] = *reinterpret_cast<const bf16x8*>(sA + (wm * WM + i * 16 + (lane & 15)) * LDK + kk +
-                                                 (lane >> 4) * 8);
+      for (int i = 0; i < FM; ++i) {
+        const int r = wm * WM + i * 16 + (lane & 15);
+        af[i] = *reinterpret_cast<const bf16x8*>(bA + r * ROWB + swz(r, chunk) * 16);
+      }
 #pragma unroll
-      for (int j = 0; j < FN; ++j)
-        bfr[j] = *reinterpret_cast<const bf16x8*>(sB + (wn * WN + j * 16 + (lane & 15)) * LDK + kk +
-                                                  (lane >> 4) * 8);
+      for (int j = 0; j < FN; ++j) {
+        const int r = wn * WN + j * 16 + (lane & 15);
+        bfr[j] = *reinterpret_cast<const bf16x8*>(bB + r * ROWB + swz(r, chunk) * 16);
+      }
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
     }
-    __syncthreads();
-  }
+  };
 
-  // Epilogue: round to bf16 (nearest-even), stage the tile in LDS, store
-  // 16-byte pieces of each row at its caller index.
-  uint16_t* sO = smem;
+  // Two stages per trip: copies of the next stage fly while this one computes.
+  // Stage barrier: wait until all of this wave's copies except the newest
+  // touch have landed in LDS (s_waitcnt 0x0F71 = vmcnt(1)), then a plain
+  // s_barrier. __syncthreads() would add a release fence, and with copies in
+  // flight the fence waits for all of them (vmcnt(0)), touches included. The
+  // asm memory clobber keeps the compiler from moving LDS reads across it; the
+  // fragment reads of the previous stage are consumed by its matrix
+  // instructions before any wave reaches the barrier.
+  if (nstages > 0) {
+    for (int p = 1; p < kAhead; ++p) touch_stage(p);
+    issue_stage(0, buf0);
+    touch_stage(kAhead);
+  }
+  for (int st = 0; st < nstages; st += 2) {
+    stage_barrier();  // stage st is in buf0 for every wave; buf1 is free again
+    if (st + 1 < nstages) {
+      issue_stage(st + 1, buf1);
+      touch_stage(st + 1 + kAhead);
+    }
+    compute_stage(buf0);
+    stage_barrier();
+    if (st + 2 < nstages) {
+      issue_stage(st + 2, buf0);
+      touch_stage(st + 2 + kAhead);
+    }
+    if (st + 1 < nstages) compute_stage(buf1);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  // Epilogue: round to bf16 (nearest-even), stage the tile in LDS (16-byte
+  // chunk c of row r at chunk position c ^ (r & OSW)), then store 16-byte
+  // pieces of each row at its caller index.
+  constexpr int OPR = TN / 8;                        // 16-byte chunks per output row
+  constexpr int OSW = (OPR < 8 ? OPR : 8) - 1;
+  uint16_t* sO = reinterpret_cast<uint16_t*>(buf0);
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -205,29 +259,205 @@ __global__ __launch_bounds__(kThreads) void fwd_mfma(const int32_t* __restrict__
       for (int e = 0; e < 4; ++e) {
         const int r = wm * WM + i * 16 + (lane >> 4) * 4 + e;
         const int c = wn * WN + j * 16 + (lane & 15);
-        sO[r * LDO + c] = f32_to_bf16_rne(acc[i][j][e]);
+        sO[r * TN + (((c >> 3) ^ (r & OSW)) << 3) + (c & 7)] = f32_to_bf16_rne(acc[i][j][e]);
       }
   __syncthreads();
-  constexpr int OPR = TN / 8;
   for (int q = tid; q < TM * OPR; q += kThreads) {
     const int r = q / OPR, cc = q % OPR;
     const int32_t row = s_row[r];
     const int co = n0 + cc * 8;
     if (row >= 0 && co < c_out)
       *reinterpret_cast<uint4*>(y + int64_t(row) * c_out + co) =
-          *reinterpret_cast<const uint4*>(sO + r * LDO + cc * 8);
+          *reinterpret_cast<const uint4*>(sO + r * TN + ((cc ^ (r & OSW)) << 3));
   }
 }
 
-template <int TM, int TN, int WM, int WN, int KC>
-hipError_t launch_tiles(const ConvArgs& a, const uint16_t* wp, hipStream_t st) {
+// Row-owning variant. Wave w of the workgroup owns rows [16*FM*w, 16*FM*(w+1))
+// of the tile and all TN = 16*FN output channels, so every gathered feature row
+// is needed by exactly one wave: its MFMA A fragments are loaded straight from
+// global memory into registers, one stage ahead (no LDS round trip). The
+// weight slice of a stage, shared by the four waves, is copied into LDS with
+// global_load_lds (double-buffered, XOR-swizzled 128-byte rows). The gather
+// indices of a tap are fetched one tap ahead.
+template <int FM, int FN>
+__global__ __launch_bounds__(kThreads, 2) void fwd_rows(const int32_t* __restrict__ nbr,
+                                                        const int32_t* __restrict__ srows,
+                                                        const uint32_t* __restrict__ vmask, int64_t n,
+                                                        const uint16_t* __restrict__ x,
+                                                        const uint16_t* __restrict__ wp,
+                                                        const uint16_t* __restrict__ zeros,
+                                                        uint16_t* __restrict__ y, int c_in, int c_out,
+                                                        int n_tiles_n) {
+  constexpr int WM = 16 * FM, TM = 4 * WM, TN = 16 * FN;
+  constexpr int KC = 64, ROWB = KC * 2;
+  constexpr int BBUF = TN * ROWB;             // weight slice of one stage
+  constexpr int OSTAGE = 4 * 16 * TN * 2;     // 16 output rows per wave, four waves
+  __shared__ __attribute__((aligned(1024))) unsigned char bbuf0[BBUF > OSTAGE ? BBUF : OSTAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char bbuf1[BBUF];
+  __shared__ int32_t s_taps[27];
+  __shared__ uint32_t s_mask;
+
+  const int tile = xcd_remap(blockIdx.x, gridDim.x);
+  const int64_t t0 = int64_t(tile / n_tiles_n) * TM;
+  const int n0 = (tile % n_tiles_n) * TN;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lr = lane & 15, kg = lane >> 4;
+
+  // This lane's rows (one per row fragment) and the taps the tile needs.
+  int32_t crow[FM];
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+    const int64_t t = t0 + wave * WM + i * 16 + lr;
+    crow[i] = t < n ? srows[t] : -1;
+    if (t < n) m |= vmask[t];
+  }
+  for (int o = 32; o > 0; o >>= 1) m |= __shfl_xor(m, o, 64);
+  if (tid == 0) s_mask = 0;
+  __syncthreads();
+  if (lane == 0) atomicOr(&s_mask, m);
+  __syncthreads();
+  const uint32_t tmask = __builtin_amdgcn_readfirstlane(s_mask);
+  if (tid < 27 && ((tmask >> tid) & 1u)) s_taps[__popc(tmask & ((1u << tid) - 1u))] = tid;
+  __syncthreads();
+  const int ntaps = __popc(tmask);
+  const int nchunks = (c_in + KC - 1) / KC;
+  const int nstages = ntaps * nchunks;
+
+  int32_t srcL[FM], srcF[FM];  // gather rows of the tap being issued / being fetched
+  auto fetch_idx = [&](int ti, int32_t (&dst)[FM]) {
+    const int k = s_taps[ti];
+#pragma unroll
+    for (int i = 0; i < FM; ++i) dst[i] = crow[i] >= 0 ? nbr[int64_t(crow[i]) * 27 + k] : -1;
+  };
+  // Issue stage st: A fragments into registers, weight slice into LDS.
+  auto issue = [&](int st, uint4 (&a)[FM][2], unsigned char* bdst) {
+    const int ti = st / nchunks;
+    const int c0 = (st - ti * nchunks) * KC;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const int c = c0 + kk * 32 + kg * 8;
+        const uint16_t* g = (srcL[i] >= 0 && c < c_in) ? x + int64_t(srcL[i]) * c_in + c : zeros;
+        a[i][kk] = *reinterpret_cast<const uint4*>(g);
+      }
+    const uint16_t* wk = wp + int64_t(s_taps[ti]) * c_out * c_in;
+#pragma unroll
+    for (int i = wave; i < TN / 8; i += 4) {
+      const int col = i * 8 + (lane >> 3);
+      const int c = c0 + swz(col, lane & 7) * 8;
+      const void* g = (n0 + col < c_out && c < c_in)
+                          ? static_cast<const void*>(wk + int64_t(n0 + col) * c_in + c)
+                          : static_cast<const void*>(zeros);
+      copy16_to_lds(g, bdst + i * 1024);
+    }
+  };
+
+  f32x4 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](const uint4 (&a)[FM][2], const unsigned char* bsrc) {
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const int chunk = kk * 4 + kg;
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int r = j * 16 + lr;
+        const bf16x8 b = *reinterpret_cast<const bf16x8*>(bsrc + r * ROWB + swz(r, chunk) * 16);
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              *reinterpret_cast<const bf16x8*>(&a[i][kk]), b, acc[i][j], 0, 0, 0);
+      }
+    }
+  };
+
+  // One stage: wait for everything issued (stage st, issued a full stage
+  // earlier), barrier (every wave's weight copies have landed and the other
+  // buffer is free), issue stage st+1, fetch indices for the tap after, compute.
+  auto step = [&](int st, const uint4 (&aC)[FM][2], uint4 (&aN)[FM][2], const unsigned char* bC,
+                  unsigned char* bN) {
+    __builtin_amdgcn_s_waitcnt(0);
+    asm volatile("s_barrier" ::: "memory");
+    if (st + 1 < nstages) {
+      if ((st + 1) % nchunks == 0) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i) srcL[i] = srcF[i];
+      }
+      issue(st + 1, aN, bN);
+      if (st + 2 < nstages && (st + 2) % nchunks == 0) fetch_idx((st + 2) / nchunks, srcF);
+    }
+    compute(aC, bC);
+  };
+
+  uint4 a0[FM][2], a1[FM][2];
+  if (nstages > 0) {
+    fetch_idx(0, srcL);
+    issue(0, a0, bbuf0);
+    if (1 < nstages && 1 % nchunks == 0) fetch_idx(1, srcF);
+  }
+  for (int st = 0; st < nstages; st += 2) {
+    step(st, a0, a1, bbuf0, bbuf1);
+    if (st + 1 < nstages) step(st + 1, a1, a0, bbuf1, bbuf0);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  // Epilogue, one 16-row block per pass: round to bf16 (nearest-even), stage
+  // the block in this wave's LDS region (16-byte chunk c of row r at c ^ (r&OSW)),
+  // then store 16-byte pieces of each row at its caller index.
+  constexpr int OPR = TN / 8;
+  constexpr int OSW = (OPR < 8 ? OPR : 8) - 1;
+  uint16_t* sO = reinterpret_cast<uint16_t*>(bbuf0) + wave * 16 * TN;
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = kg * 4 + e, c = j * 16 + lr;
+        sO[r * TN + (((c >> 3) ^ (r & OSW)) << 3) + (c & 7)] = f32_to_bf16_rne(acc[i][j][e]);
+      }
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's staging writes are done
+#pragma unroll
+    for (int q = lane; q < 16 * OPR; q += 64) {
+      const int r = q / OPR, cc = q % OPR;
+      const int32_t row = __shfl(crow[i], r, 64);
+      const int co = n0 + cc * 8;
+      if (row >= 0 && co < c_out)
+        *reinterpret_cast<uint4*>(y + int64_t(row) * c_out + co) =
+            *reinterpret_cast<const uint4*>(sO + r * TN + ((cc ^ (r & OSW)) << 3));
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // reads done before the next block overwrites
+  }
+}
+
+template <int FM, int FN>
+hipError_t launch_rows(const ConvArgs& a, const uint16_t* wp, const uint16_t* zeros, hipStream_t st) {
+  constexpr int TM = 64 * FM, TN = 16 * FN;
   const int64_t mt = (a.n + TM - 1) / TM;
   const int nt = (a.c_out + TN - 1) / TN;
   const int64_t grid = mt * nt;
   if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
-  fwd_mfma<TM, TN, WM, WN, KC><<<unsigned(grid), kThreads, 0, st>>>(
-      a.nbr, a.srows, a.mask, a.n, static_cast<const uint16_t*>(a.x), wp, static_cast<uint16_t*>(a.y),
-      a.c_in, a.c_out, nt);
+  fwd_rows<FM, FN><<<unsigned(grid), kThreads, 0, st>>>(
+      a.nbr, a.srows, a.mask, a.n, static_cast<const uint16_t*>(a.x), wp, zeros,
+      static_cast<uint16_t*>(a.y), a.c_in, a.c_out, nt);
+  return hipGetLastError();
+}
+
+template <int TM, int TN, int WM, int WN>
+hipError_t launch_tiles(const ConvArgs& a, const uint16_t* wp, const uint16_t* zeros, hipStream_t st) {
+  const int64_t mt = (a.n + TM - 1) / TM;
+  const int nt = (a.c_out + TN - 1) / TN;
+  const int64_t grid = mt * nt;
+  if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
+  fwd_mfma<TM, TN, WM, WN><<<unsigned(grid), kThreads, 0, st>>>(
+      a.nbr, a.srows, a.mask, a.n, static_cast<const uint16_t*>(a.x), wp, zeros,
+      static_cast<uint16_t*>(a.y), a.c_in, a.c_out, nt);
   return hipGetLastError();
 }
 
@@ -237,15 +467,40 @@ hipError_t launch_pack_weights(const void* w, void* wp, int c_in, int c_out, hip
   dim3 grid(unsigned((c_out + 63) / 64), unsigned((c_in + 63) / 64), 27);
   pack_weights<<<grid, kThreads, 0, st>>>(static_cast<const uint16_t*>(w), static_cast<uint16_t*>(wp),
                                           c_in, c_out);
+  zero_block<<<1, 64, 0, st>>>(static_cast<uint16_t*>(wp) + packed_weight_elems(c_in, c_out));
   return hipGetLastError();
 }
 
 hipError_t launch_forward_mfma_bf16(const ConvArgs& a, const void* wp, hipStream_t st) {
   const uint16_t* p = static_cast<const uint16_t*>(wp);
-  if (a.c_out >= 128) return launch_tiles<128, 128, 64, 64, 64>(a, p, st);
-  if (a.c_out > 32) return launch_tiles<128, 64, 32, 64, 64>(a, p, st);
-  if (a.c_out > 16) return launch_tiles<256, 32, 64, 32, 64>(a, p, st);
-  return launch_tiles<256, 16, 64, 16, 64>(a, p, st);
+  const uint16_t* zeros = p + packed_weight_elems(a.c_in, a.c_out);
+  static const char* which = getenv("TRSC_GEMM_VARIANT");
+  const char v = which ? which[0] : 'a';
+  if (v == '3') {
+    if (a.c_out >= 128) return launch_tiles<128, 128, 64, 64>(a, p, zeros, st);
+    if (a.c_out > 32) return launch_tiles<64, 64, 32, 32>(a, p, zeros, st);
+    if (a.c_out > 16) return launch_tiles<128, 32, 32, 32>(a, p, zeros, st);
+    return launch_tiles<128, 16, 32, 16>(a, p, zeros, st);
+  }
+  if (v == 'b') {  // 64-row waves
+    if (a.c_out >= 128) return launch_rows<4, 8>(a, p, zeros, st);
+    if (a.c_out > 32) return launch_rows<4, 4>(a, p, zeros, st);
+    if (a.c_out > 16) return launch_rows<4, 2>(a, p, zeros, st);
+    return launch_rows<4, 1>(a, p, zeros, st);
+  }
+  if (v == 'c') {  // 64-row waves, 64-column tiles
+    if (a.c_out > 32) return launch_rows<4, 4>(a, p, zeros, st);
+    if (a.c_out > 16) return launch_rows<4, 2>(a, p, zeros, st);
+    return launch_rows<4, 1>(a, p, zeros, st);
+  }
+  // Wide layers: 64-row waves halve the LDS reads of weight fragments per
+  // multiply (the weight slice is read once per wave). Narrow layers: 32-row
+  // waves give twice the workgroups and a third wave per SIMD.
+  if (a.c_out >= 128 && a.c_in >= 256) return launch_rows<4, 8>(a, p, zeros, st);
+  if (a.c_out >= 128) return launch_rows<2, 8>(a, p, zeros, st);
+  if (a.c_out > 32) return launch_rows<2, 4>(a, p, zeros, st);
+  if (a.c_out > 16) return launch_rows<4, 2>(a, p, zeros, st);
+  return launch_rows<4, 1>(a, p, zeros, st);
 }
 
 }  // namespace trsc

@@ -47,7 +47,7 @@ __global__ __launch_bounds__(kThreads) void kmap_kernel(const uint64_t* __restri
                                                         uint32_t* __restrict__ mask_out) {
   __shared__ int32_t res[kThreads * 27];  // odd stride: conflict-free both ways
   __shared__ int32_t rows[kThreads];
-  const int64_t base = int64_t(blockIdx.x) * kThreads;
+  const int64_t base = int64_t(xcd_remap(blockIdx.x, gridDim.x)) * kThreads;
   const int64_t s = base + threadIdx.x;
   const int32_t special = hdr->special_row;
   if (s < n) {

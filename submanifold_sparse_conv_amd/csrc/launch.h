@@ -44,7 +44,11 @@ struct ConvArgs {
 };
 hipError_t launch_forward_simple_f32(const ConvArgs& a, hipStream_t st);
 hipError_t launch_forward_simple_bf16(const ConvArgs& a, hipStream_t st);
-// wp[k][co][ci] = w[k][ci][co] (bf16), the matrix-core operand layout.
+// wp[k][co][ci] = w[k][ci][co] (bf16), the matrix-core operand layout,
+// followed by 256 zero bytes (packed_weight_elems elements, then the zeros).
+inline int64_t packed_weight_elems(int c_in, int c_out) {
+  return (int64_t(27) * c_in * c_out + 127) / 128 * 128;  // keeps the zero block 256-byte aligned
+}
 hipError_t launch_pack_weights(const void* w, void* wp, int c_in, int c_out, hipStream_t st);
 hipError_t launch_forward_mfma_bf16(const ConvArgs& a, const void* wp, hipStream_t st);
 
