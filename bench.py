@@ -248,7 +248,7 @@ def main():
                          "gbs": (hash_bytes + map_bytes) / ((t_hash + t_map) * 1e-3) / 1e9,
                          "frac": (hash_bytes + map_bytes) / ((t_hash + t_map) * 1e-3) / 1e9 / PEAK_HBM_GBS,
                          "map_only_gbs": map_bytes / (t_map * 1e-3) / 1e9},
-        "roofline": {"kernel": "fwd_mfma (gather-GEMM)", "bound": "mfma", "achieved": gemm_tflops,
+        "roofline": {"kernel": "fwd_rows (gather-GEMM)", "bound": "mfma", "achieved": gemm_tflops,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": gemm_tflops / PEAK_BF16_TFLOPS,
                      "traffic": traffic},
     }

@@ -114,6 +114,30 @@ __device__ inline int xcd_remap(int bid, int grid) {
   return xcd * per + (xcd < rem ? xcd : rem) + local;
 }
 
+// Direct global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4):
+// lane l of the wave writes lds_base + 16 * l. `lds_base` must be wave-uniform.
+__device__ inline void copy16_to_lds(const void* g, void* lds_base) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(g),
+                                   (__attribute__((address_space(3))) void*)(lds_base), 16, 0, 0);
+}
+
+// Staged operand rows are 64 bf16 = 128 bytes = eight 16-byte chunks; chunk c
+// of row r sits at chunk position c ^ (r & 7), so eight consecutive rows read
+// at one logical chunk hit eight different bank groups.
+__device__ inline int swz(int row, int chunk) { return chunk ^ (row & 7); }
+
+// Workgroup barrier without the release fence of __syncthreads(): that fence
+// waits for every outstanding global_load_lds (they count as LDS stores), even
+// ones whose data is not needed yet. Callers wait for the copies they need with
+// s_waitcnt before it. The memory clobber keeps the compiler from moving LDS
+// accesses across it.
+__device__ inline void bare_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+__device__ inline void stage_barrier() {  // all but this wave's newest copy have landed
+  __builtin_amdgcn_s_waitcnt(0x0F71);
+  bare_barrier();
+}
+
 // ---------------------------------------------------------------------------
 // bf16 helpers (bit patterns in uint16_t).
 // ---------------------------------------------------------------------------

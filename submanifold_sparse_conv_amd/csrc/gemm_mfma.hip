@@ -12,18 +12,17 @@
 // the same bit for bit on every run.
 //
 // K loop: the taps some row of the tile needs (OR of the rows' 27-bit
-// neighbour masks), each split into KC-wide channel chunks ("stages"). The
-// gather indices of every active tap are read once into LDS. Per stage the TM
-// gathered feature rows (zero where the neighbour is absent) and the KC x TN
-// weight slice are staged in LDS and four waves run v_mfma_f32_16x16x32_bf16
-// over their WM x WN sub-tiles, while the next stage's global loads are
-// already in flight into registers.
+// neighbour masks), each split into 64-channel chunks ("stages"). Each of the
+// four waves owns 16*FM whole rows of the tile and all TN columns, so every
+// gathered feature row is read by one wave only: its MFMA A fragments go from
+// global memory straight into registers, one stage ahead. The stage's weight
+// slice, which all four waves read, is copied into LDS with global_load_lds
+// (double-buffered, XOR-swizzled 128-byte rows). Matrix instruction:
+// v_mfma_f32_16x16x32_bf16.
 //
 // Weights are first re-laid out to [27][C_out][C_in] (input channels
 // contiguous), the operand order of the matrix instruction, followed by a
-// 256-byte block of zeros.
-#include <cstdlib>
-
+// 256-byte block of zeros (the copy source of absent neighbours).
 #include "common.h"
 #include "launch.h"
 
@@ -62,223 +61,9 @@ __global__ void zero_block(uint16_t* z) {
   reinterpret_cast<uint4*>(z)[threadIdx.x & 15] = make_uint4(0u, 0u, 0u, 0u);
 }
 
-// Direct global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4):
-// lane l of the wave writes lds_base + 16 * l. `lds_base` must be wave-uniform.
-__device__ inline void copy16_to_lds(const void* g, void* lds_base) {
-  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(g),
-                                   (__attribute__((address_space(3))) void*)(lds_base), 16, 0, 0);
-}
-
-// Staged operand rows are 64 bf16 = 128 bytes = eight 16-byte chunks; chunk c
-// of row r sits at chunk position c ^ (r & 7), so eight consecutive rows read
-// at one logical chunk hit eight different bank groups.
-__device__ inline int swz(int row, int chunk) { return chunk ^ (row & 7); }
-
-__device__ inline void stage_barrier() {
-  __builtin_amdgcn_s_waitcnt(0x0F71);
-  asm volatile("s_barrier" ::: "memory");
-}
-
-template <int TM, int TN, int WM, int WN>
-__global__ __launch_bounds__(kThreads, 2) void fwd_mfma(const int32_t* __restrict__ nbr,
-                                                     const int32_t* __restrict__ srows,
-                                                     const uint32_t* __restrict__ vmask, int64_t n,
-                                                     const uint16_t* __restrict__ x,
-                                                     const uint16_t* __restrict__ wp,
-                                                     const uint16_t* __restrict__ zeros,
-                                                     uint16_t* __restrict__ y, int c_in, int c_out,
-                                                     int n_tiles_n) {
-  constexpr int KC = 64;                  // input channels per stage
-  constexpr int ROWB = KC * 2;            // bytes per staged row
-  constexpr int WAVES_N = TN / WN;
-  static_assert((TM / WM) * (TN / WN) == kThreads / 64, "four waves");
-  static_assert(TM % 8 == 0 && TN % 8 == 0, "8 rows per wave copy");
-  constexpr int FM = WM / 16, FN = WN / 16;
-  constexpr int BUF = (TM + TN) * ROWB;   // bytes of one stage buffer
-  constexpr int OUTB = TM * TN * 2;       // output tile staged as bf16
-  // Two stage buffers as two distinct arrays: the compiler can then tell that
-  // the copies in flight into one do not alias the fragment reads of the other
-  // and does not wait for them. buf0 also stages the output tile.
-  __shared__ __attribute__((aligned(1024))) unsigned char buf0[BUF > OUTB ? BUF : OUTB];
-  __shared__ __attribute__((aligned(1024))) unsigned char buf1[BUF];
-  __shared__ __attribute__((aligned(1024))) unsigned char junk[1024];  // sink of the L2 touches
-  __shared__ int32_t s_row[TM];
-  __shared__ int32_t s_src[27 * TM];      // gather source row per (active tap, tile row)
-  __shared__ int32_t s_taps[27];
-  __shared__ uint32_t s_mask;
-
-  const int tile = xcd_remap(blockIdx.x, gridDim.x);
-  const int64_t t0 = int64_t(tile / n_tiles_n) * TM;
-  const int n0 = (tile % n_tiles_n) * TN;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
-
-  // Prologue: tile rows, the taps some row needs, and all gather indices.
-  if (tid == 0) s_mask = 0;
-  uint32_t m = 0;
-  for (int r = tid; r < TM; r += kThreads) {
-    const int64_t t = t0 + r;
-    s_row[r] = t < n ? srows[t] : -1;
-    if (t < n) m |= vmask[t];
-  }
-  for (int o = 32; o > 0; o >>= 1) m |= __shfl_xor(m, o, 64);
-  __syncthreads();
-  if (lane == 0) atomicOr(&s_mask, m);
-  __syncthreads();
-  const uint32_t tmask = s_mask;
-  const int ntaps = __popc(tmask);
-  if (tid < 27 && ((tmask >> tid) & 1u)) s_taps[__popc(tmask & ((1u << tid) - 1u))] = tid;
-  __syncthreads();
-  for (int q = tid; q < TM * ntaps; q += kThreads) {
-    const int r = q / ntaps, ti = q - r * ntaps;  // consecutive lanes read one row's taps
-    const int32_t row = s_row[r];
-    s_src[ti * TM + r] = row >= 0 ? nbr[int64_t(row) * 27 + s_taps[ti]] : -1;
-  }
-  __syncthreads();
-
-  const int nchunks = (c_in + KC - 1) / KC;
-  const int nstages = ntaps * nchunks;
-
-  // Issues the copies of stage st into `base`: each wave copy moves 8 staged
-  // rows (64 lanes x 16 bytes); lane l fills row 8i + l/8, chunk position
-  // l%8, i.e. logical chunk (l%8) ^ (row & 7).
-  auto issue_stage = [&](int st, unsigned char* base) {
-    const int ti = st / nchunks;
-    const int c0 = (st - ti * nchunks) * KC;
-    const int rl = lane >> 3;
-#pragma unroll
-    for (int i = wave; i < TM / 8; i += 4) {
-      const int row = i * 8 + rl;
-      const int c = c0 + swz(row, lane & 7) * 8;
-      const int32_t src = s_src[ti * TM + row];
-      const void* g = (src >= 0 && c < c_in) ? static_cast<const void*>(x + int64_t(src) * c_in + c)
-                                             : static_cast<const void*>(zeros);
-      copy16_to_lds(g, base + i * 1024);
-    }
-    const uint16_t* wk = wp + int64_t(s_taps[ti]) * c_out * c_in;
-#pragma unroll
-    for (int i = wave; i < TN / 8; i += 4) {
-      const int col = i * 8 + rl;
-      const int c = c0 + swz(col, lane & 7) * 8;
-      const void* g = (n0 + col < c_out && c < c_in)
-                          ? static_cast<const void*>(wk + int64_t(n0 + col) * c_in + c)
-                          : static_cast<const void*>(zeros);
-      copy16_to_lds(g, base + TM * ROWB + i * 1024);
-    }
-  };
-
-  // One 16-byte read per gathered row of stage st (each staged row is one
-  // 128-byte line), issued kAhead stages early so that the real copies find
-  // their lines in L2: every stage otherwise waits for its slowest lane, and
-  // some lane almost always misses. Each wave issues exactly one such read per
-  // stage (rows wave*TM/4 .. +TM/4), so "all but the last one" is vmcnt(1).
-  constexpr int kAhead = 4;
-  constexpr int RPW = TM / 4;
-  auto touch_stage = [&](int st) {
-    const int sst = st < nstages ? st : nstages - 1;
-    const int ti = sst / nchunks;
-    const int c = (sst - ti * nchunks) * KC;
-    const int row = wave * RPW + lane % RPW;
-    const int32_t src = s_src[ti * TM + row];
-    const void* g = (src >= 0 && c < c_in) ? static_cast<const void*>(x + int64_t(src) * c_in + c)
-                                           : static_cast<const void*>(zeros);
-    copy16_to_lds(g, junk);
-  };
-
-  f32x4 acc[FM][FN];
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  auto compute_stage = [&](const unsigned char* bA) {
-    const unsigned char* bB = bA + TM * ROWB;
-#pragma unroll
-    for (int kk = 0; kk < KC / 32; ++kk) {
-      const int chunk = kk * 4 + (lane >> 4);
-      bf16x8 af[FM], bfr[FN];
-#pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        const int r = wm * WM + i * 16 + (lane & 15);
-        af[i] = *reinterpret_cast<const bf16x8*>(bA + r * ROWB + swz(r, chunk) * 16);
-      }
-#pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const int r = wn * WN + j * 16 + (lane & 15);
-        bfr[j] = *reinterpret_cast<const bf16x8*>(bB + r * ROWB + swz(r, chunk) * 16);
-      }
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-    }
-  };
-
-  // Two stages per trip: copies of the next stage fly while this one computes.
-  // Stage barrier: wait until all of this wave's copies except the newest
-  // touch have landed in LDS (s_waitcnt 0x0F71 = vmcnt(1)), then a plain
-  // s_barrier. __syncthreads() would add a release fence, and with copies in
-  // flight the fence waits for all of them (vmcnt(0)), touches included. The
-  // asm memory clobber keeps the compiler from moving LDS reads across it; the
-  // fragment reads of the previous stage are consumed by its matrix
-  // instructions before any wave reaches the barrier.
-  if (nstages > 0) {
-    for (int p = 1; p < kAhead; ++p) touch_stage(p);
-    issue_stage(0, buf0);
-    touch_stage(kAhead);
-  }
-  for (int st = 0; st < nstages; st += 2) {
-    stage_barrier();  // stage st is in buf0 for every wave; buf1 is free again
-    if (st + 1 < nstages) {
-      issue_stage(st + 1, buf1);
-      touch_stage(st + 1 + kAhead);
-    }
-    compute_stage(buf0);
-    stage_barrier();
-    if (st + 2 < nstages) {
-      issue_stage(st + 2, buf0);
-      touch_stage(st + 2 + kAhead);
-    }
-    if (st + 1 < nstages) compute_stage(buf1);
-  }
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-
-  // Epilogue: round to bf16 (nearest-even), stage the tile in LDS (16-byte
-  // chunk c of row r at chunk position c ^ (r & OSW)), then store 16-byte
-  // pieces of each row at its caller index.
-  constexpr int OPR = TN / 8;                        // 16-byte chunks per output row
-  constexpr int OSW = (OPR < 8 ? OPR : 8) - 1;
-  uint16_t* sO = reinterpret_cast<uint16_t*>(buf0);
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = wm * WM + i * 16 + (lane >> 4) * 4 + e;
-        const int c = wn * WN + j * 16 + (lane & 15);
-        sO[r * TN + (((c >> 3) ^ (r & OSW)) << 3) + (c & 7)] = f32_to_bf16_rne(acc[i][j][e]);
-      }
-  __syncthreads();
-  for (int q = tid; q < TM * OPR; q += kThreads) {
-    const int r = q / OPR, cc = q % OPR;
-    const int32_t row = s_row[r];
-    const int co = n0 + cc * 8;
-    if (row >= 0 && co < c_out)
-      *reinterpret_cast<uint4*>(y + int64_t(row) * c_out + co) =
-          *reinterpret_cast<const uint4*>(sO + r * TN + ((cc ^ (r & OSW)) << 3));
-  }
-}
-
-// Row-owning variant. Wave w of the workgroup owns rows [16*FM*w, 16*FM*(w+1))
-// of the tile and all TN = 16*FN output channels, so every gathered feature row
-// is needed by exactly one wave: its MFMA A fragments are loaded straight from
-// global memory into registers, one stage ahead (no LDS round trip). The
-// weight slice of a stage, shared by the four waves, is copied into LDS with
-// global_load_lds (double-buffered, XOR-swizzled 128-byte rows). The gather
-// indices of a tap are fetched one tap ahead.
+// Wave w of the workgroup owns rows [16*FM*w, 16*FM*(w+1)) of the tile and all
+// TN = 16*FN output channels. The gather indices of a tap are fetched one tap
+// ahead, the A fragments and the weight slice one stage ahead.
 template <int FM, int FN>
 __global__ __launch_bounds__(kThreads, 2) void fwd_rows(const int32_t* __restrict__ nbr,
                                                         const int32_t* __restrict__ srows,
@@ -449,18 +234,6 @@ hipError_t launch_rows(const ConvArgs& a, const uint16_t* wp, const uint16_t* ze
   return hipGetLastError();
 }
 
-template <int TM, int TN, int WM, int WN>
-hipError_t launch_tiles(const ConvArgs& a, const uint16_t* wp, const uint16_t* zeros, hipStream_t st) {
-  const int64_t mt = (a.n + TM - 1) / TM;
-  const int nt = (a.c_out + TN - 1) / TN;
-  const int64_t grid = mt * nt;
-  if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
-  fwd_mfma<TM, TN, WM, WN><<<unsigned(grid), kThreads, 0, st>>>(
-      a.nbr, a.srows, a.mask, a.n, static_cast<const uint16_t*>(a.x), wp, zeros,
-      static_cast<uint16_t*>(a.y), a.c_in, a.c_out, nt);
-  return hipGetLastError();
-}
-
 }  // namespace
 
 hipError_t launch_pack_weights(const void* w, void* wp, int c_in, int c_out, hipStream_t st) {
@@ -474,25 +247,6 @@ hipError_t launch_pack_weights(const void* w, void* wp, int c_in, int c_out, hip
 hipError_t launch_forward_mfma_bf16(const ConvArgs& a, const void* wp, hipStream_t st) {
   const uint16_t* p = static_cast<const uint16_t*>(wp);
   const uint16_t* zeros = p + packed_weight_elems(a.c_in, a.c_out);
-  static const char* which = getenv("TRSC_GEMM_VARIANT");
-  const char v = which ? which[0] : 'a';
-  if (v == '3') {
-    if (a.c_out >= 128) return launch_tiles<128, 128, 64, 64>(a, p, zeros, st);
-    if (a.c_out > 32) return launch_tiles<64, 64, 32, 32>(a, p, zeros, st);
-    if (a.c_out > 16) return launch_tiles<128, 32, 32, 32>(a, p, zeros, st);
-    return launch_tiles<128, 16, 32, 16>(a, p, zeros, st);
-  }
-  if (v == 'b') {  // 64-row waves
-    if (a.c_out >= 128) return launch_rows<4, 8>(a, p, zeros, st);
-    if (a.c_out > 32) return launch_rows<4, 4>(a, p, zeros, st);
-    if (a.c_out > 16) return launch_rows<4, 2>(a, p, zeros, st);
-    return launch_rows<4, 1>(a, p, zeros, st);
-  }
-  if (v == 'c') {  // 64-row waves, 64-column tiles
-    if (a.c_out > 32) return launch_rows<4, 4>(a, p, zeros, st);
-    if (a.c_out > 16) return launch_rows<4, 2>(a, p, zeros, st);
-    return launch_rows<4, 1>(a, p, zeros, st);
-  }
   // Wide layers: 64-row waves halve the LDS reads of weight fragments per
   // multiply (the weight slice is read once per wave). Narrow layers: 32-row
   // waves give twice the workgroups and a third wave per SIMD.
