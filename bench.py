@@ -217,11 +217,16 @@ def main():
     gemm_tflops = flops / (t_gemm * 1e-3) / 1e12
     t_gemm_ss = measure_forward_only(sc, torch, path, args.gemm_reps)
 
-    P = int(16)
-    while P < 2 * wl.n:
-        P *= 2
-    hash_bytes = 16 * wl.n + 12 * wl.n + 16 * P
-    map_bytes = 12 * wl.n + 16 * P + 108 * wl.n + 4 * wl.n
+    # Algorithmic bytes of the topology passes. Hash: coordinates read, sorted
+    # key + row written, one 32-byte slot per occupied 4x4x4 block written.
+    # Map: sorted key + row read, the row order read once more for neighbour
+    # rows, the block table read once, nbr (108 B), mask and the tile order
+    # (row + mask) written.
+    c = wl.coords.astype(np.int64)
+    nblocks = int(np.unique(((c[:, 0] * 16384 + (c[:, 1] >> 2)) * 16384 + (c[:, 2] >> 2)) * 16384
+                            + (c[:, 3] >> 2)).size)
+    hash_bytes = 16 * wl.n + 12 * wl.n + 32 * nblocks
+    map_bytes = 12 * wl.n + 4 * wl.n + 32 * nblocks + 108 * wl.n + 4 * wl.n + 8 * wl.n
     traffic = traffic_entry()
 
     out = {
@@ -244,7 +249,7 @@ def main():
         "forward": {"voxels_per_s_steady": wl.n / (t_gemm_ss * 1e-3), "ms_steady": t_gemm_ss,
                     "effective_tflops": flops / (t_gemm_ss * 1e-3) / 1e12,
                     "frac_bf16_peak": flops / (t_gemm_ss * 1e-3) / 1e12 / PEAK_BF16_TFLOPS},
-        "hash_map_hbm": {"algorithmic_bytes": hash_bytes + map_bytes,
+        "hash_map_hbm": {"algorithmic_bytes": hash_bytes + map_bytes, "blocks_4x4x4": nblocks,
                          "gbs": (hash_bytes + map_bytes) / ((t_hash + t_map) * 1e-3) / 1e9,
                          "frac": (hash_bytes + map_bytes) / ((t_hash + t_map) * 1e-3) / 1e9 / PEAK_HBM_GBS,
                          "map_only_gbs": map_bytes / (t_map * 1e-3) / 1e9},

@@ -36,20 +36,14 @@ int hip_fail(hipError_t e, const char* where) {
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-uint32_t table_capacity(int64_t n) {  // power of two >= 4n (at most 2^31 >= 2n), at least 16
+uint32_t table_capacity(int64_t n) {  // largest table: power of two >= 2n (one block per voxel), >= 16
   uint64_t p = 16;
-  while (p < uint64_t(4 * n) && p < (uint64_t(1) << 31)) p <<= 1;
+  while (p < uint64_t(2 * n) && p < (uint64_t(1) << 31)) p <<= 1;
   return uint32_t(p);
 }
 
-int log2_u64(uint64_t v) {
-  int r = 0;
-  while ((uint64_t(1) << (r + 1)) <= v) ++r;
-  return r;
-}
-
 // Hash workspace: header | keys[2][n] | rows[2][n] | radix counts | digit
-// totals | OR/AND partials | slots[P].
+// totals | per-workgroup partials | block slots[capacity].
 struct HashLayout {
   size_t hdr, keys0, keys1, rows0, rows1, counts, totals, parts, slots, total;
   uint32_t cap;
@@ -77,7 +71,7 @@ HashLayout hash_layout(int64_t n) {
   o += align_up(size_t(pack_partials(n)) * 16, 256);
   l.cap = table_capacity(n);
   l.slots = o;
-  o += size_t(l.cap) * sizeof(Slot);
+  o += size_t(l.cap) * sizeof(BlockSlot);
   l.total = o;
   return l;
 }
@@ -88,17 +82,16 @@ struct tr_sc_hash {
   uint32_t magic;
   int64_t n;
   HashHeader* hdr;
-  TableRef table;
+  TableRef table;         // block slots, header (capacity, shift), sorted rows
   const uint64_t* skeys;  // sorted keys
-  const int32_t* srows;   // sorted position -> caller row
 };
 
 struct tr_sc_kmap {
   uint32_t magic;
   int64_t n;
   const int32_t* nbr;
-  const int32_t* srows;
-  const uint32_t* mask;
+  const int32_t* grows;   // tile row order (position -> caller row)
+  const uint32_t* gmask;  // neighbour mask of each position
 };
 
 extern "C" {
@@ -134,7 +127,7 @@ int tr_sparseconv_build_hash(const int32_t* coords, int64_t n, void* workspace, 
   uint32_t* counts = reinterpret_cast<uint32_t*>(ws + l.counts);
   uint32_t* totals = reinterpret_cast<uint32_t*>(ws + l.totals);
   unsigned long long* parts = reinterpret_cast<unsigned long long*>(ws + l.parts);
-  Slot* slots = reinterpret_cast<Slot*>(ws + l.slots);
+  BlockSlot* slots = reinterpret_cast<BlockSlot*>(ws + l.slots);
 
   hipError_t e = launch_pack(coords, n, keys[0], rows[0], parts, hdr, st);
   if (e != hipSuccess) return hip_fail(e, "build_hash: pack");
@@ -163,17 +156,15 @@ int tr_sparseconv_build_hash(const int32_t* coords, int64_t n, void* workspace, 
       cur ^= 1;
     }
   }
-  const uint32_t shift = uint32_t(64 - log2_u64(uint64_t(l.cap)));
-  e = launch_insert(keys[cur], rows[cur], n, slots, l.cap - 1, shift, hdr, st);
-  if (e != hipSuccess) return hip_fail(e, "build_hash: insert");
+  e = launch_blocks(keys[cur], n, slots, l.cap, reinterpret_cast<uint32_t*>(parts), hdr, st);
+  if (e != hipSuccess) return hip_fail(e, "build_hash: block table");
 
   tr_sc_hash* h = new tr_sc_hash;
   h->magic = kHashMagic;
   h->n = n;
   h->hdr = hdr;
-  h->table = TableRef{slots, l.cap - 1, shift};
+  h->table = TableRef{slots, hdr, rows[cur]};
   h->skeys = keys[cur];
-  h->srows = rows[cur];
   *out = h;
   return TR_SC_OK;
 }
@@ -203,7 +194,7 @@ int tr_sparseconv_hash_lookup(const tr_sc_hash* h, const int32_t* q, int64_t nq,
   if (nq > 0 && (q == nullptr || idx == nullptr)) return fail(TR_SC_ERR_INVALID_ARG, "hash_lookup: NULL buffer");
   if (reinterpret_cast<uintptr_t>(q) % 16 != 0)
     return fail(TR_SC_ERR_INVALID_ARG, "hash_lookup: queries not 16-byte aligned");
-  hipError_t e = launch_lookup(h->table, h->hdr, q, nq, idx, static_cast<hipStream_t>(stream));
+  hipError_t e = launch_lookup(h->table, q, nq, idx, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "hash_lookup");
   return TR_SC_OK;
 }
@@ -212,7 +203,7 @@ int tr_sparseconv_hash_sorted_rows(const tr_sc_hash* h, int32_t* perm, void* str
   if (h == nullptr || h->magic != kHashMagic) return fail(TR_SC_ERR_INVALID_ARG, "hash_sorted_rows: bad hash handle");
   if (h->n == 0) return TR_SC_OK;
   if (perm == nullptr) return fail(TR_SC_ERR_INVALID_ARG, "hash_sorted_rows: perm is NULL");
-  hipError_t e = hipMemcpyAsync(perm, h->srows, size_t(h->n) * 4, hipMemcpyDeviceToDevice,
+  hipError_t e = hipMemcpyAsync(perm, h->table.srows, size_t(h->n) * 4, hipMemcpyDeviceToDevice,
                                 static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "hash_sorted_rows");
   return TR_SC_OK;
@@ -225,9 +216,10 @@ void tr_sparseconv_hash_destroy(tr_sc_hash* h) {
   }
 }
 
+// Kernel-map workspace: mask[n] (Morton order) | grows[n] | gmask[n] (tile order).
 size_t tr_sparseconv_kmap_workspace_bytes(int64_t n) {
   if (n < 0 || n > kMaxN) return 0;
-  return align_up(size_t(n) * 4, 256) + 256;
+  return 3 * align_up(size_t(n) * 4, 256) + 256;
 }
 
 int tr_sparseconv_build_kernel_map(const tr_sc_hash* h, int32_t* nbr, void* workspace, size_t ws_bytes,
@@ -242,16 +234,19 @@ int tr_sparseconv_build_kernel_map(const tr_sc_hash* h, int32_t* nbr, void* work
     return fail(TR_SC_ERR_WORKSPACE, "build_kernel_map: workspace %zu bytes < %zu needed", ws_bytes, need);
   if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
     return fail(TR_SC_ERR_INVALID_ARG, "build_kernel_map: workspace not 256-byte aligned");
+  const size_t part = align_up(size_t(h->n) * 4, 256);
   uint32_t* mask = static_cast<uint32_t*>(workspace);
-  hipError_t e = launch_kmap(h->skeys, h->srows, h->n, h->table, h->hdr, nbr, mask,
+  int32_t* grows = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + part);
+  uint32_t* gmask = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + 2 * part);
+  hipError_t e = launch_kmap(h->skeys, h->n, h->table, nbr, mask, grows, gmask,
                              static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "build_kernel_map");
   tr_sc_kmap* m = new tr_sc_kmap;
   m->magic = kKmapMagic;
   m->n = h->n;
   m->nbr = nbr;
-  m->srows = h->srows;
-  m->mask = mask;
+  m->grows = grows;
+  m->gmask = gmask;
   *out = m;
   return TR_SC_OK;
 }
@@ -295,7 +290,7 @@ int run_forward(const char* who, const tr_sc_kmap* m, const void* x, const void*
   if (x == nullptr || wp == nullptr || y == nullptr) return fail(TR_SC_ERR_INVALID_ARG, "%s: NULL tensor", who);
   if (int64_t(m->n) * c_out >= (int64_t(1) << 40) || int64_t(m->n) * c_in >= (int64_t(1) << 40))
     return fail(TR_SC_ERR_UNSUPPORTED, "%s: tensor too large", who);
-  ConvArgs a{m->nbr, m->srows, m->mask, m->n, x, wp, y, c_in, c_out};
+  ConvArgs a{m->nbr, m->grows, m->gmask, m->n, x, wp, y, c_in, c_out};
   hipError_t e;
   if (dtype == TR_SC_F32) {
     e = launch_forward_simple_f32(a, st);

@@ -17,7 +17,7 @@ constexpr uint64_t kMortonMask = 0xFFFFFFFFFFFFull;  // low 48 bits
 constexpr uint64_t kMaskZ = 0x249249249249ull;       // bits 0, 3, ..., 45
 constexpr uint64_t kMaskY = kMaskZ << 1;
 constexpr uint64_t kMaskX = kMaskZ << 2;
-constexpr uint64_t kEmptyKey = ~0ull;  // also the key of (65535,65535,65535,65535)
+constexpr uint64_t kEmptyKey = ~0ull;  // empty table slot: no block key has all 64 bits set
 
 __host__ __device__ inline uint64_t dilate3(uint32_t v) {  // bit i -> bit 3i (16 bits)
   uint64_t x = v & 0xFFFFu;
@@ -42,20 +42,30 @@ __host__ __device__ inline uint64_t make_key(uint32_t b, uint32_t x, uint32_t y,
 }
 
 // ---------------------------------------------------------------------------
-// Open-addressing table. 16-byte slots {key, row}; EMPTY key = ~0. The one
-// valid key equal to ~0 (every component 65535) lives outside the table in
-// HashHeader::special_row. Capacity is a power of two >= 4N (load <= 1/4).
+// Open-addressing table of occupied 4x4x4 blocks. The key of a block is
+// key >> 6 (the voxel key without its lowest Morton triple pair), so the 64
+// cells of a block are the keys with the same high bits and their cell index
+// is key & 63. A slot holds the block key, a 64-bit occupancy bitmap (bit c set
+// when cell c is active) and `start`, the Morton-sorted position of the
+// block's first active voxel. The sorted position of an active voxel is then
+// start + popcount(bitmap & ((1 << c) - 1)), and its caller row is
+// sorted_rows[that position]. Block keys have at most 58 bits, so ~0 marks an
+// empty slot.
 //
-// Home slot: Fibonacci (multiplicative) hashing of the whole key, top bits of
-// key * 2^64/phi. Collisions are resolved by linear probing. Hashing whole keys
-// keeps probe runs short; grouping the 8 voxels of a 2x2x2 brick into one run
-// of slots gives better cache-line locality but makes clusters that lengthen
-// the probe chains several-fold, and the lookups are latency-bound.
+// Capacity: a power of two >= 2 * (number of blocks), chosen on the device
+// after the sort and kept in the header with the hash shift. Home slot:
+// Fibonacci hashing of the block key; collisions probe linearly.
+//
+// A surface of thickness ~2 fills ~20 of a block's 64 cells, so the table is
+// ~20x smaller than one slot per voxel and stays in L2; the 26 neighbours of
+// a voxel fall into at most 8 blocks (3.4 on average).
 // ---------------------------------------------------------------------------
-struct alignas(16) Slot {
-  uint64_t key;
-  int32_t row;
-  int32_t pad;
+struct alignas(32) BlockSlot {
+  uint64_t bkey;
+  uint64_t bits;
+  uint32_t start;
+  uint32_t pad0;
+  uint64_t pad1;
 };
 
 constexpr uint32_t kFlagCoordRange = 1u;
@@ -64,45 +74,64 @@ constexpr uint32_t kFlagCapacity = 4u;
 
 struct alignas(256) HashHeader {
   uint32_t flags;
-  int32_t special_row;
-  uint32_t pad0, pad1;
-  unsigned long long or_bits;   // OR of all keys
-  unsigned long long and_bits;  // AND of all keys
+  uint32_t nblocks;             // occupied 4x4x4 blocks
+  uint32_t cap_mask;            // table capacity - 1
+  uint32_t shift;               // 64 - log2(capacity)
+  unsigned long long or_bits;   // OR of all voxel keys
+  unsigned long long and_bits;  // AND of all voxel keys
 };
 
 struct TableRef {
-  const Slot* slots;
-  uint32_t mask;   // capacity - 1 (capacity a power of two >= 16)
-  uint32_t shift;  // 64 - log2(capacity)
+  const BlockSlot* slots;
+  const HashHeader* hdr;  // capacity and shift live on the device
+  const int32_t* srows;   // sorted position -> caller row
 };
 
-__host__ __device__ inline uint32_t home_slot(uint64_t key, uint32_t shift) {
-  return uint32_t((key * 0x9E3779B97F4A7C15ull) >> shift);
+__host__ __device__ inline uint32_t home_slot(uint64_t bkey, uint32_t shift) {
+  return uint32_t((bkey * 0x9E3779B97F4A7C15ull) >> shift);
 }
 
-__device__ inline uint4 load_slot(const Slot* slots, uint32_t s) {
-  return *reinterpret_cast<const uint4*>(slots + s);
-}
-
-__device__ inline uint64_t slot_key(const uint4& v) { return uint64_t(v.x) | (uint64_t(v.y) << 32); }
-
-// Continues a probe run whose first slot s (already loaded into v) did not
-// decide the lookup by itself.
-__device__ inline int32_t probe_from(const TableRef& t, uint64_t key, uint32_t s, uint4 v) {
-  for (uint32_t probe = 0; probe <= t.mask; ++probe) {
-    const uint64_t k = slot_key(v);
-    if (k == key) return int32_t(v.z);
-    if (k == kEmptyKey) return -1;
-    s = (s + 1) & t.mask;
-    v = load_slot(t.slots, s);
+// Occupancy bitmap and start of block `bkey` (bits = 0 when it is absent),
+// continuing a probe run whose first slot s is already loaded in (v0, v1).
+__device__ inline void block_probe_from(const BlockSlot* slots, uint32_t mask, uint64_t bkey, uint32_t s,
+                                        uint4 v0, uint4 v1, uint64_t& bits, uint32_t& start) {
+  bits = 0;
+  start = 0;
+  for (uint32_t probe = 0; probe <= mask; ++probe) {
+    const uint64_t k = uint64_t(v0.x) | (uint64_t(v0.y) << 32);
+    if (k == bkey) {
+      bits = uint64_t(v0.z) | (uint64_t(v0.w) << 32);
+      start = v1.x;
+      return;
+    }
+    if (k == kEmptyKey) return;
+    s = (s + 1) & mask;
+    v0 = reinterpret_cast<const uint4*>(slots + s)[0];
+    v1 = reinterpret_cast<const uint4*>(slots + s)[1];
   }
-  return -1;
 }
 
-__device__ inline int32_t table_find(const TableRef& t, uint64_t key, int32_t special_row) {
-  if (key == kEmptyKey) return special_row;
-  const uint32_t s = home_slot(key, t.shift);
-  return probe_from(t, key, s, load_slot(t.slots, s));
+__device__ inline void block_find(const BlockSlot* slots, uint32_t mask, uint32_t shift, uint64_t bkey,
+                                  uint64_t& bits, uint32_t& start) {
+  const uint32_t s = home_slot(bkey, shift) & mask;
+  block_probe_from(slots, mask, bkey, s, reinterpret_cast<const uint4*>(slots + s)[0],
+                   reinterpret_cast<const uint4*>(slots + s)[1], bits, start);
+}
+
+// Cell index (0..63) of the in-block coordinates (x, y, z in 0..3): the low
+// six bits of the Morton key.
+__host__ __device__ inline uint32_t cell_of(uint32_t x, uint32_t y, uint32_t z) {
+  return (z & 1u) | ((y & 1u) << 1) | ((x & 1u) << 2) | ((z >> 1) << 3) | ((y >> 1) << 4) | ((x >> 1) << 5);
+}
+
+// Caller row of the voxel with key `key`, or -1.
+__device__ inline int32_t voxel_find(const TableRef& t, uint32_t mask, uint32_t shift, uint64_t key) {
+  uint64_t bits;
+  uint32_t start;
+  block_find(t.slots, mask, shift, key >> 6, bits, start);
+  const uint32_t c = uint32_t(key & 63u);
+  if (!((bits >> c) & 1u)) return -1;
+  return t.srows[start + __popcll(bits & ((1ull << c) - 1ull))];
 }
 
 // Workgroup index -> work index such that each XCD (workgroups are dealt to

@@ -1,9 +1,10 @@
-// Coordinate hash: key packing, Morton radix sort, open-addressing insert and
-// lookup. The "spatial hash of the active voxels" of the sparse convolution
+// Coordinate hash: key packing, Morton radix sort, and the open-addressing
+// table of occupied 4x4x4 blocks (occupancy bitmap + first sorted position).
+// This is the "spatial hash of the active voxels" of the sparse convolution
 // ("Running TRELLIS.2 on a Mac (1/3)", section "Swapping out the CUDA libraries
 // one at a time"), built on the device in HBM. The voxels are first sorted along
-// the Z-order curve so that the kernel-map pass and the gather-GEMM tiles walk
-// space in compact blocks.
+// the Z-order curve: a block's voxels are then consecutive, and the kernel-map
+// pass and the gather-GEMM tiles walk space in compact pieces.
 #include "common.h"
 #include "launch.h"
 
@@ -211,39 +212,88 @@ __global__ __launch_bounds__(kThreads) void radix_scatter(const uint64_t* __rest
   }
 }
 
-__global__ __launch_bounds__(kThreads) void table_clear(Slot* __restrict__ slots, int64_t cap) {
-  for (int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x; i < cap; i += int64_t(gridDim.x) * kThreads)
-    *reinterpret_cast<uint4*>(slots + i) = make_uint4(0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0u);
+// Each workgroup counts the block heads among its sorted keys (first key of
+// each 4x4x4 block) into part[block] and flags adjacent equal keys (duplicate
+// coordinates: equal keys are adjacent after the sort).
+__global__ __launch_bounds__(kThreads) void block_count(const uint64_t* __restrict__ keys, int64_t n,
+                                                        uint32_t* __restrict__ part, HashHeader* hdr) {
+  __shared__ uint32_t s_cnt[kThreads / 64];
+  uint32_t cnt = 0;
+  bool dup = false;
+  for (int64_t t = int64_t(blockIdx.x) * kThreads + threadIdx.x; t < n; t += int64_t(gridDim.x) * kThreads) {
+    const uint64_t k = keys[t];
+    const uint64_t prev = t > 0 ? keys[t - 1] : ~k;
+    cnt += (t == 0 || (prev >> 6) != (k >> 6)) ? 1u : 0u;
+    dup |= t > 0 && prev == k;
+  }
+  if (__ballot(dup) != 0 && (threadIdx.x & 63) == 0) atomicOr(&hdr->flags, kFlagDuplicate);
+  for (int o = 32; o > 0; o >>= 1) cnt += __shfl_xor(cnt, o, 64);
+  if ((threadIdx.x & 63) == 0) s_cnt[threadIdx.x >> 6] = cnt;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t c = 0;
+    for (int w = 0; w < kThreads / 64; ++w) c += s_cnt[w];
+    part[blockIdx.x] = c;
+  }
 }
 
-// Inserts the sorted keys. Equal keys are adjacent after the sort, so a
-// duplicate is the key equal to its predecessor; only the first is inserted.
-__global__ __launch_bounds__(kThreads) void table_insert(const uint64_t* __restrict__ keys,
-                                                         const int32_t* __restrict__ rows, int64_t n,
-                                                         Slot* __restrict__ slots, uint32_t mask,
-                                                         uint32_t shift, HashHeader* hdr) {
+// One workgroup: number of blocks, table capacity (power of two >= 2x blocks,
+// at least 16, at most max_cap) and hash shift, into the header.
+__global__ __launch_bounds__(kThreads) void block_size(const uint32_t* __restrict__ part, int nparts,
+                                                       uint32_t max_cap, HashHeader* hdr) {
+  __shared__ uint32_t s_cnt[kThreads / 64];
+  uint32_t c = 0;
+  for (int i = threadIdx.x; i < nparts; i += kThreads) c += part[i];
+  for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o, 64);
+  if ((threadIdx.x & 63) == 0) s_cnt[threadIdx.x >> 6] = c;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t nb = 0;
+    for (int w = 0; w < kThreads / 64; ++w) nb += s_cnt[w];
+    uint32_t cap = 16, lg = 4;
+    while (cap < 2u * nb && cap < max_cap) {
+      cap <<= 1;
+      ++lg;
+    }
+    hdr->nblocks = nb;
+    hdr->cap_mask = cap - 1;
+    hdr->shift = 64 - lg;
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void block_clear(BlockSlot* __restrict__ slots,
+                                                        const HashHeader* __restrict__ hdr) {
+  const uint32_t cap = hdr->cap_mask + 1u;
+  for (uint32_t i = blockIdx.x * kThreads + threadIdx.x; i < cap; i += gridDim.x * kThreads) {
+    uint4* p = reinterpret_cast<uint4*>(slots + i);
+    p[0] = make_uint4(0xFFFFFFFFu, 0xFFFFFFFFu, 0u, 0u);
+    p[1] = make_uint4(0u, 0u, 0u, 0u);
+  }
+}
+
+// The thread at each block head builds the block's occupancy bitmap from the
+// following sorted keys (at most 64) and inserts {block key, bitmap, start}.
+__global__ __launch_bounds__(kThreads) void block_insert(const uint64_t* __restrict__ keys, int64_t n,
+                                                         BlockSlot* __restrict__ slots, HashHeader* hdr) {
   const int64_t t = int64_t(blockIdx.x) * kThreads + threadIdx.x;
   if (t >= n) return;
-  const uint64_t key = keys[t];
-  const int32_t row = rows[t];
-  if (t > 0 && keys[t - 1] == key) {
-    atomicOr(&hdr->flags, kFlagDuplicate);
-    return;
+  const uint64_t k = keys[t];
+  const uint64_t bkey = k >> 6;
+  if (t > 0 && (keys[t - 1] >> 6) == bkey) return;
+  uint64_t bits = 0;
+  for (int64_t u = t; u < n && u < t + 64; ++u) {
+    const uint64_t ku = keys[u];
+    if ((ku >> 6) != bkey) break;
+    bits |= 1ull << (ku & 63u);
   }
-  if (key == kEmptyKey) {
-    atomicExch(&hdr->special_row, row);
-    return;
-  }
-  uint32_t s = home_slot(key, shift);
+  const uint32_t mask = hdr->cap_mask, shift = hdr->shift;
+  uint32_t s = home_slot(bkey, shift) & mask;
   for (uint32_t probe = 0; probe <= mask; ++probe) {
-    unsigned long long* kp = reinterpret_cast<unsigned long long*>(&slots[s].key);
-    const unsigned long long prev = atomicCAS(kp, kEmptyKey, key);
+    unsigned long long* kp = reinterpret_cast<unsigned long long*>(&slots[s].bkey);
+    const unsigned long long prev = atomicCAS(kp, kEmptyKey, bkey);
     if (prev == kEmptyKey) {
-      slots[s].row = row;
-      return;
-    }
-    if (prev == key) {  // cannot happen after the adjacent check; kept as a guard
-      atomicOr(&hdr->flags, kFlagDuplicate);
+      slots[s].bits = bits;
+      slots[s].start = uint32_t(t);
       return;
     }
     s = (s + 1) & mask;
@@ -251,8 +301,7 @@ __global__ __launch_bounds__(kThreads) void table_insert(const uint64_t* __restr
   atomicOr(&hdr->flags, kFlagCapacity);
 }
 
-__global__ __launch_bounds__(kThreads) void table_lookup(TableRef t, const HashHeader* hdr,
-                                                         const int4* __restrict__ q, int64_t nq,
+__global__ __launch_bounds__(kThreads) void table_lookup(TableRef t, const int4* __restrict__ q, int64_t nq,
                                                          int32_t* __restrict__ out) {
   const int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x;
   if (i >= nq) return;
@@ -261,14 +310,15 @@ __global__ __launch_bounds__(kThreads) void table_lookup(TableRef t, const HashH
     out[i] = -1;
     return;
   }
-  out[i] = table_find(t, make_key(uint32_t(c.x), uint32_t(c.y), uint32_t(c.z), uint32_t(c.w)),
-                      hdr->special_row);
+  out[i] = voxel_find(t, t.hdr->cap_mask, t.hdr->shift,
+                      make_key(uint32_t(c.x), uint32_t(c.y), uint32_t(c.z), uint32_t(c.w)));
 }
 
 __global__ void header_init(HashHeader* hdr) {
   hdr->flags = 0;
-  hdr->special_row = -1;
-  hdr->pad0 = hdr->pad1 = 0;
+  hdr->nblocks = 0;
+  hdr->cap_mask = 15;
+  hdr->shift = 60;
   hdr->or_bits = 0ull;
   hdr->and_bits = ~0ull;
 }
@@ -304,22 +354,20 @@ hipError_t launch_sort_pass(const uint64_t* kin, const int32_t* vin, uint64_t* k
   return hipGetLastError();
 }
 
-hipError_t launch_insert(const uint64_t* keys, const int32_t* rows, int64_t n, Slot* slots,
-                         uint32_t cap_mask, uint32_t shift, HashHeader* hdr, hipStream_t st) {
-  const int64_t cap = int64_t(cap_mask) + 1;
-  const int64_t cb = (cap + kThreads - 1) / kThreads;
-  table_clear<<<unsigned(cb < 4096 ? cb : 4096), kThreads, 0, st>>>(slots, cap);
-  if (n > 0)
-    table_insert<<<grid_for(n, kThreads), kThreads, 0, st>>>(keys, rows, n, slots, cap_mask, shift,
-                                                             hdr);
+hipError_t launch_blocks(const uint64_t* keys, int64_t n, BlockSlot* slots, uint32_t max_cap,
+                         uint32_t* part, HashHeader* hdr, hipStream_t st) {
+  const int nb = int(pack_partials(n));
+  if (n > 0) block_count<<<nb, kThreads, 0, st>>>(keys, n, part, hdr);
+  block_size<<<1, kThreads, 0, st>>>(part, n > 0 ? nb : 0, max_cap, hdr);
+  const uint32_t cb = (max_cap + kThreads - 1) / kThreads;
+  block_clear<<<cb < 2048u ? cb : 2048u, kThreads, 0, st>>>(slots, hdr);
+  if (n > 0) block_insert<<<grid_for(n, kThreads), kThreads, 0, st>>>(keys, n, slots, hdr);
   return hipGetLastError();
 }
 
-hipError_t launch_lookup(const TableRef& t, const HashHeader* hdr, const int32_t* q, int64_t nq,
-                         int32_t* out, hipStream_t st) {
+hipError_t launch_lookup(const TableRef& t, const int32_t* q, int64_t nq, int32_t* out, hipStream_t st) {
   if (nq > 0)
-    table_lookup<<<grid_for(nq, kThreads), kThreads, 0, st>>>(t, hdr, reinterpret_cast<const int4*>(q),
-                                                              nq, out);
+    table_lookup<<<grid_for(nq, kThreads), kThreads, 0, st>>>(t, reinterpret_cast<const int4*>(q), nq, out);
   return hipGetLastError();
 }
 

@@ -22,16 +22,22 @@ hipError_t launch_pack(const int32_t* coords, int64_t n, uint64_t* keys, int32_t
 hipError_t launch_sort_pass(const uint64_t* kin, const int32_t* vin, uint64_t* kout, int32_t* vout,
                             int64_t n, const DigitSel& sel, uint32_t* counts, uint32_t* totals,
                             hipStream_t st);
-hipError_t launch_insert(const uint64_t* keys, const int32_t* rows, int64_t n, Slot* slots,
-                         uint32_t cap_mask, uint32_t shift, HashHeader* hdr, hipStream_t st);
-hipError_t launch_lookup(const TableRef& t, const HashHeader* hdr, const int32_t* q, int64_t nq,
-                         int32_t* out, hipStream_t st);
+// Block table from the sorted keys: count blocks, size the table on the device
+// (capacity <= max_cap), clear it, insert one slot per block. Also flags
+// duplicate coordinates.
+hipError_t launch_blocks(const uint64_t* keys, int64_t n, BlockSlot* slots, uint32_t max_cap,
+                         uint32_t* part, HashHeader* hdr, hipStream_t st);
+hipError_t launch_lookup(const TableRef& t, const int32_t* q, int64_t nq, int32_t* out, hipStream_t st);
 
-hipError_t launch_kmap(const uint64_t* skeys, const int32_t* srows, int64_t n, const TableRef& t,
-                       const HashHeader* hdr, int32_t* nbr, uint32_t* mask, hipStream_t st);
+// Kernel map (nbr, caller order; mask, Morton order) and the gather-GEMM row
+// order: grows / gmask = Morton order regrouped inside windows of kGroupWindow
+// voxels by the octant pattern of the neighbour mask.
+constexpr int kGroupWindow = 4096;
+hipError_t launch_kmap(const uint64_t* skeys, int64_t n, const TableRef& t, int32_t* nbr, uint32_t* mask,
+                       int32_t* grows, uint32_t* gmask, hipStream_t st);
 
-// Forward kernels. `srows` is the Morton order (sorted position -> caller row),
-// `mask` the per-sorted-voxel 27-bit neighbour masks.
+// Forward kernels. `srows` is the row order of the tiles (position -> caller
+// row), `mask` the 27-bit neighbour mask of the voxel at each position.
 struct ConvArgs {
   const int32_t* nbr;   // [n, 27] caller order
   const int32_t* srows; // [n]
