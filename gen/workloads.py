@@ -61,12 +61,12 @@ class Workload:
     B: int
     c_in: int
     c_out: int
-    dtype: str            # "f32" or "bf16"
+    dtype: str            # "f32", "bf16", "f16", "mixed-bf16" or "mixed-f16"
     seed: int
     order: str            # "raster" or "shuffled"
     coords: np.ndarray    # int32 [N, 4] (b, x, y, z)
-    x: np.ndarray | None = None   # float32 [N, c_in]; bf16-representable when dtype == "bf16"
-    w: np.ndarray | None = None   # float32 [27, c_in, c_out]; bf16-representable when dtype == "bf16"
+    x: np.ndarray | None = None   # float32 [N, c_in], representable in dtype's feature type
+    w: np.ndarray | None = None   # float32 [27, c_in, c_out], representable in dtype's weight type
 
     @property
     def n(self) -> int:
@@ -331,18 +331,46 @@ def make_coords(name: str, seed: int | None = None) -> np.ndarray:
     raise KeyError(name)
 
 
+def round_to_f16(a: np.ndarray) -> np.ndarray:
+    """Nearest-even rounding to IEEE half precision (numpy's own conversion),
+    returned as float32."""
+    return np.asarray(a, dtype=np.float32).astype(np.float16).astype(np.float32)
+
+
+# dtype -> (rounding of x, rounding of w). "mixed-bf16" / "mixed-f16": fp32
+# features with half-precision weights.
+_ROUNDINGS = {
+    "f32": (None, None),
+    "bf16": (round_to_bf16, round_to_bf16),
+    "f16": (round_to_f16, round_to_f16),
+    "mixed-bf16": (None, round_to_bf16),
+    "mixed-f16": (None, round_to_f16),
+}
+
+
 def make_values(n: int, c_in: int, c_out: int, dtype: str, rng: np.random.Generator):
     """Features N(0,1) [n, c_in]; weights N(0, 1/(27 c_in)) [27, c_in, c_out];
-    both rounded to bf16 (nearest-even) when dtype == 'bf16'. float32 arrays."""
+    each rounded (nearest-even) to the type `dtype` gives it. float32 arrays."""
+    if dtype not in _ROUNDINGS:
+        raise ValueError(dtype)
     x = rng.standard_normal((n, c_in), dtype=np.float32)
     w = rng.standard_normal((27, c_in, c_out), dtype=np.float32)
     w *= np.float32(1.0 / math.sqrt(27.0 * c_in))
-    if dtype == "bf16":
-        x = round_to_bf16(x)
-        w = round_to_bf16(w)
-    elif dtype != "f32":
-        raise ValueError(dtype)
+    rx, rw = _ROUNDINGS[dtype]
+    if rx is not None:
+        x = rx(x)
+    if rw is not None:
+        w = rw(w)
     return x, w
+
+
+def make_epilogue(n: int, c_out: int, out_dtype: str, rng: np.random.Generator):
+    """Bias N(0, 1/4) [c_out] (float32) and residual N(0, 1) [n, c_out], the
+    residual rounded to out_dtype ('f32', 'bf16' or 'f16')."""
+    bias = (rng.standard_normal(c_out, dtype=np.float32) * np.float32(0.5)).astype(np.float32)
+    res = rng.standard_normal((n, c_out), dtype=np.float32)
+    rx = _ROUNDINGS[out_dtype][0]
+    return bias, (res if rx is None else rx(res))
 
 
 def make(name: str, seed_offset: int = 0, order: str = "raster",

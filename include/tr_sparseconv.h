@@ -65,7 +65,14 @@ typedef enum {
   TR_SC_ERR_HIP = -7          /* a HIP runtime call failed                    */
 } tr_sc_status;
 
-typedef enum { TR_SC_F32 = 0, TR_SC_BF16 = 1 } tr_sc_dtype;
+typedef enum { TR_SC_F32 = 0, TR_SC_BF16 = 1, TR_SC_F16 = 2 } tr_sc_dtype;
+
+/* Activation of the fused epilogue (tr_sparseconv_forward_fused). */
+typedef enum {
+  TR_SC_ACT_NONE = 0,
+  TR_SC_ACT_RELU = 1, /* max(v, 0)                 */
+  TR_SC_ACT_SILU = 2  /* v / (1 + exp(-v))         */
+} tr_sc_act;
 
 typedef struct tr_sc_hash tr_sc_hash; /* coordinate hash (opaque)  */
 typedef struct tr_sc_kmap tr_sc_kmap; /* kernel map (opaque)       */
@@ -147,8 +154,9 @@ size_t tr_sparseconv_forward_workspace_bytes(int c_in, int c_out, int dtype);
  * x      device [n, c_in] features, dtype `dtype`.
  * w      device [27, c_in, c_out] weights, dtype `dtype`.
  * y      device [n, c_out] output, dtype `dtype`; every element is written.
- * dtype  TR_SC_BF16: bf16 inputs, fp32 accumulation, output rounded to bf16
- *        (nearest, ties to even); needs c_in % 8 == 0 and c_out % 8 == 0.
+ * dtype  TR_SC_BF16 / TR_SC_F16: half inputs, fp32 accumulation, output
+ *        rounded to the same half type (nearest, ties to even); needs
+ *        c_in % 8 == 0 and c_out % 8 == 0.
  *        TR_SC_F32: fp32 inputs, fp32 accumulation and output; any c >= 1.
  * No atomics: the result is the same bit for bit on every call. x and y must
  * not overlap. */
@@ -161,7 +169,7 @@ int tr_sparseconv_forward(const tr_sc_kmap* m, const void* x, const void* w, voi
  *
  * tr_sparseconv_pack_weights: wp (device, >= tr_sparseconv_packed_weights_bytes
  * bytes, 16-byte aligned, caller-owned) receives w [27, c_in, c_out] re-laid
- * out for the matrix cores (bf16: [27, c_out, c_in]; f32: unchanged copy).
+ * out for the matrix cores (bf16, f16: [27, c_out, c_in]; f32: unchanged copy).
  * tr_sparseconv_forward_packed: as tr_sparseconv_forward, reading the packed
  * weights. Same argument rules and errors as tr_sparseconv_forward. */
 size_t tr_sparseconv_packed_weights_bytes(int c_in, int c_out, int dtype);
@@ -169,6 +177,37 @@ int tr_sparseconv_pack_weights(const void* w, int c_in, int c_out, int dtype, vo
                                size_t wp_bytes, void* stream);
 int tr_sparseconv_forward_packed(const tr_sc_kmap* m, const void* x, const void* wp, void* y,
                                  int c_in, int c_out, int dtype, void* stream);
+
+/* The gather-GEMM with its epilogue fused into the same pass, and mixed
+ * precision. The pages fuse bias, activation, residual add and the output
+ * rounding into the convolution pass ("Porting TRELLIS.2 From Python to Rust
+ * and Metal", section V), and keep the decoders' incoming latent in fp32 while
+ * the layers after it run in half precision (same page, section IV).
+ *
+ *   y[i, co] = round_y( act( conv(x, w)[i, co] + bias[co] ) + residual[i, co] )
+ *
+ * computed in fp32 and rounded once, to y's type.
+ * m         kernel map.
+ * x         device [n, c_in], type x_dtype.
+ * wp        packed weights of type w_dtype (tr_sparseconv_pack_weights).
+ * w_dtype   TR_SC_BF16 or TR_SC_F16: x_dtype is w_dtype, or TR_SC_F32 (fp32
+ *           features, never rounded to half first: x is carried as a sum of
+ *           half terms, each multiplied exactly -- 3 bf16 terms hold x
+ *           exactly; 2 fp16 terms hold it to within 2^-23 |x| + 2^-25 and
+ *           need |x| < 65504); y_dtype is w_dtype or TR_SC_F32; c_in
+ *           and c_out multiples of 8; x, y, residual 16-byte aligned.
+ *           TR_SC_F32: x_dtype = y_dtype = TR_SC_F32, any c >= 1.
+ * bias      device fp32 [c_out], or NULL for none.
+ * act       tr_sc_act.
+ * residual  device [n, c_out] of type y_dtype, or NULL. It may be y itself
+ *           (in-place residual add); otherwise it must not overlap y.
+ * y         device [n, c_out], type y_dtype; every element is written. x must
+ *           not overlap y.
+ * Errors as tr_sparseconv_forward; TR_SC_ERR_UNSUPPORTED for other dtype
+ * combinations. */
+int tr_sparseconv_forward_fused(const tr_sc_kmap* m, const void* x, int x_dtype, const void* wp,
+                                int w_dtype, const float* bias, int act, const void* residual,
+                                void* y, int y_dtype, int c_in, int c_out, void* stream);
 
 /* Message of the last failed call on this thread ("" if none). */
 const char* tr_sparseconv_last_error(void);

@@ -56,6 +56,8 @@ def _load():
         lib.oc_kernel_map.restype = ctypes.c_int
         lib.oc_forward.argtypes = [P, I64, P, I64, P, P, ctypes.c_int, ctypes.c_int, P]
         lib.oc_forward.restype = ctypes.c_int
+        lib.oc_epilogue.argtypes = [P, I64, ctypes.c_int, P, P, ctypes.c_int]
+        lib.oc_epilogue.restype = ctypes.c_int
         lib.oc_num_threads.argtypes = []
         lib.oc_num_threads.restype = ctypes.c_int
         _lib = lib
@@ -150,6 +152,22 @@ def forward(nbr: np.ndarray, x: np.ndarray, w: np.ndarray, rows=None) -> np.ndar
     if st != OK:
         raise OracleError(st, "forward")
     return y
+
+
+ACTS = {"none": 0, "relu": 1, "silu": 2}
+
+
+def epilogue(y: np.ndarray, bias=None, residual=None, act: str = "none") -> np.ndarray:
+    """act(y + bias) + residual in fp64 (y: [m, c_out]; residual rows match y's rows)."""
+    yd = np.array(y, dtype=np.float64, copy=True, order="C")
+    m, c_out = yd.shape
+    b = None if bias is None else widen(bias).reshape(c_out)
+    r = None if residual is None else widen(residual).reshape(m, c_out)
+    st = _load().oc_epilogue(_ptr(yd), m, c_out, None if b is None else _ptr(b),
+                             None if r is None else _ptr(r), ACTS[act])
+    if st != OK:
+        raise OracleError(st, "epilogue")
+    return yd
 
 
 def conv(coords: np.ndarray, x: np.ndarray, w: np.ndarray, rows=None):

@@ -37,6 +37,7 @@
 // (k, ci) order and never rounded.
 #include <algorithm>
 #include <climits>
+#include <cmath>
 #include <cstdint>
 #include <cstring>
 #include <unordered_map>
@@ -178,6 +179,29 @@ int oc_forward(const int32_t* nbr, int64_t n, const int64_t* rows, int64_t nrows
         }
       }
       std::memcpy(y + q * c_out, acc.data(), sizeof(double) * size_t(c_out));
+    }
+  }
+  return kOk;
+}
+
+// The fused epilogue of the gather-GEMM: the pages fuse "bias, rounding,
+// activation and the residual add" into the convolution pass ("Porting
+// TRELLIS.2 ...", section V). Reading: out = act(y + bias) + residual, rounded
+// once at the end (here: never, fp64). act: 0 none, 1 ReLU max(v, 0),
+// 2 SiLU v / (1 + exp(-v)). bias is [c_out] or NULL; residual is [m, c_out]
+// (the rows of y, in the same order) or NULL. Applied in place on y [m, c_out].
+int oc_epilogue(double* y, int64_t m, int c_out, const double* bias, const double* residual, int act) {
+  if (m < 0 || c_out <= 0 || act < 0 || act > 2) return kErrInvalid;
+  if (m > 0 && y == nullptr) return kErrInvalid;
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < m; ++i) {
+    for (int co = 0; co < c_out; ++co) {
+      double v = y[i * c_out + co];
+      if (bias) v += bias[co];
+      if (act == 1) v = v > 0.0 ? v : 0.0;
+      if (act == 2) v = v / (1.0 + std::exp(-v));
+      if (residual) v += residual[i * c_out + co];
+      y[i * c_out + co] = v;
     }
   }
   return kOk;

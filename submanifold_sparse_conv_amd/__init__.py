@@ -17,11 +17,12 @@ import torch
 from . import _lib
 from ._lib import TrSparseConvError, check  # noqa: F401
 
-__all__ = ["build_hash", "build_kernel_map", "forward", "pack_weights", "forward_packed",
+__all__ = ["build_hash", "build_kernel_map", "forward", "pack_weights", "forward_packed", "forward_fused",
            "status", "hash_lookup", "hash_sorted_rows", "HashTable", "KernelMap", "PackedWeights",
            "TrSparseConvError", "version", "forward_workspace_bytes", "Workspace"]
 
-_DTYPES = {torch.float32: _lib.F32, torch.bfloat16: _lib.BF16}
+_DTYPES = {torch.float32: _lib.F32, torch.bfloat16: _lib.BF16, torch.float16: _lib.F16}
+_ACTS = {"none": _lib.ACT_NONE, "relu": _lib.ACT_RELU, "silu": _lib.ACT_SILU}
 
 
 def version() -> tuple[int, int]:
@@ -220,6 +221,44 @@ def forward_packed(m: KernelMap, x: torch.Tensor, wp: PackedWeights,
         check(_lib.lib().tr_sparseconv_forward_packed(m.handle, _ptr(x), wp._ws.ptr, _ptr(out),
                                                       wp.c_in, wp.c_out, _DTYPES[wp.dtype],
                                                       _stream(x.device)))
+    return out
+
+
+def forward_fused(m: KernelMap, x: torch.Tensor, wp: PackedWeights, bias: torch.Tensor | None = None,
+                  act: str = "none", residual: torch.Tensor | None = None,
+                  out_dtype: torch.dtype | None = None, out: torch.Tensor | None = None) -> torch.Tensor:
+    """act(conv(x, w) + bias) + residual in one pass (tr_sparseconv_forward_fused).
+
+    x may be fp32 with half weights (mixed precision); the output is the weights'
+    type or fp32 (out_dtype, default: x's type). bias is fp32 [C_out]; residual
+    has the output's type and shape and may be `out` itself."""
+    if x.dtype not in _DTYPES:
+        raise ValueError(f"unsupported dtype {x.dtype}")
+    _require(x, "x", x.dtype, 2)
+    if int(x.shape[0]) != m.n or int(x.shape[1]) != wp.c_in:
+        raise ValueError(f"x must be [{m.n}, {wp.c_in}], got {tuple(x.shape)}")
+    if act not in _ACTS:
+        raise ValueError(f"act must be one of {sorted(_ACTS)}")
+    out_dtype = out_dtype or (out.dtype if out is not None else x.dtype)
+    if out_dtype not in _DTYPES:
+        raise ValueError(f"unsupported output dtype {out_dtype}")
+    if out is None:
+        out = torch.empty((m.n, wp.c_out), dtype=out_dtype, device=x.device)
+    _require(out, "out", out_dtype, 2)
+    if tuple(out.shape) != (m.n, wp.c_out):
+        raise ValueError(f"out must be [{m.n}, {wp.c_out}]")
+    if bias is not None:
+        _require(bias, "bias", torch.float32, 1)
+        if int(bias.shape[0]) != wp.c_out:
+            raise ValueError(f"bias must be [{wp.c_out}]")
+    if residual is not None:
+        _require(residual, "residual", out_dtype, 2)
+        if tuple(residual.shape) != (m.n, wp.c_out):
+            raise ValueError(f"residual must be [{m.n}, {wp.c_out}]")
+    with torch.cuda.device(x.device):
+        check(_lib.lib().tr_sparseconv_forward_fused(
+            m.handle, _ptr(x), _DTYPES[x.dtype], wp._ws.ptr, _DTYPES[wp.dtype], _ptr(bias), _ACTS[act],
+            _ptr(residual), _ptr(out), _DTYPES[out_dtype], wp.c_in, wp.c_out, _stream(x.device)))
     return out
 
 

@@ -27,6 +27,11 @@ STATUS_NAMES = {OK: "OK", ERR_INVALID_ARG: "INVALID_ARG", ERR_COORD_RANGE: "COOR
 
 F32 = 0
 BF16 = 1
+F16 = 2
+
+ACT_NONE = 0
+ACT_RELU = 1
+ACT_SILU = 2
 
 # (name, restype, argtypes) of every exported symbol.
 _P = ctypes.c_void_p
@@ -52,6 +57,7 @@ SIGNATURES = [
     ("tr_sparseconv_packed_weights_bytes", _SZ, [_I, _I, _I]),
     ("tr_sparseconv_pack_weights", _I, [_P, _I, _I, _I, _P, _SZ, _P]),
     ("tr_sparseconv_forward_packed", _I, [_P, _P, _P, _P, _I, _I, _I, _P]),
+    ("tr_sparseconv_forward_fused", _I, [_P, _P, _I, _P, _I, _P, _I, _P, _P, _I, _I, _I, _P]),
 ]
 
 _lib = None

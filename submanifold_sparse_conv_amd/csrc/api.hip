@@ -261,7 +261,8 @@ void tr_sparseconv_kmap_destroy(tr_sc_kmap* m) {
 size_t tr_sparseconv_packed_weights_bytes(int c_in, int c_out, int dtype) {
   if (c_in <= 0 || c_out <= 0) return 0;
   const size_t elems = size_t(27) * size_t(c_in) * size_t(c_out);
-  if (dtype == TR_SC_BF16) return size_t(packed_weight_elems(c_in, c_out)) * 2 + 256;  // + zero block
+  if (dtype == TR_SC_BF16 || dtype == TR_SC_F16)
+    return size_t(packed_weight_elems(c_in, c_out)) * 2 + 256;  // + zero block
   if (dtype == TR_SC_F32) return align_up(elems * 4, 256);
   return 0;
 }
@@ -273,31 +274,33 @@ size_t tr_sparseconv_forward_workspace_bytes(int c_in, int c_out, int dtype) {
 
 namespace {
 
+bool is_half(int dtype) { return dtype == TR_SC_BF16 || dtype == TR_SC_F16; }
+
 int check_channels(const char* who, int c_in, int c_out, int dtype) {
   if (c_in <= 0 || c_out <= 0) return fail(TR_SC_ERR_INVALID_ARG, "%s: c_in = %d, c_out = %d", who, c_in, c_out);
-  if (dtype != TR_SC_F32 && dtype != TR_SC_BF16) return fail(TR_SC_ERR_UNSUPPORTED, "%s: dtype %d", who, dtype);
-  if (dtype == TR_SC_BF16 && (c_in % 8 != 0 || c_out % 8 != 0))
-    return fail(TR_SC_ERR_UNSUPPORTED, "%s: bf16 needs c_in and c_out multiples of 8 (got %d, %d)", who, c_in,
-                c_out);
+  if (dtype != TR_SC_F32 && !is_half(dtype)) return fail(TR_SC_ERR_UNSUPPORTED, "%s: dtype %d", who, dtype);
+  if (is_half(dtype) && (c_in % 8 != 0 || c_out % 8 != 0))
+    return fail(TR_SC_ERR_UNSUPPORTED, "%s: half precision needs c_in and c_out multiples of 8 (got %d, %d)", who,
+                c_in, c_out);
   return TR_SC_OK;
 }
 
 bool misaligned16(const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 != 0; }
 
 // Launches the gather-GEMM of an already validated call.
-int run_forward(const char* who, const tr_sc_kmap* m, const void* x, const void* wp, void* y, int c_in,
-                int c_out, int dtype, hipStream_t st) {
+int run_forward(const char* who, const tr_sc_kmap* m, const void* x, int x_dtype, const void* wp, int w_dtype,
+                void* y, int y_dtype, const Epilogue& epi, int c_in, int c_out, hipStream_t st) {
   if (x == nullptr || wp == nullptr || y == nullptr) return fail(TR_SC_ERR_INVALID_ARG, "%s: NULL tensor", who);
   if (int64_t(m->n) * c_out >= (int64_t(1) << 40) || int64_t(m->n) * c_in >= (int64_t(1) << 40))
     return fail(TR_SC_ERR_UNSUPPORTED, "%s: tensor too large", who);
-  ConvArgs a{m->nbr, m->grows, m->gmask, m->n, x, wp, y, c_in, c_out};
+  ConvArgs a{m->nbr, m->grows, m->gmask, m->n, x, wp, y, c_in, c_out, x_dtype, w_dtype, y_dtype, epi};
   hipError_t e;
-  if (dtype == TR_SC_F32) {
+  if (w_dtype == TR_SC_F32) {
     e = launch_forward_simple_f32(a, st);
   } else {
-    if (misaligned16(x) || misaligned16(y) || misaligned16(wp))
-      return fail(TR_SC_ERR_INVALID_ARG, "%s: bf16 x, y and packed weights must be 16-byte aligned", who);
-    e = launch_forward_mfma_bf16(a, wp, st);
+    if (misaligned16(x) || misaligned16(y) || misaligned16(wp) || misaligned16(epi.residual))
+      return fail(TR_SC_ERR_INVALID_ARG, "%s: x, y, residual and packed weights must be 16-byte aligned", who);
+    e = launch_forward_mfma(a, wp, st);
   }
   if (e != hipSuccess) return hip_fail(e, who);
   return TR_SC_OK;
@@ -315,7 +318,7 @@ int tr_sparseconv_pack_weights(const void* w, int c_in, int c_out, int dtype, vo
   if (misaligned16(wp)) return fail(TR_SC_ERR_INVALID_ARG, "pack_weights: wp not 16-byte aligned");
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e;
-  if (dtype == TR_SC_BF16)
+  if (is_half(dtype))
     e = launch_pack_weights(w, wp, c_in, c_out, st);
   else
     e = hipMemcpyAsync(wp, w, size_t(27) * c_in * c_out * 4, hipMemcpyDeviceToDevice, st);
@@ -330,7 +333,8 @@ int tr_sparseconv_forward_packed(const tr_sc_kmap* m, const void* x, const void*
   const int c = check_channels("forward_packed", c_in, c_out, dtype);
   if (c != TR_SC_OK) return c;
   if (m->n == 0) return TR_SC_OK;
-  return run_forward("forward_packed", m, x, wp, y, c_in, c_out, dtype, static_cast<hipStream_t>(stream));
+  return run_forward("forward_packed", m, x, dtype, wp, dtype, y, dtype, Epilogue{nullptr, nullptr, kActNone},
+                     c_in, c_out, static_cast<hipStream_t>(stream));
 }
 
 int tr_sparseconv_forward(const tr_sc_kmap* m, const void* x, const void* w, void* y, int c_in, int c_out,
@@ -344,11 +348,34 @@ int tr_sparseconv_forward(const tr_sc_kmap* m, const void* x, const void* w, voi
   if (m->n == 0) return TR_SC_OK;
   if (w == nullptr) return fail(TR_SC_ERR_INVALID_ARG, "forward: NULL tensor");
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (dtype == TR_SC_F32) return run_forward("forward", m, x, w, y, c_in, c_out, dtype, st);
+  const Epilogue none{nullptr, nullptr, kActNone};
+  if (dtype == TR_SC_F32) return run_forward("forward", m, x, dtype, w, dtype, y, dtype, none, c_in, c_out, st);
   if (misaligned16(workspace)) return fail(TR_SC_ERR_INVALID_ARG, "forward: workspace not 16-byte aligned");
   hipError_t e = launch_pack_weights(w, workspace, c_in, c_out, st);
   if (e != hipSuccess) return hip_fail(e, "forward: pack");
-  return run_forward("forward", m, x, workspace, y, c_in, c_out, dtype, st);
+  return run_forward("forward", m, x, dtype, workspace, dtype, y, dtype, none, c_in, c_out, st);
+}
+
+int tr_sparseconv_forward_fused(const tr_sc_kmap* m, const void* x, int x_dtype, const void* wp, int w_dtype,
+                                const float* bias, int act, const void* residual, void* y, int y_dtype,
+                                int c_in, int c_out, void* stream) {
+  if (m == nullptr || m->magic != kKmapMagic)
+    return fail(TR_SC_ERR_INVALID_ARG, "forward_fused: bad kernel-map handle");
+  const int c = check_channels("forward_fused", c_in, c_out, w_dtype);
+  if (c != TR_SC_OK) return c;
+  if (act != TR_SC_ACT_NONE && act != TR_SC_ACT_RELU && act != TR_SC_ACT_SILU)
+    return fail(TR_SC_ERR_INVALID_ARG, "forward_fused: activation %d", act);
+  const bool ok_types = w_dtype == TR_SC_F32
+                            ? (x_dtype == TR_SC_F32 && y_dtype == TR_SC_F32)
+                            : ((x_dtype == w_dtype || x_dtype == TR_SC_F32) &&
+                               (y_dtype == w_dtype || y_dtype == TR_SC_F32));
+  if (!ok_types)
+    return fail(TR_SC_ERR_UNSUPPORTED, "forward_fused: x dtype %d, weight dtype %d, y dtype %d", x_dtype, w_dtype,
+                y_dtype);
+  if (m->n == 0) return TR_SC_OK;
+  if (x == y) return fail(TR_SC_ERR_INVALID_ARG, "forward_fused: x and y are the same buffer");
+  return run_forward("forward_fused", m, x, x_dtype, wp, w_dtype, y, y_dtype, Epilogue{bias, residual, act}, c_in,
+                     c_out, static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

@@ -1,5 +1,5 @@
-// Gather-GEMM on the matrix cores (bf16 in, fp32 accumulate, bf16 out): the
-// compute half of the sparse convolution -- a gather-GEMM over the neighbour
+// Gather-GEMM on the matrix cores (bf16 or fp16 operands, fp32 accumulate):
+// the compute half of the sparse convolution -- a gather-GEMM over the neighbour
 // table with half-precision inputs and single-precision accumulation
 // ("Porting TRELLIS.2 From Python to Rust and Metal", section V), i.e. the
 // per-kernel-position gather -> matmul -> sum of "Running TRELLIS.2 on a Mac
@@ -18,7 +18,13 @@
 // global memory straight into registers, one stage ahead. The stage's weight
 // slice, which all four waves read, is copied into LDS with global_load_lds
 // (double-buffered, XOR-swizzled 128-byte rows). Matrix instruction:
-// v_mfma_f32_16x16x32_bf16.
+// v_mfma_f32_16x16x32_bf16 / _f16.
+//
+// Precision paths: half features with half weights; or fp32 features with half
+// weights, each fp32 value carried as a sum of half terms (the pages' decoders
+// keep their incoming latent in fp32 and run the layers after it in half --
+// "Porting TRELLIS.2 ...", section IV). Output: half or fp32, after a fused
+// bias / activation / residual epilogue.
 //
 // Weights are first re-laid out to [27][C_out][C_in] (input channels
 // contiguous), the operand order of the matrix instruction, followed by a
@@ -30,6 +36,7 @@ namespace trsc {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
@@ -61,30 +68,98 @@ __global__ void zero_block(uint16_t* z) {
   reinterpret_cast<uint4*>(z)[threadIdx.x & 15] = make_uint4(0u, 0u, 0u, 0u);
 }
 
+// The two half types of the matrix cores: their MFMA and conversions.
+template <bool F16>
+struct Half;
+template <>
+struct Half<false> {
+  typedef bf16x8 vec;
+  typedef __bf16 elt;
+  static __device__ __forceinline__ f32x4 mma(vec a, vec b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ float widen(uint16_t h) { return bf16_to_f32(h); }
+  static __device__ __forceinline__ uint16_t narrow(float v) { return f32_to_bf16_rne(v); }
+};
+template <>
+struct Half<true> {
+  typedef f16x8 vec;
+  typedef _Float16 elt;
+  static __device__ __forceinline__ f32x4 mma(vec a, vec b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ float widen(uint16_t h) {
+    return float(__builtin_bit_cast(_Float16, h));
+  }
+  static __device__ __forceinline__ uint16_t narrow(float v) {
+    return __builtin_bit_cast(uint16_t, static_cast<_Float16>(v));  // nearest, ties to even
+  }
+};
+
+// fp32 features as a sum of XT half-precision terms, x = t0 + t1 (+ t2):
+// each term is the rounding of what the earlier ones left over, and every
+// remainder is exact in fp32. A half weight times a half term is exact in the
+// fp32 accumulator, so the XT products carry x itself rather than x rounded to
+// half precision: three bf16 terms hold all 24 significant bits; two fp16 terms
+// hold x to within 2^-23 |x| (2^-25 absolute where the second term is below
+// the fp16 normal range).
+template <class H, int XT>
+__device__ __forceinline__ void split_terms(const uint4 (&raw)[2], typename H::vec (&t)[XT]) {
+  const float* f = reinterpret_cast<const float*>(raw);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    float r = f[e];
+#pragma unroll
+    for (int q = 0; q < XT; ++q) {
+      const typename H::elt h = static_cast<typename H::elt>(r);
+      t[q][e] = h;
+      if (q + 1 < XT) r -= static_cast<float>(h);
+    }
+  }
+}
+
+__device__ __forceinline__ float activate(float v, int act) {
+  if (act == kActRelu) return v < 0.f ? 0.f : v;
+  if (act == kActSilu) return v / (1.f + expf(-v));
+  return v;
+}
+
+struct RowsArgs {
+  const int32_t* nbr;
+  const int32_t* srows;
+  const uint32_t* vmask;
+  int64_t n;
+  const void* x;          // [n, c_in]: half (XT = 1) or fp32 (XT > 1)
+  const uint16_t* wp;     // packed [27][c_out][c_in] half weights
+  const uint16_t* zeros;  // 256 zero bytes
+  void* y;                // [n, c_out]: half or fp32 (y_f32)
+  const float* bias;      // [c_out] or null
+  const void* residual;   // [n, c_out], y's type, or null; may be y itself
+  int act, y_f32;
+  int c_in, c_out, n_tiles_n;
+};
+
 // Wave w of the workgroup owns rows [16*FM*w, 16*FM*(w+1)) of the tile and all
 // TN = 16*FN output channels. The gather indices of a tap are fetched one tap
 // ahead, the A fragments and the weight slice one stage ahead.
-template <int FM, int FN>
-__global__ __launch_bounds__(kThreads, 2) void fwd_rows(const int32_t* __restrict__ nbr,
-                                                        const int32_t* __restrict__ srows,
-                                                        const uint32_t* __restrict__ vmask, int64_t n,
-                                                        const uint16_t* __restrict__ x,
-                                                        const uint16_t* __restrict__ wp,
-                                                        const uint16_t* __restrict__ zeros,
-                                                        uint16_t* __restrict__ y, int c_in, int c_out,
-                                                        int n_tiles_n) {
+template <int FM, int FN, bool F16, int XT>
+__global__ __launch_bounds__(kThreads, 2) void fwd_rows(const RowsArgs p) {
+  typedef Half<F16> H;
+  typedef typename H::vec hvec;
   constexpr int WM = 16 * FM, TM = 4 * WM, TN = 16 * FN;
   constexpr int KC = 64, ROWB = KC * 2;
+  constexpr int AV = XT == 1 ? 1 : 2;         // 16-byte loads per 8 input channels
   constexpr int BBUF = TN * ROWB;             // weight slice of one stage
-  constexpr int OSTAGE = 4 * 16 * TN * 2;     // 16 output rows per wave, four waves
+  constexpr int OSTAGE = 4 * 16 * TN * 4;     // 16 fp32 output rows per wave, four waves
   __shared__ __attribute__((aligned(1024))) unsigned char bbuf0[BBUF > OSTAGE ? BBUF : OSTAGE];
   __shared__ __attribute__((aligned(1024))) unsigned char bbuf1[BBUF];
   __shared__ int32_t s_taps[27];
   __shared__ uint32_t s_mask;
 
+  const int c_in = p.c_in, c_out = p.c_out;
   const int tile = xcd_remap(blockIdx.x, gridDim.x);
-  const int64_t t0 = int64_t(tile / n_tiles_n) * TM;
-  const int n0 = (tile % n_tiles_n) * TN;
+  const int64_t t0 = int64_t(tile / p.n_tiles_n) * TM;
+  const int n0 = (tile % p.n_tiles_n) * TN;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, kg = lane >> 4;
 
@@ -94,8 +169,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_rows(const int32_t* __restric
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
     const int64_t t = t0 + wave * WM + i * 16 + lr;
-    crow[i] = t < n ? srows[t] : -1;
-    if (t < n) m |= vmask[t];
+    crow[i] = t < p.n ? p.srows[t] : -1;
+    if (t < p.n) m |= p.vmask[t];
   }
   for (int o = 32; o > 0; o >>= 1) m |= __shfl_xor(m, o, 64);
   if (tid == 0) s_mask = 0;
@@ -113,10 +188,10 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_rows(const int32_t* __restric
   auto fetch_idx = [&](int ti, int32_t (&dst)[FM]) {
     const int k = s_taps[ti];
 #pragma unroll
-    for (int i = 0; i < FM; ++i) dst[i] = crow[i] >= 0 ? nbr[int64_t(crow[i]) * 27 + k] : -1;
+    for (int i = 0; i < FM; ++i) dst[i] = crow[i] >= 0 ? p.nbr[int64_t(crow[i]) * 27 + k] : -1;
   };
   // Issue stage st: A fragments into registers, weight slice into LDS.
-  auto issue = [&](int st, uint4 (&a)[FM][2], unsigned char* bdst) {
+  auto issue = [&](int st, uint4 (&a)[FM][2][AV], unsigned char* bdst) {
     const int ti = st / nchunks;
     const int c0 = (st - ti * nchunks) * KC;
 #pragma unroll
@@ -124,17 +199,22 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_rows(const int32_t* __restric
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
         const int c = c0 + kk * 32 + kg * 8;
-        const uint16_t* g = (srcL[i] >= 0 && c < c_in) ? x + int64_t(srcL[i]) * c_in + c : zeros;
-        a[i][kk] = *reinterpret_cast<const uint4*>(g);
+        const bool ok = srcL[i] >= 0 && c < c_in;
+        const int64_t off = int64_t(srcL[i]) * c_in + c;
+        const unsigned char* g =
+            ok ? static_cast<const unsigned char*>(p.x) + off * (XT == 1 ? 2 : 4)
+               : reinterpret_cast<const unsigned char*>(p.zeros);
+#pragma unroll
+        for (int v = 0; v < AV; ++v) a[i][kk][v] = reinterpret_cast<const uint4*>(g)[v];
       }
-    const uint16_t* wk = wp + int64_t(s_taps[ti]) * c_out * c_in;
+    const uint16_t* wk = p.wp + int64_t(s_taps[ti]) * c_out * c_in;
 #pragma unroll
     for (int i = wave; i < TN / 8; i += 4) {
       const int col = i * 8 + (lane >> 3);
       const int c = c0 + swz(col, lane & 7) * 8;
       const void* g = (n0 + col < c_out && c < c_in)
                           ? static_cast<const void*>(wk + int64_t(n0 + col) * c_in + c)
-                          : static_cast<const void*>(zeros);
+                          : static_cast<const void*>(p.zeros);
       copy16_to_lds(g, bdst + i * 1024);
     }
   };
@@ -145,18 +225,26 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_rows(const int32_t* __restric
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](const uint4 (&a)[FM][2], const unsigned char* bsrc) {
+  auto compute = [&](const uint4 (&a)[FM][2][AV], const unsigned char* bsrc) {
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       const int chunk = kk * 4 + kg;
+      hvec av[FM][XT];
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        if constexpr (XT == 1)
+          av[i][0] = *reinterpret_cast<const hvec*>(&a[i][kk][0]);
+        else
+          split_terms<H, XT>(a[i][kk], av[i]);
+      }
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
         const int r = j * 16 + lr;
-        const bf16x8 b = *reinterpret_cast<const bf16x8*>(bsrc + r * ROWB + swz(r, chunk) * 16);
+        const hvec b = *reinterpret_cast<const hvec*>(bsrc + r * ROWB + swz(r, chunk) * 16);
 #pragma unroll
         for (int i = 0; i < FM; ++i)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              *reinterpret_cast<const bf16x8*>(&a[i][kk]), b, acc[i][j], 0, 0, 0);
+#pragma unroll
+          for (int q = 0; q < XT; ++q) acc[i][j] = H::mma(av[i][q], b, acc[i][j]);
       }
     }
   };
@@ -164,7 +252,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_rows(const int32_t* __restric
   // One stage: wait for everything issued (stage st, issued a full stage
   // earlier), barrier (every wave's weight copies have landed and the other
   // buffer is free), issue stage st+1, fetch indices for the tap after, compute.
-  auto step = [&](int st, const uint4 (&aC)[FM][2], uint4 (&aN)[FM][2], const unsigned char* bC,
+  auto step = [&](int st, const uint4 (&aC)[FM][2][AV], uint4 (&aN)[FM][2][AV], const unsigned char* bC,
                   unsigned char* bN) {
     __builtin_amdgcn_s_waitcnt(0);
     asm volatile("s_barrier" ::: "memory");
@@ -179,7 +267,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_rows(const int32_t* __restric
     compute(aC, bC);
   };
 
-  uint4 a0[FM][2], a1[FM][2];
+  uint4 a0[FM][2][AV], a1[FM][2][AV];
   if (nstages > 0) {
     fetch_idx(0, srcL);
     issue(0, a0, bbuf0);
@@ -189,15 +277,28 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_rows(const int32_t* __restric
     step(st, a0, a1, bbuf0, bbuf1);
     if (st + 1 < nstages) step(st + 1, a1, a0, bbuf1, bbuf0);
   }
+
+  // Epilogue, fused into the same pass as the pages fuse theirs (bias,
+  // activation, residual add and the output rounding -- "Porting TRELLIS.2
+  // ...", section V): v = act(acc + bias) in fp32, staged per 16-row block in
+  // this wave's LDS region; then each lane adds the residual to 16 bytes' worth
+  // of one output row and rounds once, to the output type.
+  float bv[FN];
+#pragma unroll
+  for (int j = 0; j < FN; ++j) {
+    const int c = n0 + j * 16 + lr;
+    bv[j] = (p.bias != nullptr && c < c_out) ? p.bias[c] : 0.f;
+  }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  // Epilogue, one 16-row block per pass: round to bf16 (nearest-even), stage
-  // the block in this wave's LDS region (16-byte chunk c of row r at c ^ (r&OSW)),
-  // then store 16-byte pieces of each row at its caller index.
-  constexpr int OPR = TN / 8;
-  constexpr int OSW = (OPR < 8 ? OPR : 8) - 1;
-  uint16_t* sO = reinterpret_cast<uint16_t*>(bbuf0) + wave * 16 * TN;
+  // Staged row r holds TN floats in 16-byte pieces; piece q sits at q ^ osw(r),
+  // which spreads the four rows one write instruction touches over the banks
+  // and keeps each aligned group of four pieces contiguous.
+  constexpr int PPR = TN / 4;
+  auto spos = [](int r, int q) { return r * TN + ((q ^ ((((r >> 2) & 3) << 2) & (PPR - 1))) << 2); };
+  float* sO = reinterpret_cast<float*>(bbuf0) + wave * 16 * TN;
+  const int act = p.act;
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
 #pragma unroll
@@ -205,33 +306,88 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_rows(const int32_t* __restric
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = kg * 4 + e, c = j * 16 + lr;
-        sO[r * TN + (((c >> 3) ^ (r & OSW)) << 3) + (c & 7)] = f32_to_bf16_rne(acc[i][j][e]);
+        sO[spos(r, c >> 2) + (c & 3)] = activate(acc[i][j][e] + bv[j], act);
       }
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's staging writes are done
+    if (!p.y_f32) {
+      constexpr int OPR = TN / 8;
 #pragma unroll
-    for (int q = lane; q < 16 * OPR; q += 64) {
-      const int r = q / OPR, cc = q % OPR;
-      const int32_t row = __shfl(crow[i], r, 64);
-      const int co = n0 + cc * 8;
-      if (row >= 0 && co < c_out)
-        *reinterpret_cast<uint4*>(y + int64_t(row) * c_out + co) =
-            *reinterpret_cast<const uint4*>(sO + r * TN + ((cc ^ (r & OSW)) << 3));
+      for (int q = lane; q < 16 * OPR; q += 64) {
+        const int r = q / OPR, cc = q % OPR;
+        const int32_t row = __shfl(crow[i], r, 64);
+        const int co = n0 + cc * 8;
+        if (row >= 0 && co < c_out) {
+          const float4 lo = *reinterpret_cast<const float4*>(sO + spos(r, 2 * cc));
+          const float4 hi = *reinterpret_cast<const float4*>(sO + spos(r, 2 * cc + 1));
+          float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+          const int64_t off = int64_t(row) * c_out + co;
+          if (p.residual != nullptr) {
+            const uint4 rr = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.residual) + off);
+            const uint16_t* rh = reinterpret_cast<const uint16_t*>(&rr);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] += H::widen(rh[e]);
+          }
+          uint4 o;
+          uint16_t* oh = reinterpret_cast<uint16_t*>(&o);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) oh[e] = H::narrow(v[e]);
+          *reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.y) + off) = o;
+        }
+      }
+    } else {
+      constexpr int OPR = TN / 4;
+#pragma unroll
+      for (int q = lane; q < 16 * OPR; q += 64) {
+        const int r = q / OPR, cc = q % OPR;
+        const int32_t row = __shfl(crow[i], r, 64);
+        const int co = n0 + cc * 4;
+        if (row >= 0 && co < c_out) {
+          float4 v = *reinterpret_cast<const float4*>(sO + spos(r, cc));
+          const int64_t off = int64_t(row) * c_out + co;
+          if (p.residual != nullptr) {
+            const float4 rr = *reinterpret_cast<const float4*>(static_cast<const float*>(p.residual) + off);
+            v.x += rr.x, v.y += rr.y, v.z += rr.z, v.w += rr.w;
+          }
+          *reinterpret_cast<float4*>(static_cast<float*>(p.y) + off) = v;
+        }
+      }
     }
     __builtin_amdgcn_s_waitcnt(0xC07F);  // reads done before the next block overwrites
   }
 }
 
-template <int FM, int FN>
+template <int FM, int FN, bool F16, int XT>
 hipError_t launch_rows(const ConvArgs& a, const uint16_t* wp, const uint16_t* zeros, hipStream_t st) {
   constexpr int TM = 64 * FM, TN = 16 * FN;
   const int64_t mt = (a.n + TM - 1) / TM;
   const int nt = (a.c_out + TN - 1) / TN;
   const int64_t grid = mt * nt;
   if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
-  fwd_rows<FM, FN><<<unsigned(grid), kThreads, 0, st>>>(
-      a.nbr, a.srows, a.mask, a.n, static_cast<const uint16_t*>(a.x), wp, zeros,
-      static_cast<uint16_t*>(a.y), a.c_in, a.c_out, nt);
+  RowsArgs p{a.nbr, a.srows, a.mask, a.n, a.x, wp, zeros, a.y, a.epi.bias, a.epi.residual,
+             a.epi.act, a.y_dtype == TR_SC_F32 ? 1 : 0, a.c_in, a.c_out, nt};
+  fwd_rows<FM, FN, F16, XT><<<unsigned(grid), kThreads, 0, st>>>(p);
   return hipGetLastError();
+}
+
+template <bool F16>
+hipError_t dispatch(const ConvArgs& a, const uint16_t* p, const uint16_t* zeros, hipStream_t st) {
+  constexpr int XT = F16 ? 2 : 3;
+  if (a.x_dtype == TR_SC_F32) {
+    // fp32 features: XT products per multiply; 32-row waves keep the split
+    // terms and the wider A fragments within the register budget.
+    if (a.c_out >= 128) return launch_rows<2, 8, F16, XT>(a, p, zeros, st);
+    if (a.c_out > 32) return launch_rows<2, 4, F16, XT>(a, p, zeros, st);
+    if (a.c_out > 16) return launch_rows<2, 2, F16, XT>(a, p, zeros, st);
+    return launch_rows<2, 1, F16, XT>(a, p, zeros, st);
+  }
+  // Wide layers: 64-row waves halve the LDS reads of weight fragments per
+  // multiply (the weight slice is read once per wave). Narrow layers: 32-row
+  // waves give twice the workgroups and a third wave per SIMD.
+  if (a.c_out >= 128 && a.c_in >= 256) return launch_rows<4, 8, F16, 1>(a, p, zeros, st);
+  if (a.c_out >= 128) return launch_rows<2, 8, F16, 1>(a, p, zeros, st);
+  if (a.c_out > 32) return launch_rows<2, 4, F16, 1>(a, p, zeros, st);
+  if (a.c_out > 16) return launch_rows<4, 2, F16, 1>(a, p, zeros, st);
+  return launch_rows<4, 1, F16, 1>(a, p, zeros, st);
 }
 
 }  // namespace
@@ -244,17 +400,11 @@ hipError_t launch_pack_weights(const void* w, void* wp, int c_in, int c_out, hip
   return hipGetLastError();
 }
 
-hipError_t launch_forward_mfma_bf16(const ConvArgs& a, const void* wp, hipStream_t st) {
+hipError_t launch_forward_mfma(const ConvArgs& a, const void* wp, hipStream_t st) {
   const uint16_t* p = static_cast<const uint16_t*>(wp);
   const uint16_t* zeros = p + packed_weight_elems(a.c_in, a.c_out);
-  // Wide layers: 64-row waves halve the LDS reads of weight fragments per
-  // multiply (the weight slice is read once per wave). Narrow layers: 32-row
-  // waves give twice the workgroups and a third wave per SIMD.
-  if (a.c_out >= 128 && a.c_in >= 256) return launch_rows<4, 8>(a, p, zeros, st);
-  if (a.c_out >= 128) return launch_rows<2, 8>(a, p, zeros, st);
-  if (a.c_out > 32) return launch_rows<2, 4>(a, p, zeros, st);
-  if (a.c_out > 16) return launch_rows<4, 2>(a, p, zeros, st);
-  return launch_rows<4, 1>(a, p, zeros, st);
+  if (a.w_dtype == TR_SC_F16) return dispatch<true>(a, p, zeros, st);
+  return dispatch<false>(a, p, zeros, st);
 }
 
 }  // namespace trsc

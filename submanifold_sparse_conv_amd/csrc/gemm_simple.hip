@@ -1,6 +1,5 @@
-// Direct (one output element per lane) form of the gather-GEMM. It is the fp32
-// path of the library and the bf16 path for channel counts the matrix-core
-// kernel does not tile. y[i, co] = sum over taps k with nbr[i][k] = j >= 0 and
+// Direct (one output element per lane) form of the gather-GEMM: the fp32 path
+// of the library. y[i, co] = sum over taps k with nbr[i][k] = j >= 0 and
 // over ci of w[k, ci, co] * x[j, ci] ("Running TRELLIS.2 on a Mac (1/3)",
 // sparse 3D convolution paragraph), fp32 fused multiply-adds in (k, ci) order.
 #include "common.h"
@@ -11,11 +10,19 @@ namespace {
 
 constexpr int kThreads = 256;
 
-template <bool kBf16>
+__device__ __forceinline__ float activate(float v, int act) {
+  if (act == kActRelu) return v < 0.f ? 0.f : v;
+  if (act == kActSilu) return v / (1.f + expf(-v));
+  return v;
+}
+
+// fp32 x, w, y; the fused epilogue of the matrix-core path, in fp32:
+// y = act(sum + bias) + residual.
 __global__ __launch_bounds__(kThreads) void fwd_simple(const int32_t* __restrict__ nbr, int64_t n,
-                                                       const void* __restrict__ xv,
-                                                       const void* __restrict__ wv,
-                                                       void* __restrict__ yv, int c_in, int c_out) {
+                                                       const float* __restrict__ x,
+                                                       const float* __restrict__ w, float* y, int c_in,
+                                                       int c_out, const float* __restrict__ bias,
+                                                       const float* residual, int act) {
   const int64_t e = int64_t(blockIdx.x) * kThreads + threadIdx.x;
   if (e >= n * c_out) return;
   const int64_t row = e / c_out;
@@ -26,22 +33,11 @@ __global__ __launch_bounds__(kThreads) void fwd_simple(const int32_t* __restrict
     if (j < 0) continue;
     const int64_t xo = int64_t(j) * c_in;
     const int64_t wo = int64_t(k) * c_in * c_out + co;
-    for (int ci = 0; ci < c_in; ++ci) {
-      float a, b;
-      if constexpr (kBf16) {
-        a = bf16_to_f32(static_cast<const uint16_t*>(xv)[xo + ci]);
-        b = bf16_to_f32(static_cast<const uint16_t*>(wv)[wo + int64_t(ci) * c_out]);
-      } else {
-        a = static_cast<const float*>(xv)[xo + ci];
-        b = static_cast<const float*>(wv)[wo + int64_t(ci) * c_out];
-      }
-      acc = fmaf(a, b, acc);
-    }
+    for (int ci = 0; ci < c_in; ++ci) acc = fmaf(x[xo + ci], w[wo + int64_t(ci) * c_out], acc);
   }
-  if constexpr (kBf16)
-    static_cast<uint16_t*>(yv)[e] = f32_to_bf16_rne(acc);
-  else
-    static_cast<float*>(yv)[e] = acc;
+  float v = activate(acc + (bias != nullptr ? bias[co] : 0.f), act);
+  if (residual != nullptr) v += residual[e];
+  y[e] = v;
 }
 
 }  // namespace
@@ -49,16 +45,10 @@ __global__ __launch_bounds__(kThreads) void fwd_simple(const int32_t* __restrict
 hipError_t launch_forward_simple_f32(const ConvArgs& a, hipStream_t st) {
   const int64_t total = a.n * a.c_out;
   if (total > 0)
-    fwd_simple<false><<<unsigned((total + kThreads - 1) / kThreads), kThreads, 0, st>>>(
-        a.nbr, a.n, a.x, a.w, a.y, a.c_in, a.c_out);
-  return hipGetLastError();
-}
-
-hipError_t launch_forward_simple_bf16(const ConvArgs& a, hipStream_t st) {
-  const int64_t total = a.n * a.c_out;
-  if (total > 0)
-    fwd_simple<true><<<unsigned((total + kThreads - 1) / kThreads), kThreads, 0, st>>>(
-        a.nbr, a.n, a.x, a.w, a.y, a.c_in, a.c_out);
+    fwd_simple<<<unsigned((total + kThreads - 1) / kThreads), kThreads, 0, st>>>(
+        a.nbr, a.n, static_cast<const float*>(a.x), static_cast<const float*>(a.w),
+        static_cast<float*>(a.y), a.c_in, a.c_out, a.epi.bias, static_cast<const float*>(a.epi.residual),
+        a.epi.act);
   return hipGetLastError();
 }
 

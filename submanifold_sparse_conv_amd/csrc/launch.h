@@ -5,6 +5,7 @@
 #include <cstdint>
 
 #include "common.h"
+#include "tr_sparseconv.h"
 
 namespace trsc {
 
@@ -38,6 +39,12 @@ hipError_t launch_kmap(const uint64_t* skeys, int64_t n, const TableRef& t, int3
 
 // Forward kernels. `srows` is the row order of the tiles (position -> caller
 // row), `mask` the 27-bit neighbour mask of the voxel at each position.
+constexpr int kActNone = TR_SC_ACT_NONE, kActRelu = TR_SC_ACT_RELU, kActSilu = TR_SC_ACT_SILU;
+struct Epilogue {
+  const float* bias;     // [c_out] or null
+  const void* residual;  // [n, c_out] in the output type, or null
+  int act;               // kAct*
+};
 struct ConvArgs {
   const int32_t* nbr;   // [n, 27] caller order
   const int32_t* srows; // [n]
@@ -47,15 +54,16 @@ struct ConvArgs {
   const void* w;
   void* y;
   int c_in, c_out;
+  int x_dtype, w_dtype, y_dtype;  // TR_SC_*
+  Epilogue epi;
 };
 hipError_t launch_forward_simple_f32(const ConvArgs& a, hipStream_t st);
-hipError_t launch_forward_simple_bf16(const ConvArgs& a, hipStream_t st);
-// wp[k][co][ci] = w[k][ci][co] (bf16), the matrix-core operand layout,
+// wp[k][co][ci] = w[k][ci][co] (bf16 or fp16), the matrix-core operand layout,
 // followed by 256 zero bytes (packed_weight_elems elements, then the zeros).
 inline int64_t packed_weight_elems(int c_in, int c_out) {
   return (int64_t(27) * c_in * c_out + 127) / 128 * 128;  // keeps the zero block 256-byte aligned
 }
 hipError_t launch_pack_weights(const void* w, void* wp, int c_in, int c_out, hipStream_t st);
-hipError_t launch_forward_mfma_bf16(const ConvArgs& a, const void* wp, hipStream_t st);
+hipError_t launch_forward_mfma(const ConvArgs& a, const void* wp, hipStream_t st);
 
 }  // namespace trsc

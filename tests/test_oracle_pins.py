@@ -323,3 +323,39 @@ def test_rows_subset_matches_full():
     rows = np.random.default_rng(1).choice(wl.n, 500, replace=False)
     full = oracle.forward(nbr, wl.x, wl.w)
     np.testing.assert_array_equal(oracle.forward(nbr, wl.x, wl.w, rows=rows), full[rows])
+
+
+# --------------------------------------------------------------------------
+# fused epilogue: act(conv + bias) + residual
+# --------------------------------------------------------------------------
+def test_epilogue_values():
+    y = np.array([[-2.0, -0.5, 0.0, 0.5, 3.0]])
+    bias = np.array([1.0, 0.0, -1.0, 0.25, -3.0])
+    res = np.array([[10.0, 20.0, 30.0, 40.0, 50.0]])
+    np.testing.assert_array_equal(oracle.epilogue(y), y)
+    np.testing.assert_array_equal(oracle.epilogue(y, bias=bias), y + bias)
+    np.testing.assert_array_equal(oracle.epilogue(y, act="relu"), [[0.0, 0.0, 0.0, 0.5, 3.0]])
+    np.testing.assert_array_equal(oracle.epilogue(y, bias=bias, act="relu", residual=res),
+                                  [[10.0, 20.0, 30.0, 40.75, 50.0]])
+    # SiLU(v) = v * sigmoid(v): torch's silu in float64 is an independent routine
+    v = y + bias
+    ref = torch.nn.functional.silu(torch.from_numpy(v)).numpy() + res
+    np.testing.assert_allclose(oracle.epilogue(y, bias=bias, act="silu", residual=res), ref,
+                               rtol=1e-15, atol=1e-15)
+    assert oracle.epilogue(np.array([[0.0]]), act="silu")[0, 0] == 0.0
+
+
+def test_epilogue_resblock_matches_dense_torch():
+    # x + conv2(silu(conv1(x) + b1)) + ... on a tiny grid, against torch's dense conv3d
+    rng = np.random.default_rng(21)
+    D, c = 7, 4
+    coords = W.random_sparse(rng, 150, D=D)
+    x = rng.standard_normal((len(coords), c))
+    w1, w2 = rng.standard_normal((27, c, c)), rng.standard_normal((27, c, c))
+    b1 = rng.standard_normal(c)
+    nbr = oracle.kernel_map(coords)
+    h = oracle.epilogue(oracle.forward(nbr, x, w1), bias=b1, act="silu")
+    out = oracle.epilogue(oracle.forward(nbr, h, w2), residual=x)
+    h_ref = torch.nn.functional.silu(torch.from_numpy(torch_dense_conv(coords, x, w1, 1, D) + b1)).numpy()
+    out_ref = torch_dense_conv(coords, h_ref, w2, 1, D) + x
+    assert rel_err(out, out_ref) < 1e-12
