@@ -58,6 +58,10 @@ def _load():
         lib.oc_forward.restype = ctypes.c_int
         lib.oc_epilogue.argtypes = [P, I64, ctypes.c_int, P, P, ctypes.c_int]
         lib.oc_epilogue.restype = ctypes.c_int
+        lib.oc_backward_data.argtypes = [P, I64, P, I64, P, P, ctypes.c_int, ctypes.c_int, P]
+        lib.oc_backward_data.restype = ctypes.c_int
+        lib.oc_backward_weights.argtypes = [P, I64, P, P, ctypes.c_int, ctypes.c_int, P, I64, P]
+        lib.oc_backward_weights.restype = ctypes.c_int
         lib.oc_num_threads.argtypes = []
         lib.oc_num_threads.restype = ctypes.c_int
         _lib = lib
@@ -152,6 +156,40 @@ def forward(nbr: np.ndarray, x: np.ndarray, w: np.ndarray, rows=None) -> np.ndar
     if st != OK:
         raise OracleError(st, "forward")
     return y
+
+
+def backward_data(nbr: np.ndarray, dy: np.ndarray, w: np.ndarray, rows=None) -> np.ndarray:
+    """dx[rows] (fp64) of L = sum <y, dy> for y = forward(nbr, x, w)."""
+    nbr = np.ascontiguousarray(nbr, dtype=np.int32)
+    n = nbr.shape[0]
+    wd = widen(w)
+    c_in, c_out = wd.shape[1], wd.shape[2]
+    dyd = widen(dy).reshape(n, c_out)
+    r = None if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
+    m = n if r is None else len(r)
+    dx = np.empty((m, c_in), dtype=np.float64)
+    st = _load().oc_backward_data(_ptr(nbr), n, None if r is None else _ptr(r), 0 if r is None else len(r),
+                                  _ptr(dyd), _ptr(wd), c_in, c_out, _ptr(dx))
+    if st != OK:
+        raise OracleError(st, "backward_data")
+    return dx
+
+
+def backward_weights(nbr: np.ndarray, x: np.ndarray, dy: np.ndarray, sel=None) -> np.ndarray:
+    """dw (fp64): [27, c_in, c_out], or [len(sel), c_out] for sel = [(k, ci), ...]."""
+    nbr = np.ascontiguousarray(nbr, dtype=np.int32)
+    n = nbr.shape[0]
+    xd = widen(x).reshape(n, -1)
+    dyd = widen(dy).reshape(n, -1)
+    c_in, c_out = xd.shape[1], dyd.shape[1]
+    s = None if sel is None else np.ascontiguousarray(sel, dtype=np.int32).reshape(-1, 2)
+    m = 27 * c_in if s is None else len(s)
+    dw = np.empty((m, c_out), dtype=np.float64)
+    st = _load().oc_backward_weights(_ptr(nbr), n, _ptr(xd), _ptr(dyd), c_in, c_out,
+                                     None if s is None else _ptr(s), 0 if s is None else len(s), _ptr(dw))
+    if st != OK:
+        raise OracleError(st, "backward_weights")
+    return dw.reshape(27, c_in, c_out) if s is None else dw
 
 
 ACTS = {"none": 0, "relu": 1, "silu": 2}

@@ -184,10 +184,10 @@ int oc_forward(const int32_t* nbr, int64_t n, const int64_t* rows, int64_t nrows
   return kOk;
 }
 
-// The fused epilogue of the gather-GEMM: the pages fuse "bias, rounding,
-// activation and the residual add" into the convolution pass ("Porting
-// TRELLIS.2 ...", section V). Reading: out = act(y + bias) + residual, rounded
-// once at the end (here: never, fp64). act: 0 none, 1 ReLU max(v, 0),
+// The fused epilogue of the gather-GEMM: the pages fuse the bias, the
+// activation, the residual add and the output rounding into the convolution
+// pass ("Porting TRELLIS.2 ...", section V). Reading: out = act(y + bias) +
+// residual, rounded once at the end (here: never, fp64). act: 0 none, 1 ReLU max(v, 0),
 // 2 SiLU v / (1 + exp(-v)). bias is [c_out] or NULL; residual is [m, c_out]
 // (the rows of y, in the same order) or NULL. Applied in place on y [m, c_out].
 int oc_epilogue(double* y, int64_t m, int c_out, const double* bias, const double* residual, int act) {
@@ -202,6 +202,88 @@ int oc_epilogue(double* y, int64_t m, int c_out, const double* bias, const doubl
       if (act == 2) v = v / (1.0 + std::exp(-v));
       if (residual) v += residual[i * c_out + co];
       y[i * c_out + co] = v;
+    }
+  }
+  return kOk;
+}
+
+// Backward of the convolution (the gradients of L = sum_i <y[i], dy[i]>),
+// written from the forward sum above: every term w[k, ci, co] * x[j, ci] with
+// j = nbr[i][k] >= 0 contributes
+//   dx[j, ci]     += w[k, ci, co] * dy[i, co]     (data gradient)
+//   dw[k, ci, co] += x[j, ci]     * dy[i, co]     (weight gradient).
+//
+// Data gradient, for the output rows `rows` (all rows if NULL): the terms that
+// land on row j are found by a full scan of nbr for entries equal to j (the
+// inverse of the map, built here from nbr alone), then summed in (i, k, co)
+// order in fp64.
+int oc_backward_data(const int32_t* nbr, int64_t n, const int64_t* rows, int64_t nrows,
+                     const double* dy, const double* w, int c_in, int c_out, double* dx) {
+  if (n < 0 || c_in <= 0 || c_out <= 0) return kErrInvalid;
+  const int64_t m = rows ? nrows : n;
+  if (m < 0) return kErrInvalid;
+  if (m > 0 && (nbr == nullptr || dy == nullptr || w == nullptr || dx == nullptr)) return kErrInvalid;
+  for (int64_t q = 0; q < (rows ? nrows : 0); ++q)
+    if (rows[q] < 0 || rows[q] >= n) return kErrInvalid;
+  // inverse map in CSR form: for each j, the (i, k) with nbr[i][k] == j, by i then k
+  std::vector<int64_t> start(size_t(n) + 1, 0);
+  for (int64_t e = 0; e < n * 27; ++e) {
+    const int32_t j = nbr[e];
+    if (j < -1 || j >= n) return kErrInvalid;
+    if (j >= 0) ++start[size_t(j) + 1];
+  }
+  for (int64_t j = 0; j < n; ++j) start[size_t(j) + 1] += start[size_t(j)];
+  std::vector<int64_t> fill(start.begin(), start.end() - 1);
+  std::vector<int64_t> src(size_t(start[size_t(n)]));
+  for (int64_t e = 0; e < n * 27; ++e)
+    if (nbr[e] >= 0) src[size_t(fill[size_t(nbr[e])]++)] = e;  // e = i * 27 + k
+#pragma omp parallel
+  {
+    std::vector<double> acc(static_cast<size_t>(c_in));
+#pragma omp for schedule(dynamic, 64)
+    for (int64_t q = 0; q < m; ++q) {
+      const int64_t j = rows ? rows[q] : q;
+      std::fill(acc.begin(), acc.end(), 0.0);
+      for (int64_t t = start[size_t(j)]; t < start[size_t(j) + 1]; ++t) {
+        const int64_t i = src[size_t(t)] / 27;
+        const int k = int(src[size_t(t)] % 27);
+        const double* g = dy + i * c_out;
+        const double* wk = w + int64_t(k) * c_in * c_out;
+        for (int ci = 0; ci < c_in; ++ci) {
+          double sacc = 0.0;
+          for (int co = 0; co < c_out; ++co) sacc += wk[int64_t(ci) * c_out + co] * g[co];
+          acc[size_t(ci)] += sacc;
+        }
+      }
+      std::memcpy(dx + q * c_in, acc.data(), sizeof(double) * size_t(c_in));
+    }
+  }
+  return kOk;
+}
+
+// Weight gradient, for the (tap, input channel) entries listed in sel (pairs
+// k, ci; all 27 * c_in in (k, ci) order if NULL): dw_sel[s, co] = sum over i
+// with nbr[i][k] = j >= 0, in order of i, of x[j, ci] * dy[i, co], in fp64.
+int oc_backward_weights(const int32_t* nbr, int64_t n, const double* x, const double* dy, int c_in,
+                        int c_out, const int32_t* sel, int64_t nsel, double* dw) {
+  if (n < 0 || c_in <= 0 || c_out <= 0) return kErrInvalid;
+  const int64_t m = sel ? nsel : int64_t(27) * c_in;
+  if (m < 0 || (m > 0 && dw == nullptr) || (n > 0 && (nbr == nullptr || x == nullptr || dy == nullptr)))
+    return kErrInvalid;
+  for (int64_t s = 0; s < (sel ? nsel : 0); ++s)
+    if (sel[2 * s] < 0 || sel[2 * s] > 26 || sel[2 * s + 1] < 0 || sel[2 * s + 1] >= c_in) return kErrInvalid;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t s = 0; s < m; ++s) {
+    const int k = sel ? sel[2 * s] : int(s / c_in);
+    const int ci = sel ? sel[2 * s + 1] : int(s % c_in);
+    double* out = dw + s * c_out;
+    std::fill(out, out + c_out, 0.0);
+    for (int64_t i = 0; i < n; ++i) {
+      const int32_t j = nbr[i * 27 + k];
+      if (j < 0) continue;
+      const double xv = x[int64_t(j) * c_in + ci];
+      const double* g = dy + i * c_out;
+      for (int co = 0; co < c_out; ++co) out[co] += xv * g[co];
     }
   }
   return kOk;

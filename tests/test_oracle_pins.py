@@ -359,3 +359,67 @@ def test_epilogue_resblock_matches_dense_torch():
     h_ref = torch.nn.functional.silu(torch.from_numpy(torch_dense_conv(coords, x, w1, 1, D) + b1)).numpy()
     out_ref = torch_dense_conv(coords, h_ref, w2, 1, D) + x
     assert rel_err(out, out_ref) < 1e-12
+
+
+# --------------------------------------------------------------------------
+# backward: data and weight gradients of L = sum_i <y[i], dy[i]>
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("seed", [0, 1])
+def test_backward_vs_dense_autograd(seed):
+    # torch autograd through a dense float64 conv3d, read at the active sites
+    rng = np.random.default_rng(300 + seed)
+    D, B, ci, co = 8, 2, 3, 4
+    coords = W.random_sparse(rng, 250, D=D, B=B)
+    coords = coords[rng.permutation(len(coords))]
+    x = rng.standard_normal((len(coords), ci))
+    w = rng.standard_normal((27, ci, co))
+    dy = rng.standard_normal((len(coords), co))
+    c = torch.from_numpy(coords.astype(np.int64))
+    dense = torch.from_numpy(dense_inputs(coords, x, B, D)).requires_grad_(True)
+    wt = torch.from_numpy(np.ascontiguousarray(w.reshape(3, 3, 3, ci, co).transpose(4, 3, 0, 1, 2)))
+    wt.requires_grad_(True)
+    out = torch.nn.functional.conv3d(dense, wt, padding=1)
+    y = out[c[:, 0], :, c[:, 1], c[:, 2], c[:, 3]]
+    (y * torch.from_numpy(dy)).sum().backward()
+    dx_ref = dense.grad[c[:, 0], :, c[:, 1], c[:, 2], c[:, 3]].numpy()
+    dw_ref = wt.grad.numpy().transpose(2, 3, 4, 1, 0).reshape(27, ci, co)
+    nbr = oracle.kernel_map(coords)
+    assert rel_err(oracle.backward_data(nbr, dy, w), dx_ref) < 1e-12
+    assert rel_err(oracle.backward_weights(nbr, x, dy), dw_ref) < 1e-12
+
+
+def test_backward_adjoint_identities():
+    # <conv(x), dy> = <x, dx(dy)> = <w, dw(x, dy)>: the three are the same sum
+    wl = W.make("T", seed_offset=50, order="shuffled")
+    rng = np.random.default_rng(5)
+    dy = rng.standard_normal((wl.n, wl.c_out))
+    nbr = oracle.kernel_map(wl.coords)
+    a = float((oracle.forward(nbr, wl.x, wl.w) * dy).sum())
+    b = float((wl.x.astype(np.float64) * oracle.backward_data(nbr, dy, wl.w)).sum())
+    c = float((wl.w.astype(np.float64) * oracle.backward_weights(nbr, wl.x, dy)).sum())
+    assert abs(a - b) <= 1e-10 * abs(a) and abs(a - c) <= 1e-10 * abs(a)
+
+
+def test_backward_subsets_and_single_tap():
+    rng = np.random.default_rng(9)
+    coords = W.random_sparse(rng, 400, D=10, B=1)
+    x = rng.standard_normal((len(coords), 4))
+    dy = rng.standard_normal((len(coords), 6))
+    w = rng.standard_normal((27, 4, 6))
+    nbr = oracle.kernel_map(coords)
+    full = oracle.backward_data(nbr, dy, w)
+    rows = np.array([5, 0, len(coords) - 1, 17])
+    np.testing.assert_array_equal(oracle.backward_data(nbr, dy, w, rows=rows), full[rows])
+    dw = oracle.backward_weights(nbr, x, dy)
+    sel = np.array([[0, 0], [13, 3], [26, 1], [4, 2]])
+    np.testing.assert_array_equal(oracle.backward_weights(nbr, x, dy, sel=sel), dw[sel[:, 0], sel[:, 1]])
+    # centre tap: every voxel is its own neighbour, so dw[13] = x^T dy exactly up to rounding
+    assert rel_err(dw[13], x.T @ dy) < 1e-12
+    # a single non-zero tap k: dx[j] = w[k] dy[i] for the i whose tap k reads j
+    k = 5
+    wk = np.zeros_like(w)
+    wk[k] = w[k]
+    ii = np.nonzero(nbr[:, k] >= 0)[0]
+    exp = np.zeros((len(coords), 4))
+    exp[nbr[ii, k]] = dy[ii] @ w[k].T
+    assert rel_err(oracle.backward_data(nbr, dy, wk), exp) < 1e-12
