@@ -44,6 +44,8 @@ def parse():
     p.add_argument("--config", default="L", choices=list(WORKLOAD_NAMES))
     p.add_argument("--also", default="S", help="extra configs measured forward-only, comma list ('' = none)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-variants", action="store_true",
+                   help="skip the fused-epilogue / fp16 / mixed-precision / backward timings")
     p.add_argument("--cpu-seconds", type=float, default=8.0, help="target wall time of the oracle forward sample")
     p.add_argument("--gemm-reps", type=int, default=50)
     p.add_argument("--copy-probe-mib", type=int, default=0,
@@ -125,6 +127,55 @@ def measure_forward_only(sc, torch, path, reps):
     e.record()
     torch.cuda.synchronize()
     return s.elapsed_time(e) / reps
+
+
+def time_reps(torch, fn, reps):
+    """Mean ms of `fn` launched back to back between two events."""
+    for _ in range(3):
+        fn()
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(reps):
+        fn()
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / reps
+
+
+def variants(sc, torch, wl, path, M, reps):
+    """The other precision paths, the fused epilogue and the backward, on the
+    same kernel map: steady-state ms and effective TFLOP/s (2 C_in C_out M
+    useful flops per call)."""
+    n, ci, co = wl.n, wl.c_in, wl.c_out
+    flops = 2.0 * ci * co * M
+    g = torch.Generator(device="cuda").manual_seed(7)
+    bias = torch.randn(co, device="cuda", generator=g) * 0.5
+    res = torch.randn((n, co), device="cuda", generator=g).bfloat16()
+    dy = torch.randn((n, co), device="cuda", generator=g).bfloat16()
+    x16, w16 = path.x.half(), path.w.half()
+    wp16 = sc.pack_weights(w16)
+    xf = torch.randn((n, ci), device="cuda", generator=g)
+    wpd = sc.pack_weights_dgrad(path.w)
+    y_f32 = torch.empty((n, co), device="cuda")
+    dx = torch.empty((n, ci), device="cuda", dtype=torch.bfloat16)
+    dw = torch.empty((27, ci, co), device="cuda")
+    y16 = torch.empty((n, co), device="cuda", dtype=torch.float16)
+    wsw = sc.Workspace(sc._lib.lib().tr_sparseconv_backward_weights_workspace_bytes(n, ci, co, sc._lib.BF16),
+                       "cuda")
+    cases = {
+        "forward_bf16_bias_silu_residual": lambda: sc.forward_fused(path.m, path.x, path.wp, bias=bias, act="silu",
+                                                                    residual=res, out=path.y),
+        "forward_f16": lambda: sc.forward_packed(path.m, x16, wp16, out=y16),
+        "forward_f32x_bf16w_f32y": lambda: sc.forward_fused(path.m, xf, path.wp, out=y_f32),
+        "backward_data_bf16": lambda: sc.backward_data(path.m, dy, wpd, out=dx),
+        "backward_weights_bf16": lambda: sc.backward_weights(path.m, path.x, dy, out=dw, workspace=wsw),
+    }
+    out = {}
+    for name, fn in cases.items():
+        ms = time_reps(torch, fn, reps)
+        out[name] = {"ms": ms, "effective_tflops": flops / (ms * 1e-3) / 1e12}
+    return out
 
 
 def cpu_baseline(wl, target_s):
@@ -280,6 +331,8 @@ def main():
         del p2, c2, x2, w2
     if extra:
         out["also"] = extra
+    if not args.no_variants and wl.dtype == "bf16":
+        out["variants"] = variants(sc, torch, wl, path, M, max(5, args.gemm_reps // 2))
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     print(json.dumps(out), flush=True)

@@ -209,6 +209,41 @@ int tr_sparseconv_forward_fused(const tr_sc_kmap* m, const void* x, int x_dtype,
                                 int w_dtype, const float* bias, int act, const void* residual,
                                 void* y, int y_dtype, int c_in, int c_out, void* stream);
 
+/* ------------------------------------------------------------------------
+ * Backward: the gradients of L = sum_i <y[i], dy[i]> for y = the convolution
+ * of x with w. From the forward sum above, each term w[k, ci, co] * x[j, ci]
+ * with j = nbr[i][k] contributes w[k, ci, co] * dy[i, co] to dx[j, ci] and
+ * x[j, ci] * dy[i, co] to dw[k, ci, co].
+ * ------------------------------------------------------------------------ */
+
+/* Data gradient. Voxel i reads j at tap k exactly when j reads i at tap 26 - k,
+ * so dx is the forward gather-GEMM over the same kernel map with input dy and
+ * mirrored, transposed weights.
+ * tr_sparseconv_pack_weights_dgrad: w [27, c_in, c_out] (dtype) -> wp, of
+ *   >= tr_sparseconv_packed_weights_bytes(c_in, c_out, dtype) bytes, 16-byte
+ *   aligned, caller-owned.
+ * tr_sparseconv_backward_data: dy [n, c_out] (dy_dtype), wp from
+ *   tr_sparseconv_pack_weights_dgrad (w_dtype), dx [n, c_in] (dx_dtype; every
+ *   element written). Type rules, alignment and errors as
+ *   tr_sparseconv_forward_fused with (x, y) = (dy, dx). */
+int tr_sparseconv_pack_weights_dgrad(const void* w, int c_in, int c_out, int dtype, void* wp,
+                                     size_t wp_bytes, void* stream);
+int tr_sparseconv_backward_data(const tr_sc_kmap* m, const void* dy, int dy_dtype, const void* wp,
+                                int w_dtype, void* dx, int dx_dtype, int c_in, int c_out,
+                                void* stream);
+
+/* Weight gradient dw [27, c_in, c_out], fp32, every element written.
+ * x [n, c_in] and dy [n, c_out] share dtype (bf16, f16 with c_in, c_out
+ * multiples of 8 and 16-byte aligned pointers; or f32). The half-precision
+ * path sums over voxel pairs on the matrix cores in fp32, split over ranges of
+ * voxels whose partial sums are added in a fixed order (no atomics: the same
+ * bits on every call). workspace: >= tr_sparseconv_backward_weights_workspace_bytes
+ * bytes, 256-byte aligned (0 bytes for f32). */
+size_t tr_sparseconv_backward_weights_workspace_bytes(int64_t n, int c_in, int c_out, int dtype);
+int tr_sparseconv_backward_weights(const tr_sc_kmap* m, const void* x, const void* dy, float* dw,
+                                   int c_in, int c_out, int dtype, void* workspace,
+                                   size_t ws_bytes, void* stream);
+
 /* Message of the last failed call on this thread ("" if none). */
 const char* tr_sparseconv_last_error(void);
 

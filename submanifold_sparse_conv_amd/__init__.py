@@ -18,6 +18,7 @@ from . import _lib
 from ._lib import TrSparseConvError, check  # noqa: F401
 
 __all__ = ["build_hash", "build_kernel_map", "forward", "pack_weights", "forward_packed", "forward_fused",
+           "pack_weights_dgrad", "backward_data", "backward_weights",
            "status", "hash_lookup", "hash_sorted_rows", "HashTable", "KernelMap", "PackedWeights",
            "TrSparseConvError", "version", "forward_workspace_bytes", "Workspace"]
 
@@ -173,26 +174,33 @@ def build_kernel_map(h: HashTable, nbr: torch.Tensor | None = None,
 
 
 class PackedWeights:
-    """Weights re-laid out for the gather-GEMM (tr_sparseconv_pack_weights)."""
+    """Weights re-laid out for the gather-GEMM (tr_sparseconv_pack_weights), or,
+    with dgrad=True, for the data gradient (tr_sparseconv_pack_weights_dgrad)."""
 
-    def __init__(self, w: torch.Tensor):
+    def __init__(self, w: torch.Tensor, dgrad: bool = False):
         if w.dtype not in _DTYPES:
             raise ValueError(f"unsupported dtype {w.dtype}")
         _require(w, "w", w.dtype, 3)
         if w.shape[0] != 27:
             raise ValueError(f"w must be [27, C_in, C_out], got {tuple(w.shape)}")
         self.dtype = w.dtype
+        self.dgrad = dgrad
         self.c_in, self.c_out = int(w.shape[1]), int(w.shape[2])
         dt = _DTYPES[w.dtype]
         L = _lib.lib()
         self._ws = Workspace(L.tr_sparseconv_packed_weights_bytes(self.c_in, self.c_out, dt), w.device)
+        fn = L.tr_sparseconv_pack_weights_dgrad if dgrad else L.tr_sparseconv_pack_weights
         with torch.cuda.device(w.device):
-            check(L.tr_sparseconv_pack_weights(_ptr(w), self.c_in, self.c_out, dt, self._ws.ptr,
-                                               self._ws.nbytes, _stream(w.device)))
+            check(fn(_ptr(w), self.c_in, self.c_out, dt, self._ws.ptr, self._ws.nbytes, _stream(w.device)))
 
 
 def pack_weights(w: torch.Tensor) -> PackedWeights:
     return PackedWeights(w)
+
+
+def pack_weights_dgrad(w: torch.Tensor) -> PackedWeights:
+    """w [27, C_in, C_out] packed for backward_data (taps mirrored)."""
+    return PackedWeights(w, dgrad=True)
 
 
 def _check_x(m, x, c_in, dtype):
@@ -259,6 +267,55 @@ def forward_fused(m: KernelMap, x: torch.Tensor, wp: PackedWeights, bias: torch.
         check(_lib.lib().tr_sparseconv_forward_fused(
             m.handle, _ptr(x), _DTYPES[x.dtype], wp._ws.ptr, _DTYPES[wp.dtype], _ptr(bias), _ACTS[act],
             _ptr(residual), _ptr(out), _DTYPES[out_dtype], wp.c_in, wp.c_out, _stream(x.device)))
+    return out
+
+
+def backward_data(m: KernelMap, dy: torch.Tensor, wpd: PackedWeights, out_dtype: torch.dtype | None = None,
+                  out: torch.Tensor | None = None) -> torch.Tensor:
+    """dx [N, C_in] of L = sum <y, dy> (tr_sparseconv_backward_data); wpd from pack_weights_dgrad."""
+    if not wpd.dgrad:
+        raise ValueError("backward_data needs weights from pack_weights_dgrad")
+    if dy.dtype not in _DTYPES:
+        raise ValueError(f"unsupported dtype {dy.dtype}")
+    _require(dy, "dy", dy.dtype, 2)
+    if tuple(dy.shape) != (m.n, wpd.c_out):
+        raise ValueError(f"dy must be [{m.n}, {wpd.c_out}], got {tuple(dy.shape)}")
+    out_dtype = out_dtype or (out.dtype if out is not None else dy.dtype)
+    if out_dtype not in _DTYPES:
+        raise ValueError(f"unsupported output dtype {out_dtype}")
+    if out is None:
+        out = torch.empty((m.n, wpd.c_in), dtype=out_dtype, device=dy.device)
+    _require(out, "out", out_dtype, 2)
+    if tuple(out.shape) != (m.n, wpd.c_in):
+        raise ValueError(f"out must be [{m.n}, {wpd.c_in}]")
+    with torch.cuda.device(dy.device):
+        check(_lib.lib().tr_sparseconv_backward_data(
+            m.handle, _ptr(dy), _DTYPES[dy.dtype], wpd._ws.ptr, _DTYPES[wpd.dtype], _ptr(out), _DTYPES[out_dtype],
+            wpd.c_in, wpd.c_out, _stream(dy.device)))
+    return out
+
+
+def backward_weights(m: KernelMap, x: torch.Tensor, dy: torch.Tensor, out: torch.Tensor | None = None,
+                     workspace: Workspace | None = None) -> torch.Tensor:
+    """dw [27, C_in, C_out] (fp32) of L = sum <y, dy> (tr_sparseconv_backward_weights)."""
+    if x.dtype not in _DTYPES or dy.dtype != x.dtype:
+        raise ValueError(f"x and dy must share a supported dtype, got {x.dtype}, {dy.dtype}")
+    _require(x, "x", x.dtype, 2)
+    _require(dy, "dy", x.dtype, 2)
+    if int(x.shape[0]) != m.n or int(dy.shape[0]) != m.n:
+        raise ValueError(f"x and dy must have {m.n} rows")
+    c_in, c_out = int(x.shape[1]), int(dy.shape[1])
+    if out is None:
+        out = torch.empty((27, c_in, c_out), dtype=torch.float32, device=x.device)
+    _require(out, "out", torch.float32, 3)
+    if tuple(out.shape) != (27, c_in, c_out):
+        raise ValueError(f"out must be [27, {c_in}, {c_out}]")
+    dt = _DTYPES[x.dtype]
+    L = _lib.lib()
+    ws = _workspace(L.tr_sparseconv_backward_weights_workspace_bytes(m.n, c_in, c_out, dt), x.device, workspace)
+    with torch.cuda.device(x.device):
+        check(L.tr_sparseconv_backward_weights(m.handle, _ptr(x), _ptr(dy), _ptr(out), c_in, c_out, dt, ws.ptr,
+                                               ws.nbytes, _stream(x.device)))
     return out
 
 

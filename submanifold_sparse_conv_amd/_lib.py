@@ -58,6 +58,10 @@ SIGNATURES = [
     ("tr_sparseconv_pack_weights", _I, [_P, _I, _I, _I, _P, _SZ, _P]),
     ("tr_sparseconv_forward_packed", _I, [_P, _P, _P, _P, _I, _I, _I, _P]),
     ("tr_sparseconv_forward_fused", _I, [_P, _P, _I, _P, _I, _P, _I, _P, _P, _I, _I, _I, _P]),
+    ("tr_sparseconv_pack_weights_dgrad", _I, [_P, _I, _I, _I, _P, _SZ, _P]),
+    ("tr_sparseconv_backward_data", _I, [_P, _P, _I, _P, _I, _P, _I, _I, _I, _P]),
+    ("tr_sparseconv_backward_weights_workspace_bytes", _SZ, [_I64, _I, _I, _I]),
+    ("tr_sparseconv_backward_weights", _I, [_P, _P, _P, _P, _I, _I, _I, _P, _SZ, _P]),
 ]
 
 _lib = None

@@ -378,4 +378,73 @@ int tr_sparseconv_forward_fused(const tr_sc_kmap* m, const void* x, int x_dtype,
                      c_out, static_cast<hipStream_t>(stream));
 }
 
+// ---------------------------------------------------------------------------
+// Backward.
+// ---------------------------------------------------------------------------
+int tr_sparseconv_pack_weights_dgrad(const void* w, int c_in, int c_out, int dtype, void* wp, size_t wp_bytes,
+                                     void* stream) {
+  const int c = check_channels("pack_weights_dgrad", c_in, c_out, dtype);
+  if (c != TR_SC_OK) return c;
+  if (w == nullptr || wp == nullptr) return fail(TR_SC_ERR_INVALID_ARG, "pack_weights_dgrad: NULL pointer");
+  const size_t need = tr_sparseconv_packed_weights_bytes(c_out, c_in, dtype);
+  if (wp_bytes < need)
+    return fail(TR_SC_ERR_WORKSPACE, "pack_weights_dgrad: %zu bytes < %zu needed", wp_bytes, need);
+  if (misaligned16(wp) || (is_half(dtype) && misaligned16(w)))
+    return fail(TR_SC_ERR_INVALID_ARG, "pack_weights_dgrad: w and wp must be 16-byte aligned");
+  const hipError_t e = launch_pack_dgrad(w, wp, c_in, c_out, dtype, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "pack_weights_dgrad");
+  return TR_SC_OK;
+}
+
+int tr_sparseconv_backward_data(const tr_sc_kmap* m, const void* dy, int dy_dtype, const void* wpd, int w_dtype,
+                                void* dx, int dx_dtype, int c_in, int c_out, void* stream) {
+  if (m == nullptr || m->magic != kKmapMagic)
+    return fail(TR_SC_ERR_INVALID_ARG, "backward_data: bad kernel-map handle");
+  const int c = check_channels("backward_data", c_in, c_out, w_dtype);
+  if (c != TR_SC_OK) return c;
+  const bool ok_types = w_dtype == TR_SC_F32
+                            ? (dy_dtype == TR_SC_F32 && dx_dtype == TR_SC_F32)
+                            : ((dy_dtype == w_dtype || dy_dtype == TR_SC_F32) &&
+                               (dx_dtype == w_dtype || dx_dtype == TR_SC_F32));
+  if (!ok_types)
+    return fail(TR_SC_ERR_UNSUPPORTED, "backward_data: dy dtype %d, weight dtype %d, dx dtype %d", dy_dtype,
+                w_dtype, dx_dtype);
+  if (m->n == 0) return TR_SC_OK;
+  if (dy == dx) return fail(TR_SC_ERR_INVALID_ARG, "backward_data: dy and dx are the same buffer");
+  // the forward gather-GEMM of the c_out -> c_in convolution with the mirrored taps
+  return run_forward("backward_data", m, dy, dy_dtype, wpd, w_dtype, dx, dx_dtype,
+                     Epilogue{nullptr, nullptr, kActNone}, c_out, c_in, static_cast<hipStream_t>(stream));
+}
+
+size_t tr_sparseconv_backward_weights_workspace_bytes(int64_t n, int c_in, int c_out, int dtype) {
+  if (n < 0 || c_in <= 0 || c_out <= 0) return 0;
+  if (dtype == TR_SC_F32) return 0;
+  return 256 + align_up(plan_wgrad(n, c_in, c_out).partial_bytes, 256);
+}
+
+int tr_sparseconv_backward_weights(const tr_sc_kmap* m, const void* x, const void* dy, float* dw, int c_in,
+                                   int c_out, int dtype, void* workspace, size_t ws_bytes, void* stream) {
+  if (m == nullptr || m->magic != kKmapMagic)
+    return fail(TR_SC_ERR_INVALID_ARG, "backward_weights: bad kernel-map handle");
+  const int c = check_channels("backward_weights", c_in, c_out, dtype);
+  if (c != TR_SC_OK) return c;
+  const size_t need = tr_sparseconv_backward_weights_workspace_bytes(m->n, c_in, c_out, dtype);
+  if (ws_bytes < need)
+    return fail(TR_SC_ERR_WORKSPACE, "backward_weights: workspace %zu bytes < %zu needed", ws_bytes, need);
+  if (need > 0 && (workspace == nullptr || reinterpret_cast<uintptr_t>(workspace) % 256 != 0))
+    return fail(TR_SC_ERR_INVALID_ARG, "backward_weights: workspace NULL or not 256-byte aligned");
+  if (dw == nullptr || (m->n > 0 && (x == nullptr || dy == nullptr)))
+    return fail(TR_SC_ERR_INVALID_ARG, "backward_weights: NULL tensor");
+  if (is_half(dtype) && (misaligned16(x) || misaligned16(dy) || misaligned16(dw)))
+    return fail(TR_SC_ERR_INVALID_ARG, "backward_weights: x, dy and dw must be 16-byte aligned");
+  if (int64_t(m->n) * c_out >= (int64_t(1) << 40) || int64_t(m->n) * c_in >= (int64_t(1) << 40))
+    return fail(TR_SC_ERR_UNSUPPORTED, "backward_weights: tensor too large");
+  char* ws = static_cast<char*>(workspace);
+  WgradCall call{m->nbr, m->grows, m->gmask, m->n, x, dy, dw,
+                 need > 0 ? reinterpret_cast<float*>(ws + 256) : nullptr, ws, c_in, c_out, dtype};
+  const hipError_t e = launch_wgrad(call, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "backward_weights");
+  return TR_SC_OK;
+}
+
 }  // extern "C"

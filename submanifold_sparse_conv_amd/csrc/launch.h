@@ -66,4 +66,31 @@ inline int64_t packed_weight_elems(int c_in, int c_out) {
 hipError_t launch_pack_weights(const void* w, void* wp, int c_in, int c_out, hipStream_t st);
 hipError_t launch_forward_mfma(const ConvArgs& a, const void* wp, hipStream_t st);
 
+// Backward. Data-gradient weights: the forward packing of the c_out -> c_in
+// convolution with taps reversed (packed_weight_elems(c_out, c_in) elements and
+// the zero block for half types; [27][c_out][c_in] for fp32).
+hipError_t launch_pack_dgrad(const void* w, void* wp, int c_in, int c_out, int dtype, hipStream_t st);
+
+// Weight gradient: split of the positions into `splits` ranges of `range`
+// positions; partials [splits][27][c_in][c_out] fp32 when splits > 1.
+struct WgradPlan {
+  int ti, tj, tiles_i, tiles, splits;
+  int64_t range;
+  size_t partial_bytes;
+};
+WgradPlan plan_wgrad(int64_t n, int c_in, int c_out);
+struct WgradCall {
+  const int32_t* nbr;
+  const int32_t* grows;
+  const uint32_t* gmask;
+  int64_t n;
+  const void* x;
+  const void* dy;
+  float* dw;        // [27, c_in, c_out]
+  float* partials;  // plan_wgrad(...).partial_bytes
+  void* zeros;      // 256 bytes of workspace
+  int c_in, c_out, dtype;
+};
+hipError_t launch_wgrad(const WgradCall& c, hipStream_t st);
+
 }  // namespace trsc
