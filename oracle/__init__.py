@@ -62,6 +62,12 @@ def _load():
         lib.oc_backward_data.restype = ctypes.c_int
         lib.oc_backward_weights.argtypes = [P, I64, P, P, ctypes.c_int, ctypes.c_int, P, I64, P]
         lib.oc_backward_weights.restype = ctypes.c_int
+        lib.oc_downsample.argtypes = [P, I64, P, P, P]
+        lib.oc_downsample.restype = ctypes.c_int
+        lib.oc_subdivide.argtypes = [P, I64, P, P, P, P]
+        lib.oc_subdivide.restype = ctypes.c_int
+        lib.oc_regroup.argtypes = [P, I64, I64, ctypes.c_int, ctypes.c_int, P, P]
+        lib.oc_regroup.restype = ctypes.c_int
         lib.oc_num_threads.argtypes = []
         lib.oc_num_threads.restype = ctypes.c_int
         _lib = lib
@@ -190,6 +196,58 @@ def backward_weights(nbr: np.ndarray, x: np.ndarray, dy: np.ndarray, sel=None) -
     if st != OK:
         raise OracleError(st, "backward_weights")
     return dw.reshape(27, c_in, c_out) if s is None else dw
+
+
+def downsample(coords: np.ndarray):
+    """(coarse coords [m, 4], children [m, 8]) of the parent level."""
+    c = np.ascontiguousarray(coords, dtype=np.int32).reshape(-1, 4)
+    n = len(c)
+    coarse = np.empty((n, 4), dtype=np.int32)
+    children = np.empty((n, 8), dtype=np.int32)
+    m = ctypes.c_int64(0)
+    st = _load().oc_downsample(_ptr(c), n, _ptr(coarse), _ptr(children), ctypes.byref(m))
+    if st != OK:
+        raise OracleError(st, "downsample")
+    return coarse[:m.value].copy(), children[:m.value].copy()
+
+
+def subdivide(coords: np.ndarray, keep=None):
+    """(fine coords [f, 4], children [n, 8]); keep: uint8 [n] child bitmasks or None (all)."""
+    c = np.ascontiguousarray(coords, dtype=np.int32).reshape(-1, 4)
+    n = len(c)
+    k = None if keep is None else np.ascontiguousarray(keep, dtype=np.uint8).reshape(n)
+    fine = np.empty((8 * n, 4), dtype=np.int32)
+    children = np.empty((n, 8), dtype=np.int32)
+    f = ctypes.c_int64(0)
+    st = _load().oc_subdivide(_ptr(c), n, None if k is None else _ptr(k), _ptr(fine), _ptr(children),
+                              ctypes.byref(f))
+    if st != OK:
+        raise OracleError(st, "subdivide")
+    return fine[:f.value].copy(), children
+
+
+def channel2spatial(children: np.ndarray, x_coarse: np.ndarray, n_fine: int) -> np.ndarray:
+    """x_fine [n_fine, C] (fp64) from x_coarse [n_coarse, 8 C]."""
+    ch = np.ascontiguousarray(children, dtype=np.int32).reshape(-1, 8)
+    xc = widen(x_coarse).reshape(len(ch), -1)
+    c_fine = xc.shape[1] // 8
+    xf = np.zeros((n_fine, c_fine), dtype=np.float64)
+    st = _load().oc_regroup(_ptr(ch), len(ch), n_fine, c_fine, 1, _ptr(xc), _ptr(xf))
+    if st != OK:
+        raise OracleError(st, "channel2spatial")
+    return xf
+
+
+def spatial2channel(children: np.ndarray, x_fine: np.ndarray) -> np.ndarray:
+    """x_coarse [n_coarse, 8 C] (fp64) from x_fine [n_fine, C]."""
+    ch = np.ascontiguousarray(children, dtype=np.int32).reshape(-1, 8)
+    xf = widen(x_fine)
+    c_fine = xf.shape[1]
+    xc = np.empty((len(ch), 8 * c_fine), dtype=np.float64)
+    st = _load().oc_regroup(_ptr(ch), len(ch), len(xf), c_fine, 0, _ptr(xc), _ptr(xf))
+    if st != OK:
+        raise OracleError(st, "spatial2channel")
+    return xc
 
 
 ACTS = {"none": 0, "relu": 1, "silu": 2}

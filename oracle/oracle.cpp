@@ -36,6 +36,7 @@
 // of W[k, ci, co] * x[nbr[i][k], ci], accumulated in double in exactly that
 // (k, ci) order and never rounded.
 #include <algorithm>
+#include <array>
 #include <climits>
 #include <cmath>
 #include <cstdint>
@@ -286,6 +287,121 @@ int oc_backward_weights(const int32_t* nbr, int64_t n, const double* x, const do
       for (int co = 0; co < c_out; ++co) out[co] += xv * g[co];
     }
   }
+  return kOk;
+}
+
+// ---------------------------------------------------------------------------
+// Moving between resolution levels. The pages build one neighbour table per
+// resolution level ("Porting TRELLIS.2 ...", section V); their decoders change
+// level with pixel-shuffle / Channel2Spatial upsampling driven by subdivision
+// predictions (TRELLIS.2 MLX port README, repository tree and pipeline list).
+// Readings (listed in the design notes): the parent of (b, x, y, z) is
+// (b, x >> 1, y >> 1, z >> 1); the children of (b, x, y, z) are
+// (b, 2x + dx, 2y + dy, 2z + dz) with octant o = 4 dx + 2 dy + dz; a parent
+// row of 8C channels holds child o's channel c at c * 8 + o (the channel order
+// of a pixel shuffle).
+// ---------------------------------------------------------------------------
+
+// Z-order rank of (x, y, z): bit i of x, y, z at bits 3i + 2, 3i + 1, 3i.
+static uint64_t zorder(uint32_t x, uint32_t y, uint32_t z) {
+  uint64_t key = 0;
+  for (int i = 0; i < 16; ++i) {
+    key |= uint64_t((x >> i) & 1u) << (3 * i + 2);
+    key |= uint64_t((y >> i) & 1u) << (3 * i + 1);
+    key |= uint64_t((z >> i) & 1u) << (3 * i);
+  }
+  return key;
+}
+
+// Coarser level: the set of parents, ordered by batch index, then Z-order of
+// (x, y, z); children[q * 8 + o] = the row of child o of parent q, or -1.
+int oc_downsample(const int32_t* coords, int64_t n, int32_t* coarse, int32_t* children, int64_t* n_coarse) {
+  if (n < 0 || n_coarse == nullptr || (n > 0 && (coords == nullptr || coarse == nullptr || children == nullptr)))
+    return kErrInvalid;
+  std::unordered_map<uint64_t, int64_t> parent;  // packed parent coordinate -> index in `order`
+  std::vector<std::array<int32_t, 4>> order;
+  for (int64_t i = 0; i < n; ++i) {
+    const int32_t* c = coords + 4 * i;
+    if (!in_range(c[0]) || !in_range(c[1]) || !in_range(c[2]) || !in_range(c[3])) return kErrCoordRange;
+    const std::array<int32_t, 4> pc{c[0], c[1] >> 1, c[2] >> 1, c[3] >> 1};
+    if (parent.emplace(pack_key(pc[0], pc[1], pc[2], pc[3]), int64_t(order.size())).second) order.push_back(pc);
+  }
+  std::vector<int64_t> rank(order.size());
+  for (size_t q = 0; q < order.size(); ++q) rank[q] = int64_t(q);
+  std::sort(rank.begin(), rank.end(), [&](int64_t a, int64_t b) {
+    const auto& A = order[size_t(a)];
+    const auto& B = order[size_t(b)];
+    if (A[0] != B[0]) return A[0] < B[0];
+    return zorder(uint32_t(A[1]), uint32_t(A[2]), uint32_t(A[3])) <
+           zorder(uint32_t(B[1]), uint32_t(B[2]), uint32_t(B[3]));
+  });
+  std::vector<int64_t> pos(order.size());
+  for (size_t r = 0; r < rank.size(); ++r) pos[size_t(rank[r])] = int64_t(r);
+  const int64_t m = int64_t(order.size());
+  for (int64_t q = 0; q < m; ++q)
+    for (int e = 0; e < 4; ++e) coarse[4 * pos[size_t(q)] + e] = order[size_t(q)][size_t(e)];
+  std::fill(children, children + 8 * m, -1);
+  for (int64_t i = 0; i < n; ++i) {
+    const int32_t* c = coords + 4 * i;
+    const int64_t q = pos[size_t(parent.at(pack_key(c[0], c[1] >> 1, c[2] >> 1, c[3] >> 1)))];
+    const int o = 4 * (c[1] & 1) + 2 * (c[2] & 1) + (c[3] & 1);
+    children[8 * q + o] = int32_t(i);
+  }
+  *n_coarse = m;
+  return kOk;
+}
+
+// Finer level: for each row i in order and octant o = 0..7 with bit o of
+// keep[i] set (all 8 if keep is NULL), the next fine row is child o of i.
+// children[i * 8 + o] = that fine row, or -1. Fine coordinates must stay below
+// 2^16 on every axis.
+int oc_subdivide(const int32_t* coords, int64_t n, const uint8_t* keep, int32_t* fine, int32_t* children,
+                 int64_t* n_fine) {
+  if (n < 0 || n_fine == nullptr || (n > 0 && (coords == nullptr || fine == nullptr || children == nullptr)))
+    return kErrInvalid;
+  int64_t f = 0;
+  for (int64_t i = 0; i < n; ++i) {
+    const int32_t* c = coords + 4 * i;
+    if (!in_range(c[0]) || !in_range(2 * c[1] + 1) || !in_range(2 * c[2] + 1) || !in_range(2 * c[3] + 1) ||
+        c[1] < 0 || c[2] < 0 || c[3] < 0)
+      return kErrCoordRange;
+    for (int o = 0; o < 8; ++o) {
+      if (keep != nullptr && !((keep[i] >> o) & 1)) {
+        children[8 * i + o] = -1;
+        continue;
+      }
+      fine[4 * f + 0] = c[0];
+      fine[4 * f + 1] = 2 * c[1] + ((o >> 2) & 1);
+      fine[4 * f + 2] = 2 * c[2] + ((o >> 1) & 1);
+      fine[4 * f + 3] = 2 * c[3] + (o & 1);
+      children[8 * i + o] = int32_t(f);
+      ++f;
+    }
+  }
+  *n_fine = f;
+  return kOk;
+}
+
+// x_fine[children[q * 8 + o], c] = x_coarse[q, c * 8 + o] (Channel2Spatial):
+// with to_fine = 1 from coarse [n_coarse, 8 C] to fine [n_fine, C]; with
+// to_fine = 0 the inverse gather, x_coarse[q, c * 8 + o] = x_fine[child, c] or
+// 0 where child o is absent (Spatial2Channel).
+int oc_regroup(const int32_t* children, int64_t n_coarse, int64_t n_fine, int c_fine, int to_fine,
+               double* x_coarse, double* x_fine) {
+  if (n_coarse < 0 || n_fine < 0 || c_fine <= 0) return kErrInvalid;
+  for (int64_t q = 0; q < n_coarse; ++q)
+    for (int o = 0; o < 8; ++o) {
+      const int32_t f = children[8 * q + o];
+      if (f < -1 || f >= n_fine) return kErrInvalid;
+      for (int c = 0; c < c_fine; ++c) {
+        double& xc = x_coarse[q * 8 * c_fine + int64_t(c) * 8 + o];
+        if (to_fine) {
+          if (f >= 0) x_fine[int64_t(f) * c_fine + c] = xc;
+        } else {
+          xc = f >= 0 ? x_fine[int64_t(f) * c_fine + c] : 0.0;
+        }
+      }
+    }
   return kOk;
 }
 

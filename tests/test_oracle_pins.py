@@ -423,3 +423,76 @@ def test_backward_subsets_and_single_tap():
     exp = np.zeros((len(coords), 4))
     exp[nbr[ii, k]] = dy[ii] @ w[k].T
     assert rel_err(oracle.backward_data(nbr, dy, wk), exp) < 1e-12
+
+
+# --------------------------------------------------------------------------
+# resolution levels: parents, children, Channel2Spatial regrouping
+# --------------------------------------------------------------------------
+def test_downsample_brute_force():
+    from tests.helpers import morton_keys_numpy
+    rng = np.random.default_rng(31)
+    coords = W.random_sparse(rng, 700, D=13, B=2)
+    coords = coords[rng.permutation(len(coords))]
+    coarse, children = oracle.downsample(coords)
+    par = {(b, x // 2, y // 2, z // 2) for b, x, y, z in coords.tolist()}
+    assert set(map(tuple, coarse.tolist())) == par and len(coarse) == len(par)
+    keys = morton_keys_numpy(coarse)
+    assert (np.diff(keys.astype(np.float64)) > 0).all()          # strictly in (b, Z-order)
+    row = {tuple(r): i for i, r in enumerate(coords.tolist())}
+    for q, (b, x, y, z) in enumerate(coarse.tolist()):
+        for o in range(8):
+            dx, dy, dz = o >> 2, (o >> 1) & 1, o & 1
+            assert children[q, o] == row.get((b, 2 * x + dx, 2 * y + dy, 2 * z + dz), -1)
+    ch = children[children >= 0]
+    np.testing.assert_array_equal(np.sort(ch), np.arange(len(coords)))
+
+
+def test_subdivide_definition_and_round_trip():
+    rng = np.random.default_rng(32)
+    coords = W.random_sparse(rng, 300, D=20, B=2)
+    keep = rng.integers(0, 256, len(coords)).astype(np.uint8)
+    keep[:5] = 0
+    fine, children = oracle.subdivide(coords, keep)
+    assert len(fine) == int(sum(bin(int(k)).count("1") for k in keep))
+    f = 0
+    for i, (b, x, y, z) in enumerate(coords.tolist()):
+        for o in range(8):
+            if (keep[i] >> o) & 1:
+                assert fine[f].tolist() == [b, 2 * x + (o >> 2), 2 * y + ((o >> 1) & 1), 2 * z + (o & 1)]
+                assert children[i, o] == f
+                f += 1
+            else:
+                assert children[i, o] == -1
+    # coarsening the subdivided set gives back the parents that kept a child
+    coarse, ch2 = oracle.downsample(fine)
+    kept = {tuple(c) for c, k in zip(coords.tolist(), keep) if k}
+    assert set(map(tuple, coarse.tolist())) == kept
+    back = {tuple(c): i for i, c in enumerate(coords.tolist())}
+    for q, c in enumerate(coarse.tolist()):
+        np.testing.assert_array_equal(ch2[q], children[back[tuple(c)]])
+    all_fine, _ = oracle.subdivide(coords)
+    assert len(all_fine) == 8 * len(coords)
+    with pytest.raises(oracle.OracleError):
+        oracle.subdivide(np.array([[0, 32768, 0, 0]], np.int32))
+
+
+def test_channel2spatial_is_a_dense_pixel_shuffle():
+    # dense 3D pixel shuffle by reshape/permute: channel c*8 + (4dx + 2dy + dz)
+    # of coarse cell p goes to channel c of fine cell 2p + (dx, dy, dz)
+    rng = np.random.default_rng(33)
+    D, B, C = 6, 2, 3
+    coords = W.random_sparse(rng, 120, D=D, B=B)
+    keep = rng.integers(1, 256, len(coords)).astype(np.uint8)
+    fine, children = oracle.subdivide(coords, keep)
+    xc = rng.standard_normal((len(coords), 8 * C))
+    dense = torch.from_numpy(dense_inputs(coords, xc, B, D))          # [B, 8C, D, D, D]
+    fine_dense = (dense.reshape(B, C, 2, 2, 2, D, D, D).permute(0, 1, 5, 2, 6, 3, 7, 4)
+                  .reshape(B, C, 2 * D, 2 * D, 2 * D).numpy())
+    f = fine.astype(np.int64)
+    expect = fine_dense[f[:, 0], :, f[:, 1], f[:, 2], f[:, 3]]
+    got = oracle.channel2spatial(children, xc, len(fine))
+    np.testing.assert_array_equal(got, expect)
+    # Spatial2Channel is its inverse on kept children and puts zeros elsewhere
+    back = oracle.spatial2channel(children, got)
+    mask = np.repeat((children >= 0)[:, None, :], C, axis=1).reshape(len(coords), 8 * C)
+    np.testing.assert_array_equal(back, np.where(mask, xc, 0.0))
