@@ -244,6 +244,52 @@ int tr_sparseconv_backward_weights(const tr_sc_kmap* m, const void* x, const voi
                                    int c_in, int c_out, int dtype, void* workspace,
                                    size_t ws_bytes, void* stream);
 
+/* ------------------------------------------------------------------------
+ * Resolution levels. The pages build one neighbour table per resolution level
+ * ("Porting TRELLIS.2 ...", section V) and move between levels with
+ * pixel-shuffle / Channel2Spatial upsampling driven by subdivision
+ * predictions (TRELLIS.2 MLX port README: repository tree, pipeline list).
+ * Conventions: the parent of (b, x, y, z) is (b, x >> 1, y >> 1, z >> 1);
+ * child o = 4 dx + 2 dy + dz of (b, x, y, z) is (b, 2x + dx, 2y + dy, 2z + dz);
+ * a parent feature row of 8C channels holds channel c of child o at c * 8 + o.
+ * A `children` table is int32 [n_coarse, 8]: the row of child o, or -1.
+ * ------------------------------------------------------------------------ */
+
+/* Workspace bytes of tr_sparseconv_downsample / tr_sparseconv_subdivide over n
+ * input rows (256-byte aligned buffer). */
+size_t tr_sparseconv_level_workspace_bytes(int64_t n);
+
+/* Parent level of the voxel set of h: coarse_coords int32 [cap, 4] receives
+ * the parents ordered by b, then Z-order of (x, y, z); children [cap, 8] their
+ * children (rows of h's coordinate array). *n_coarse receives the count (one
+ * small read-back: the call waits for `stream`). TR_SC_ERR_CAPACITY if more
+ * than cap parents (cap = n always suffices). No sort: the hash's Morton
+ * order already groups children by parent. */
+int tr_sparseconv_downsample(const tr_sc_hash* h, int32_t* coarse_coords, int32_t* children,
+                             int64_t cap, void* workspace, size_t ws_bytes, void* stream,
+                             int64_t* n_coarse);
+
+/* Finer level: coords int32 [n, 4] (16-byte aligned); keep uint8 [n], bit o
+ * set = child o exists (NULL: all eight). fine_coords int32 [cap, 4] receives
+ * the children in (row, octant) order, children [n, 8] their fine rows.
+ * *n_fine receives the count (read back; waits for `stream`).
+ * TR_SC_ERR_COORD_RANGE if a component is negative or a child would leave
+ * [0, 65536); TR_SC_ERR_CAPACITY if more than cap children (8n suffices). */
+int tr_sparseconv_subdivide(const int32_t* coords, int64_t n, const uint8_t* keep,
+                            int32_t* fine_coords, int32_t* children, int64_t cap,
+                            void* workspace, size_t ws_bytes, void* stream, int64_t* n_fine);
+
+/* Channel2Spatial: x_fine[children[q][o], c] = x_coarse[q, c * 8 + o]
+ * (x_coarse [n_coarse, 8 c_fine], x_fine [*, c_fine]; fine rows that are no
+ * one's child are left as they are). Spatial2Channel, its inverse gather:
+ * x_coarse[q, c * 8 + o] = x_fine[children[q][o], c], or 0 where child o is
+ * absent. dtype: f32 (c_fine % 4 == 0), bf16 or f16 (c_fine % 8 == 0); all
+ * pointers 16-byte aligned. Pure data movement: bit-exact. */
+int tr_sparseconv_channel2spatial(const int32_t* children, int64_t n_coarse, const void* x_coarse,
+                                  void* x_fine, int c_fine, int dtype, void* stream);
+int tr_sparseconv_spatial2channel(const int32_t* children, int64_t n_coarse, const void* x_fine,
+                                  void* x_coarse, int c_fine, int dtype, void* stream);
+
 /* Message of the last failed call on this thread ("" if none). */
 const char* tr_sparseconv_last_error(void);
 

@@ -18,7 +18,8 @@ from . import _lib
 from ._lib import TrSparseConvError, check  # noqa: F401
 
 __all__ = ["build_hash", "build_kernel_map", "forward", "pack_weights", "forward_packed", "forward_fused",
-           "pack_weights_dgrad", "backward_data", "backward_weights",
+           "pack_weights_dgrad", "backward_data", "backward_weights", "downsample", "subdivide",
+           "channel2spatial", "spatial2channel",
            "status", "hash_lookup", "hash_sorted_rows", "HashTable", "KernelMap", "PackedWeights",
            "TrSparseConvError", "version", "forward_workspace_bytes", "Workspace"]
 
@@ -85,6 +86,7 @@ class HashTable:
             check(L.tr_sparseconv_build_hash(_ptr(coords), self.n, self._ws.ptr, self._ws.nbytes,
                                              _stream(self.device), ctypes.byref(h)))
         self._h = h
+        self._destroy = L.tr_sparseconv_hash_destroy
         if check_status:
             self.check_status()
 
@@ -114,9 +116,11 @@ class HashTable:
         return perm
 
     def __del__(self):
-        h = getattr(self, "_h", None)
-        if h is not None and _lib._lib is not None:
-            _lib._lib.tr_sparseconv_hash_destroy(h)
+        # the bound C function is held by the instance: module globals may
+        # already be gone when this runs at interpreter exit
+        h, destroy = getattr(self, "_h", None), getattr(self, "_destroy", None)
+        if h is not None and destroy is not None:
+            destroy(h)
             self._h = None
 
 
@@ -143,6 +147,7 @@ class KernelMap:
                                                    self._ws.nbytes, _stream(self.device),
                                                    ctypes.byref(m)))
         self._m = m
+        self._destroy = L.tr_sparseconv_kmap_destroy
         self._fws = {}
 
     @property
@@ -157,9 +162,9 @@ class KernelMap:
         return self._fws[key]
 
     def __del__(self):
-        m = getattr(self, "_m", None)
-        if m is not None and _lib._lib is not None:
-            _lib._lib.tr_sparseconv_kmap_destroy(m)
+        m, destroy = getattr(self, "_m", None), getattr(self, "_destroy", None)
+        if m is not None and destroy is not None:
+            destroy(m)
             self._m = None
 
 
@@ -316,6 +321,78 @@ def backward_weights(m: KernelMap, x: torch.Tensor, dy: torch.Tensor, out: torch
     with torch.cuda.device(x.device):
         check(L.tr_sparseconv_backward_weights(m.handle, _ptr(x), _ptr(dy), _ptr(out), c_in, c_out, dt, ws.ptr,
                                                ws.nbytes, _stream(x.device)))
+    return out
+
+
+def downsample(h: HashTable, workspace: Workspace | None = None):
+    """Parent level of the voxel set of `h`: (coarse coords int32 [M, 4] in
+    (b, Z-order) order, children int32 [M, 8] = row of child o or -1)."""
+    L = _lib.lib()
+    coarse = torch.empty((max(h.n, 1), 4), dtype=torch.int32, device=h.device)
+    children = torch.empty((max(h.n, 1), 8), dtype=torch.int32, device=h.device)
+    ws = _workspace(L.tr_sparseconv_level_workspace_bytes(h.n), h.device, workspace)
+    m = ctypes.c_int64(0)
+    with torch.cuda.device(h.device):
+        check(L.tr_sparseconv_downsample(h.handle, _ptr(coarse), _ptr(children), h.n, ws.ptr, ws.nbytes,
+                                         _stream(h.device), ctypes.byref(m)))
+    return coarse[:m.value], children[:m.value]
+
+
+def subdivide(coords: torch.Tensor, keep: torch.Tensor | None = None, workspace: Workspace | None = None):
+    """Finer level: child o of row i exists where bit o of keep[i] (uint8 [N])
+    is set (all eight if keep is None). Returns (fine coords int32 [F, 4] in
+    (row, octant) order, children int32 [N, 8] = fine row of child o or -1)."""
+    _require(coords, "coords", torch.int32, 2)
+    n = int(coords.shape[0])
+    if keep is not None:
+        _require(keep, "keep", torch.uint8, 1)
+        if int(keep.shape[0]) != n:
+            raise ValueError(f"keep must be [{n}]")
+    L = _lib.lib()
+    cap = 8 * n
+    fine = torch.empty((max(cap, 1), 4), dtype=torch.int32, device=coords.device)
+    children = torch.empty((max(n, 1), 8), dtype=torch.int32, device=coords.device)
+    ws = _workspace(L.tr_sparseconv_level_workspace_bytes(n), coords.device, workspace)
+    f = ctypes.c_int64(0)
+    with torch.cuda.device(coords.device):
+        check(L.tr_sparseconv_subdivide(_ptr(coords), n, _ptr(keep), _ptr(fine), _ptr(children), cap, ws.ptr,
+                                        ws.nbytes, _stream(coords.device), ctypes.byref(f)))
+    return fine[:f.value], children[:n]
+
+
+def channel2spatial(children: torch.Tensor, x_coarse: torch.Tensor, n_fine: int,
+                    out: torch.Tensor | None = None) -> torch.Tensor:
+    """x_fine [n_fine, C] from x_coarse [M, 8C]: channel c * 8 + o of parent q
+    goes to channel c of its child o (children [M, 8])."""
+    _require(children, "children", torch.int32, 2)
+    _require(x_coarse, "x_coarse", x_coarse.dtype, 2)
+    if x_coarse.dtype not in _DTYPES or x_coarse.shape[1] % 8:
+        raise ValueError("x_coarse must be [M, 8C] of a supported dtype")
+    c_fine = int(x_coarse.shape[1]) // 8
+    if out is None:
+        out = torch.empty((n_fine, c_fine), dtype=x_coarse.dtype, device=x_coarse.device)
+    _require(out, "out", x_coarse.dtype, 2)
+    with torch.cuda.device(x_coarse.device):
+        check(_lib.lib().tr_sparseconv_channel2spatial(_ptr(children), int(children.shape[0]), _ptr(x_coarse),
+                                                       _ptr(out), c_fine, _DTYPES[x_coarse.dtype],
+                                                       _stream(x_coarse.device)))
+    return out
+
+
+def spatial2channel(children: torch.Tensor, x_fine: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """x_coarse [M, 8C] from x_fine [F, C]; absent children give zeros."""
+    _require(children, "children", torch.int32, 2)
+    if x_fine.dtype not in _DTYPES:
+        raise ValueError(f"unsupported dtype {x_fine.dtype}")
+    _require(x_fine, "x_fine", x_fine.dtype, 2)
+    c_fine = int(x_fine.shape[1])
+    if out is None:
+        out = torch.empty((int(children.shape[0]), 8 * c_fine), dtype=x_fine.dtype, device=x_fine.device)
+    _require(out, "out", x_fine.dtype, 2)
+    with torch.cuda.device(x_fine.device):
+        check(_lib.lib().tr_sparseconv_spatial2channel(_ptr(children), int(children.shape[0]), _ptr(x_fine),
+                                                       _ptr(out), c_fine, _DTYPES[x_fine.dtype],
+                                                       _stream(x_fine.device)))
     return out
 
 

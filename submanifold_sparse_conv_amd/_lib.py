@@ -62,6 +62,11 @@ SIGNATURES = [
     ("tr_sparseconv_backward_data", _I, [_P, _P, _I, _P, _I, _P, _I, _I, _I, _P]),
     ("tr_sparseconv_backward_weights_workspace_bytes", _SZ, [_I64, _I, _I, _I]),
     ("tr_sparseconv_backward_weights", _I, [_P, _P, _P, _P, _I, _I, _I, _P, _SZ, _P]),
+    ("tr_sparseconv_level_workspace_bytes", _SZ, [_I64]),
+    ("tr_sparseconv_downsample", _I, [_P, _P, _P, _I64, _P, _SZ, _P, ctypes.POINTER(ctypes.c_int64)]),
+    ("tr_sparseconv_subdivide", _I, [_P, _I64, _P, _P, _P, _I64, _P, _SZ, _P, ctypes.POINTER(ctypes.c_int64)]),
+    ("tr_sparseconv_channel2spatial", _I, [_P, _I64, _P, _P, _I, _I, _P]),
+    ("tr_sparseconv_spatial2channel", _I, [_P, _I64, _P, _P, _I, _I, _P]),
 ]
 
 _lib = None

@@ -447,4 +447,122 @@ int tr_sparseconv_backward_weights(const tr_sc_kmap* m, const void* x, const voi
   return TR_SC_OK;
 }
 
+// ---------------------------------------------------------------------------
+// Resolution levels.
+// ---------------------------------------------------------------------------
+namespace {
+
+struct LevelHeader {
+  int64_t total;
+  uint32_t flags;
+  uint32_t pad;
+};
+
+__global__ void level_header_init(LevelHeader* h) {
+  if (threadIdx.x == 0) {
+    h->total = 0;
+    h->flags = 0;
+  }
+}
+
+// Reads the produced count (and flags) back; waits for `st`.
+int level_readback(const char* who, LevelHeader* dh, int64_t cap, hipStream_t st, int64_t* count) {
+  LevelHeader host{};
+  hipError_t e = hipMemcpyAsync(&host, dh, sizeof(host), hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return hip_fail(e, who);
+  *count = host.total;
+  if (host.flags & kFlagCoordRange)
+    return fail(TR_SC_ERR_COORD_RANGE, "%s: a coordinate component is negative or its children leave [0, 65536)",
+                who);
+  if (host.total > cap)
+    return fail(TR_SC_ERR_CAPACITY, "%s: %lld rows produced, capacity %lld", who, (long long)host.total,
+                (long long)cap);
+  return TR_SC_OK;
+}
+
+}  // namespace
+
+size_t tr_sparseconv_level_workspace_bytes(int64_t n) {
+  if (n < 0) return 0;
+  return 256 + align_up(size_t(level_blocks(n)) * 8, 256);
+}
+
+int tr_sparseconv_downsample(const tr_sc_hash* h, int32_t* coarse_coords, int32_t* children, int64_t cap,
+                             void* workspace, size_t ws_bytes, void* stream, int64_t* n_coarse) {
+  if (h == nullptr || h->magic != kHashMagic) return fail(TR_SC_ERR_INVALID_ARG, "downsample: bad hash handle");
+  if (n_coarse == nullptr || cap < 0) return fail(TR_SC_ERR_INVALID_ARG, "downsample: bad output arguments");
+  *n_coarse = 0;
+  const size_t need = tr_sparseconv_level_workspace_bytes(h->n);
+  if (ws_bytes < need) return fail(TR_SC_ERR_WORKSPACE, "downsample: workspace %zu bytes < %zu", ws_bytes, need);
+  if (workspace == nullptr || reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+    return fail(TR_SC_ERR_INVALID_ARG, "downsample: workspace NULL or not 256-byte aligned");
+  if (cap > 0 && (coarse_coords == nullptr || children == nullptr || misaligned16(coarse_coords) ||
+                  misaligned16(children)))
+    return fail(TR_SC_ERR_INVALID_ARG, "downsample: outputs NULL or not 16-byte aligned");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  LevelHeader* dh = static_cast<LevelHeader*>(workspace);
+  int64_t* part = reinterpret_cast<int64_t*>(static_cast<char*>(workspace) + 256);
+  level_header_init<<<1, 64, 0, st>>>(dh);
+  hipError_t e = launch_downsample(h->skeys, h->table.srows, h->n, cap, part, &dh->total, coarse_coords, children,
+                                   st);
+  if (e != hipSuccess) return hip_fail(e, "downsample");
+  return level_readback("downsample", dh, cap, st, n_coarse);
+}
+
+int tr_sparseconv_subdivide(const int32_t* coords, int64_t n, const uint8_t* keep, int32_t* fine_coords,
+                            int32_t* children, int64_t cap, void* workspace, size_t ws_bytes, void* stream,
+                            int64_t* n_fine) {
+  if (n_fine == nullptr || n < 0 || cap < 0 || n > kMaxN)
+    return fail(TR_SC_ERR_INVALID_ARG, "subdivide: bad sizes or output count pointer");
+  *n_fine = 0;
+  const size_t need = tr_sparseconv_level_workspace_bytes(n);
+  if (ws_bytes < need) return fail(TR_SC_ERR_WORKSPACE, "subdivide: workspace %zu bytes < %zu", ws_bytes, need);
+  if (workspace == nullptr || reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+    return fail(TR_SC_ERR_INVALID_ARG, "subdivide: workspace NULL or not 256-byte aligned");
+  if (n > 0 && (coords == nullptr || children == nullptr || misaligned16(coords) || misaligned16(children)))
+    return fail(TR_SC_ERR_INVALID_ARG, "subdivide: coords / children NULL or not 16-byte aligned");
+  if (cap > 0 && (fine_coords == nullptr || misaligned16(fine_coords)))
+    return fail(TR_SC_ERR_INVALID_ARG, "subdivide: fine_coords NULL or not 16-byte aligned");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  LevelHeader* dh = static_cast<LevelHeader*>(workspace);
+  int64_t* part = reinterpret_cast<int64_t*>(static_cast<char*>(workspace) + 256);
+  level_header_init<<<1, 64, 0, st>>>(dh);
+  hipError_t e = launch_subdivide(coords, keep, n, cap, part, &dh->total, &dh->flags, fine_coords, children, st);
+  if (e != hipSuccess) return hip_fail(e, "subdivide");
+  return level_readback("subdivide", dh, cap, st, n_fine);
+}
+
+namespace {
+int regroup_call(const char* who, const int32_t* children, int64_t n_coarse, const void* src, void* dst,
+                 int c_fine, int dtype, bool to_fine, void* stream) {
+  if (n_coarse < 0 || c_fine <= 0) return fail(TR_SC_ERR_INVALID_ARG, "%s: n_coarse %lld, c_fine %d", who,
+                                                (long long)n_coarse, c_fine);
+  if (dtype != TR_SC_F32 && !is_half(dtype)) return fail(TR_SC_ERR_UNSUPPORTED, "%s: dtype %d", who, dtype);
+  const int v = dtype == TR_SC_F32 ? 4 : 8;
+  if (c_fine % v != 0)
+    return fail(TR_SC_ERR_UNSUPPORTED, "%s: c_fine must be a multiple of %d for this dtype", who, v);
+  if (n_coarse == 0) return TR_SC_OK;
+  if (children == nullptr || src == nullptr || dst == nullptr) return fail(TR_SC_ERR_INVALID_ARG, "%s: NULL", who);
+  if (misaligned16(children) || misaligned16(src) || misaligned16(dst))
+    return fail(TR_SC_ERR_INVALID_ARG, "%s: pointers must be 16-byte aligned", who);
+  void* xc = to_fine ? const_cast<void*>(src) : dst;
+  void* xf = to_fine ? dst : const_cast<void*>(src);
+  const hipError_t e = launch_regroup(children, n_coarse, xc, xf, c_fine, dtype == TR_SC_F32 ? 4 : 2, to_fine,
+                                      static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, who);
+  return TR_SC_OK;
+}
+}  // namespace
+
+int tr_sparseconv_channel2spatial(const int32_t* children, int64_t n_coarse, const void* x_coarse, void* x_fine,
+                                  int c_fine, int dtype, void* stream) {
+  return regroup_call("channel2spatial", children, n_coarse, x_coarse, x_fine, c_fine, dtype, true, stream);
+}
+
+int tr_sparseconv_spatial2channel(const int32_t* children, int64_t n_coarse, const void* x_fine, void* x_coarse,
+                                  int c_fine, int dtype, void* stream) {
+  return regroup_call("spatial2channel", children, n_coarse, x_fine, x_coarse, c_fine, dtype, false, stream);
+}
+
 }  // extern "C"

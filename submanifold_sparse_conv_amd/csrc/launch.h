@@ -93,4 +93,14 @@ struct WgradCall {
 };
 hipError_t launch_wgrad(const WgradCall& c, hipStream_t st);
 
+// Resolution levels: per-1024-item block partials (int64) scanned in place; the
+// produced count goes to *total.
+int64_t level_blocks(int64_t n);
+hipError_t launch_downsample(const uint64_t* skeys, const int32_t* srows, int64_t n, int64_t cap, int64_t* part,
+                             int64_t* total, int32_t* coarse, int32_t* children, hipStream_t st);
+hipError_t launch_subdivide(const int32_t* coords, const uint8_t* keep, int64_t n, int64_t cap, int64_t* part,
+                            int64_t* total, uint32_t* flags, int32_t* fine, int32_t* children, hipStream_t st);
+hipError_t launch_regroup(const int32_t* children, int64_t n_coarse, void* xc, void* xf, int c_fine, int elem_bytes,
+                          bool to_fine, hipStream_t st);
+
 }  // namespace trsc
