@@ -39,13 +39,18 @@ WORKLOAD_NAMES = {
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=3)
+    # The GPU needs on the order of 0.1 s of sustained load to reach its steady
+    # clocks: 50 warm-up steps, then 200 timed steps (about 0.15 s) by default.
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=50)
     p.add_argument("--config", default="L", choices=list(WORKLOAD_NAMES))
     p.add_argument("--also", default="S", help="extra configs measured forward-only, comma list ('' = none)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-variants", action="store_true",
                    help="skip the fused-epilogue / fp16 / mixed-precision / backward timings")
+    p.add_argument("--no-chain", action="store_true", help="skip the decoder-level layer chain")
+    p.add_argument("--chain-blocks", type=int, default=4)
+    p.add_argument("--chain-channels", type=int, default=64)
     p.add_argument("--cpu-seconds", type=float, default=8.0, help="target wall time of the oracle forward sample")
     p.add_argument("--gemm-reps", type=int, default=50)
     p.add_argument("--copy-probe-mib", type=int, default=0,
@@ -116,9 +121,10 @@ def pairs_of(nbr_t):
 
 
 def measure_forward_only(sc, torch, path, reps):
-    """Back-to-back gather-GEMM launches between two events (steady state)."""
+    """Back-to-back gather-GEMM launches between two events (steady state,
+    after 2 x reps untimed launches)."""
     s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    for _ in range(3):
+    for _ in range(2 * reps):
         sc.forward_packed(path.m, path.x, path.wp, out=path.y)
     torch.cuda.synchronize()
     s.record()
@@ -130,8 +136,9 @@ def measure_forward_only(sc, torch, path, reps):
 
 
 def time_reps(torch, fn, reps):
-    """Mean ms of `fn` launched back to back between two events."""
-    for _ in range(3):
+    """Mean ms of `fn` launched back to back between two events (after reps
+    untimed calls)."""
+    for _ in range(reps):
         fn()
     torch.cuda.synchronize()
     s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -176,6 +183,56 @@ def variants(sc, torch, wl, path, M, reps):
         ms = time_reps(torch, fn, reps)
         out[name] = {"ms": ms, "effective_tflops": flops / (ms * 1e-3) / 1e12}
     return out
+
+
+def layer_chain(sc, torch, wl, blocks, ch, reps=5):
+    """A decoder level: the coarse voxel set subdivided with every child kept
+    (Channel2Spatial step: 8x the voxels at twice the resolution), then one
+    hash + kernel map and `blocks` residual blocks of two fp16 convolutions,
+    h = silu(conv(x) + b1), x = conv(h) + b2 + x, epilogues fused. Times the
+    whole level (subdivide + regroup + map + convs) and its parts."""
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device="cuda").manual_seed(11)
+    coarse = torch.from_numpy(wl.coords).to(dev)
+    xc = (torch.randn((wl.n, 8 * ch), device=dev, generator=g)).half()
+    ws = [sc.pack_weights((torch.randn((27, ch, ch), device=dev, generator=g) / (27 * ch) ** 0.5).half())
+          for _ in range(2 * blocks)]
+    bs = [torch.randn(ch, device=dev, generator=g) * 0.1 for _ in range(2 * blocks)]
+
+    def level():
+        fine, children = sc.subdivide(coarse)
+        x = sc.channel2spatial(children, xc, int(fine.shape[0]))
+        h = sc.build_hash(fine, check_status=False)
+        m = sc.build_kernel_map(h)
+        t = torch.empty_like(x)
+        for b in range(blocks):
+            sc.forward_fused(m, x, ws[2 * b], bias=bs[2 * b], act="silu", out=t)
+            sc.forward_fused(m, t, ws[2 * b + 1], bias=bs[2 * b + 1], residual=x, out=x)
+        return fine, m, x
+
+    fine, m, x = level()
+    torch.cuda.synchronize()
+    nf = int(fine.shape[0])
+    M = pairs_of(m.nbr)
+    t_level = []
+    for _ in range(reps):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        level()
+        torch.cuda.synchronize()
+        t_level.append((time.perf_counter() - t0) * 1e3)
+    t_map = time_reps(torch, lambda: sc.build_kernel_map(sc.build_hash(fine, check_status=False)), reps)
+    t = torch.empty_like(x)
+    t_conv = time_reps(torch, lambda: sc.forward_fused(m, x, ws[0], bias=bs[0], act="silu", out=t), 4 * reps)
+    flops = 2.0 * ch * ch * M
+    return {"workload": f"256^3 fBm shell subdivided (all children kept) -> {nf} voxels at 512^3, "
+                        f"{blocks} residual blocks of two 3x3x3 convs, C {ch}->{ch} fp16",
+            "n_voxels": nf, "pairs_M": M, "convs": 2 * blocks,
+            "ms_level": float(np.median(t_level)),
+            "ms_hash_and_map": t_map, "ms_per_conv": t_conv,
+            "map_share_of_level": t_map / float(np.median(t_level)),
+            "conv_effective_tflops": flops / (t_conv * 1e-3) / 1e12,
+            "voxel_layers_per_s": nf * 2 * blocks / (float(np.median(t_level)) * 1e-3)}
 
 
 def cpu_baseline(wl, target_s):
@@ -333,6 +390,8 @@ def main():
         out["also"] = extra
     if not args.no_variants and wl.dtype == "bf16":
         out["variants"] = variants(sc, torch, wl, path, M, max(5, args.gemm_reps // 2))
+    if not args.no_chain and args.config == "L":
+        out["chain"] = layer_chain(sc, torch, wl, args.chain_blocks, args.chain_channels)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     print(json.dumps(out), flush=True)
