@@ -34,15 +34,17 @@
  * Memory and streams. Every tensor pointer is a DEVICE pointer owned by the
  * caller, who must keep it alive while a handle that refers to it is in use.
  * `stream` is a hipStream_t (NULL = the null stream). Work is enqueued on it;
- * only tr_sparseconv_build_hash (one small read-back) and tr_sparseconv_status
- * wait for the device. Handles are small host structs; destroying one frees
- * that struct only, never device memory.
+ * only tr_sparseconv_status and the level calls that return a row count
+ * (tr_sparseconv_downsample, tr_sparseconv_subdivide) wait for the device.
+ * Handles are small host structs; destroying one frees that struct only, never
+ * device memory.
  *
  * Errors. Every int-returning call returns TR_SC_OK (0) or a negative
  * tr_sc_status. A failed call enqueues nothing further and records a message
  * for tr_sparseconv_last_error() (thread-local). Problems that only the device
- * can see after the read-back (duplicate coordinates, a full table) are kept in
- * a status word inside the hash workspace and returned by tr_sparseconv_status.
+ * can see (coordinates out of range, duplicate coordinates, a full table) are
+ * kept in a status word inside the hash workspace and returned by
+ * tr_sparseconv_status.
  */
 #ifndef TR_SPARSECONV_H
 #define TR_SPARSECONV_H
@@ -96,15 +98,16 @@ size_t tr_sparseconv_hash_workspace_bytes(int64_t n);
  * workspace device buffer of >= tr_sparseconv_hash_workspace_bytes(n) bytes,
  *           256-byte aligned; it holds the table and must outlive the handle.
  * out       receives a new handle (release with tr_sparseconv_hash_destroy).
- * Returns TR_SC_ERR_COORD_RANGE if any component is outside [0, 65536); this
- * is found by the device and read back once, so the call waits for the work
- * enqueued before it on `stream`. Duplicate coordinates are reported by
- * tr_sparseconv_status. */
+ * Enqueues the whole build on `stream` and returns without waiting for the
+ * device. Coordinates with a component outside [0, 65536) and duplicate
+ * coordinates are found on the device and reported by tr_sparseconv_status;
+ * until then the hash of such input must not be used. */
 int tr_sparseconv_build_hash(const int32_t* coords, int64_t n, void* workspace,
                              size_t ws_bytes, void* stream, tr_sc_hash** out);
 
 /* Device-found errors of the build, read from the workspace status word:
- * TR_SC_OK, TR_SC_ERR_DUPLICATE or TR_SC_ERR_CAPACITY. Synchronises `stream`. */
+ * TR_SC_OK, TR_SC_ERR_COORD_RANGE, TR_SC_ERR_DUPLICATE or TR_SC_ERR_CAPACITY.
+ * Synchronises `stream`. */
 int tr_sparseconv_status(const tr_sc_hash* h, void* stream);
 
 /* Number of voxels the hash was built over. */

@@ -64,11 +64,11 @@ HashLayout hash_layout(int64_t n) {
   l.rows1 = o;
   o += align_up(un * 4, 256);
   l.counts = o;
-  o += align_up(size_t(sort_blocks(n)) * 256 * 4, 256);
+  o += align_up(size_t(sort_blocks(n)) * kSortBuckets * 4, 256);
   l.totals = o;
-  o += 256 * 4;
+  o += kSortBuckets * 4;
   l.parts = o;
-  o += align_up(size_t(pack_partials(n)) * 16, 256);
+  o += align_up(size_t(pack_partials(n)) * 24, 256);
   l.cap = table_capacity(n);
   l.slots = o;
   o += size_t(l.cap) * sizeof(BlockSlot);
@@ -129,32 +129,15 @@ int tr_sparseconv_build_hash(const int32_t* coords, int64_t n, void* workspace, 
   unsigned long long* parts = reinterpret_cast<unsigned long long*>(ws + l.parts);
   BlockSlot* slots = reinterpret_cast<BlockSlot*>(ws + l.slots);
 
+  // No host wait: the digits of the sort are chosen on the device from the key
+  // bits that vary; range and duplicate errors are left in the header for
+  // tr_sparseconv_status.
   hipError_t e = launch_pack(coords, n, keys[0], rows[0], parts, hdr, st);
   if (e != hipSuccess) return hip_fail(e, "build_hash: pack");
-  // One read-back: the range flag and which key bits vary (they set the number
-  // of radix passes).
-  HashHeader host{};
-  e = hipMemcpyAsync(&host, hdr, sizeof(HashHeader), hipMemcpyDeviceToHost, st);
-  if (e == hipSuccess) e = hipStreamSynchronize(st);
-  if (e != hipSuccess) return hip_fail(e, "build_hash: read-back");
-  if (host.flags & kFlagCoordRange)
-    return fail(TR_SC_ERR_COORD_RANGE, "build_hash: a coordinate component is outside [0, 65536)");
-
-  int cur = 0;
-  if (n > 1) {
-    const uint64_t vary = host.or_bits ^ host.and_bits;
-    uint8_t pos[64];
-    int nv = 0;
-    for (int b = 0; b < 64; ++b)
-      if ((vary >> b) & 1u) pos[nv++] = uint8_t(b);
-    for (int p0 = 0; p0 < nv; p0 += 8) {
-      DigitSel sel{};
-      sel.nbits = nv - p0 < 8 ? nv - p0 : 8;
-      for (int j = 0; j < sel.nbits; ++j) sel.pos[j] = pos[p0 + j];
-      e = launch_sort_pass(keys[cur], rows[cur], keys[cur ^ 1], rows[cur ^ 1], n, sel, counts, totals, st);
-      if (e != hipSuccess) return hip_fail(e, "build_hash: sort");
-      cur ^= 1;
-    }
+  const int cur = 1;
+  if (n > 0) {
+    e = launch_sort(keys[0], rows[0], keys[1], rows[1], n, hdr, counts, totals, st);
+    if (e != hipSuccess) return hip_fail(e, "build_hash: sort");
   }
   e = launch_blocks(keys[cur], n, slots, l.cap, reinterpret_cast<uint32_t*>(parts), hdr, st);
   if (e != hipSuccess) return hip_fail(e, "build_hash: block table");

@@ -72,6 +72,13 @@ constexpr uint32_t kFlagCoordRange = 1u;
 constexpr uint32_t kFlagDuplicate = 2u;
 constexpr uint32_t kFlagCapacity = 4u;
 
+// One radix digit: key bits pos[0..nbits) (least significant first).
+constexpr int kMaxDigitBits = 11;
+struct DigitBits {
+  uint8_t pos[12];
+  int32_t nbits;
+};
+
 struct alignas(256) HashHeader {
   uint32_t flags;
   uint32_t nblocks;             // occupied 4x4x4 blocks
@@ -79,6 +86,9 @@ struct alignas(256) HashHeader {
   uint32_t shift;               // 64 - log2(capacity)
   unsigned long long or_bits;   // OR of all voxel keys
   unsigned long long and_bits;  // AND of all voxel keys
+  DigitBits digit[3];           // the three radix passes over the key bits that vary
+  int32_t rest_n;               // varying bits beyond the three digits (sorted by radix_rest)
+  uint8_t rest_pos[64];
 };
 
 struct TableRef {

@@ -41,11 +41,15 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
 
-// wp[k][co][ci] = w[k][ci][co], through 64 x 64 LDS tiles.
+// wp[k][co][ci] = w[k][ci][co], through 64 x 64 LDS tiles; the first
+// workgroup also writes the 256 zero bytes after the packed weights (the copy
+// source of absent neighbours and of channels past c_in).
 __global__ __launch_bounds__(kThreads) void pack_weights(const uint16_t* __restrict__ w,
                                                          uint16_t* __restrict__ wp, int c_in,
-                                                         int c_out) {
+                                                         int c_out, uint16_t* __restrict__ zeros) {
   __shared__ uint16_t t[64][65];
+  if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && threadIdx.x < 16)
+    reinterpret_cast<uint4*>(zeros)[threadIdx.x] = make_uint4(0u, 0u, 0u, 0u);
   const int k = blockIdx.z;
   const int ci0 = blockIdx.y * 64, co0 = blockIdx.x * 64;
   const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
@@ -60,12 +64,6 @@ __global__ __launch_bounds__(kThreads) void pack_weights(const uint16_t* __restr
     const int co = co0 + y, ci = ci0 + tx;
     if (co < c_out && ci < c_in) dst[int64_t(co) * c_in + ci] = t[tx][y];
   }
-}
-
-// The 256 zero bytes after the packed weights: the copy source of absent
-// neighbours and of channels past c_in.
-__global__ void zero_block(uint16_t* z) {
-  reinterpret_cast<uint4*>(z)[threadIdx.x & 15] = make_uint4(0u, 0u, 0u, 0u);
 }
 
 // The two half types of the matrix cores: their MFMA and conversions.
@@ -150,7 +148,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_rows(const RowsArgs p) {
   constexpr int KC = 64, ROWB = KC * 2;
   constexpr int AV = XT == 1 ? 1 : 2;         // 16-byte loads per 8 input channels
   constexpr int BBUF = TN * ROWB;             // weight slice of one stage
-  constexpr int OSTAGE = 4 * 16 * TN * 4;     // 16 fp32 output rows per wave, four waves
+  constexpr int OSTAGE = 4 * 8 * TN * 4;      // 8 fp32 output rows per wave, four waves
   __shared__ __attribute__((aligned(1024))) unsigned char bbuf0[BBUF > OSTAGE ? BBUF : OSTAGE];
   __shared__ __attribute__((aligned(1024))) unsigned char bbuf1[BBUF];
   __shared__ int32_t s_taps[27];
@@ -292,67 +290,73 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_rows(const RowsArgs p) {
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  // Staged row r holds TN floats in 16-byte pieces; piece q sits at q ^ osw(r),
-  // which spreads the four rows one write instruction touches over the banks
-  // and keeps each aligned group of four pieces contiguous.
+  // Staged row r (8 per pass) holds TN floats in 16-byte pieces; piece q sits
+  // at q ^ osw(r), which puts the two rows one write instruction touches on
+  // different banks and keeps each aligned group of four pieces contiguous.
   constexpr int PPR = TN / 4;
-  auto spos = [](int r, int q) { return r * TN + ((q ^ ((((r >> 2) & 3) << 2) & (PPR - 1))) << 2); };
-  float* sO = reinterpret_cast<float*>(bbuf0) + wave * 16 * TN;
+  auto spos = [](int r, int q) { return r * TN + ((q ^ (((r >> 2) & 1) << 2 & (PPR - 1))) << 2); };
+  float* sO = reinterpret_cast<float*>(bbuf0) + wave * 8 * TN;
   const int act = p.act;
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
 #pragma unroll
-    for (int j = 0; j < FN; ++j)
+    for (int h = 0; h < 2; ++h) {
+      // D rows 4 kg + e of this fragment: lanes with kg >> 1 == h hold rows 8h .. 8h + 7
+      if ((kg >> 1) == h) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = kg * 4 + e, c = j * 16 + lr;
-        sO[spos(r, c >> 2) + (c & 3)] = activate(acc[i][j][e] + bv[j], act);
-      }
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's staging writes are done
-    if (!p.y_f32) {
-      constexpr int OPR = TN / 8;
+        for (int j = 0; j < FN; ++j)
 #pragma unroll
-      for (int q = lane; q < 16 * OPR; q += 64) {
-        const int r = q / OPR, cc = q % OPR;
-        const int32_t row = __shfl(crow[i], r, 64);
-        const int co = n0 + cc * 8;
-        if (row >= 0 && co < c_out) {
-          const float4 lo = *reinterpret_cast<const float4*>(sO + spos(r, 2 * cc));
-          const float4 hi = *reinterpret_cast<const float4*>(sO + spos(r, 2 * cc + 1));
-          float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-          const int64_t off = int64_t(row) * c_out + co;
-          if (p.residual != nullptr) {
-            const uint4 rr = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.residual) + off);
-            const uint16_t* rh = reinterpret_cast<const uint16_t*>(&rr);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) v[e] += H::widen(rh[e]);
+          for (int e = 0; e < 4; ++e) {
+            const int r = (kg & 1) * 4 + e, c = j * 16 + lr;
+            sO[spos(r, c >> 2) + (c & 3)] = activate(acc[i][j][e] + bv[j], act);
           }
-          uint4 o;
-          uint16_t* oh = reinterpret_cast<uint16_t*>(&o);
+      }
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's staging writes are done
+      if (!p.y_f32) {
+        constexpr int OPR = TN / 8;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) oh[e] = H::narrow(v[e]);
-          *reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.y) + off) = o;
+        for (int q = lane; q < 8 * OPR; q += 64) {
+          const int r = q / OPR, cc = q % OPR;
+          const int32_t row = __shfl(crow[i], 8 * h + r, 64);
+          const int co = n0 + cc * 8;
+          if (row >= 0 && co < c_out) {
+            const float4 lo = *reinterpret_cast<const float4*>(sO + spos(r, 2 * cc));
+            const float4 hi = *reinterpret_cast<const float4*>(sO + spos(r, 2 * cc + 1));
+            float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+            const int64_t off = int64_t(row) * c_out + co;
+            if (p.residual != nullptr) {
+              const uint4 rr = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.residual) + off);
+              const uint16_t* rh = reinterpret_cast<const uint16_t*>(&rr);
+#pragma unroll
+              for (int e = 0; e < 8; ++e) v[e] += H::widen(rh[e]);
+            }
+            uint4 o;
+            uint16_t* oh = reinterpret_cast<uint16_t*>(&o);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) oh[e] = H::narrow(v[e]);
+            *reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.y) + off) = o;
+          }
+        }
+      } else {
+        constexpr int OPR = TN / 4;
+#pragma unroll
+        for (int q = lane; q < 8 * OPR; q += 64) {
+          const int r = q / OPR, cc = q % OPR;
+          const int32_t row = __shfl(crow[i], 8 * h + r, 64);
+          const int co = n0 + cc * 4;
+          if (row >= 0 && co < c_out) {
+            float4 v = *reinterpret_cast<const float4*>(sO + spos(r, cc));
+            const int64_t off = int64_t(row) * c_out + co;
+            if (p.residual != nullptr) {
+              const float4 rr = *reinterpret_cast<const float4*>(static_cast<const float*>(p.residual) + off);
+              v.x += rr.x, v.y += rr.y, v.z += rr.z, v.w += rr.w;
+            }
+            *reinterpret_cast<float4*>(static_cast<float*>(p.y) + off) = v;
+          }
         }
       }
-    } else {
-      constexpr int OPR = TN / 4;
-#pragma unroll
-      for (int q = lane; q < 16 * OPR; q += 64) {
-        const int r = q / OPR, cc = q % OPR;
-        const int32_t row = __shfl(crow[i], r, 64);
-        const int co = n0 + cc * 4;
-        if (row >= 0 && co < c_out) {
-          float4 v = *reinterpret_cast<const float4*>(sO + spos(r, cc));
-          const int64_t off = int64_t(row) * c_out + co;
-          if (p.residual != nullptr) {
-            const float4 rr = *reinterpret_cast<const float4*>(static_cast<const float*>(p.residual) + off);
-            v.x += rr.x, v.y += rr.y, v.z += rr.z, v.w += rr.w;
-          }
-          *reinterpret_cast<float4*>(static_cast<float*>(p.y) + off) = v;
-        }
-      }
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // reads done before the next pass overwrites
     }
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // reads done before the next block overwrites
   }
 }
 
@@ -395,8 +399,8 @@ hipError_t dispatch(const ConvArgs& a, const uint16_t* p, const uint16_t* zeros,
 hipError_t launch_pack_weights(const void* w, void* wp, int c_in, int c_out, hipStream_t st) {
   dim3 grid(unsigned((c_out + 63) / 64), unsigned((c_in + 63) / 64), 27);
   pack_weights<<<grid, kThreads, 0, st>>>(static_cast<const uint16_t*>(w), static_cast<uint16_t*>(wp),
-                                          c_in, c_out);
-  zero_block<<<1, 64, 0, st>>>(static_cast<uint16_t*>(wp) + packed_weight_elems(c_in, c_out));
+                                          c_in, c_out,
+                                          static_cast<uint16_t*>(wp) + packed_weight_elems(c_in, c_out));
   return hipGetLastError();
 }
 

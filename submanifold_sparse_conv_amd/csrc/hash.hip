@@ -27,13 +27,13 @@ __device__ inline unsigned long long wave_and(unsigned long long v) {
 }
 
 // keys[i] = key of coords[i]; rows[i] = i. Each block leaves the OR and AND of
-// its keys in part[2 * block + {0, 1}]; out-of-range coordinates set a flag.
+// its keys and an out-of-range flag in part[3 * block + {0, 1, 2}].
 __global__ __launch_bounds__(kThreads) void pack_keys(const int4* __restrict__ coords, int64_t n,
                                                       uint64_t* __restrict__ keys,
                                                       int32_t* __restrict__ rows,
-                                                      unsigned long long* __restrict__ part,
-                                                      HashHeader* hdr) {
+                                                      unsigned long long* __restrict__ part) {
   __shared__ unsigned long long s_or[kThreads / 64], s_and[kThreads / 64];
+  __shared__ int s_bad[kThreads / 64];
   unsigned long long k_or = 0, k_and = ~0ull;
   bool bad = false;
   for (int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x; i < n;
@@ -47,71 +47,111 @@ __global__ __launch_bounds__(kThreads) void pack_keys(const int4* __restrict__ c
     k_or |= key;
     k_and &= key;
   }
-  if (__ballot(bad) != 0 && (threadIdx.x & 63) == 0) atomicOr(&hdr->flags, kFlagCoordRange);
   k_or = wave_or(k_or);
   k_and = wave_and(k_and);
   const int wave = threadIdx.x >> 6;
+  const bool wbad = __ballot(bad) != 0;
   if ((threadIdx.x & 63) == 0) {
     s_or[wave] = k_or;
     s_and[wave] = k_and;
+    s_bad[wave] = wbad;
   }
   __syncthreads();
   if (threadIdx.x == 0) {
+    int anybad = s_bad[0];
     for (int w = 1; w < kThreads / 64; ++w) {
       k_or |= s_or[w];
       k_and &= s_and[w];
+      anybad |= s_bad[w];
     }
-    part[2 * blockIdx.x] = k_or;
-    part[2 * blockIdx.x + 1] = k_and;
+    part[3 * blockIdx.x] = k_or;
+    part[3 * blockIdx.x + 1] = k_and;
+    part[3 * blockIdx.x + 2] = anybad ? 1ull : 0ull;
   }
 }
 
+// Initialises the header: flags, an empty-table capacity, the OR / AND of all
+// keys, and the radix digits. The key bits that differ between keys (OR ^ AND)
+// are split, least significant first, into three digits of equal width (at
+// most kMaxDigitBits); any further bits go to the single-workgroup pass.
 __global__ __launch_bounds__(kThreads) void reduce_bits(const unsigned long long* __restrict__ part,
                                                         int nparts, HashHeader* hdr) {
   __shared__ unsigned long long s_or[kThreads / 64], s_and[kThreads / 64];
-  unsigned long long k_or = 0, k_and = ~0ull;
+  __shared__ unsigned long long s_bad[kThreads / 64];
+  unsigned long long k_or = 0, k_and = ~0ull, bad = 0;
   for (int i = threadIdx.x; i < nparts; i += kThreads) {
-    k_or |= part[2 * i];
-    k_and &= part[2 * i + 1];
+    k_or |= part[3 * i];
+    k_and &= part[3 * i + 1];
+    bad |= part[3 * i + 2];
   }
   k_or = wave_or(k_or);
   k_and = wave_and(k_and);
+  bad = wave_or(bad);
   if ((threadIdx.x & 63) == 0) {
     s_or[threadIdx.x >> 6] = k_or;
     s_and[threadIdx.x >> 6] = k_and;
+    s_bad[threadIdx.x >> 6] = bad;
   }
   __syncthreads();
   if (threadIdx.x == 0) {
     for (int w = 1; w < kThreads / 64; ++w) {
       k_or |= s_or[w];
       k_and &= s_and[w];
+      bad |= s_bad[w];
     }
-    hdr->or_bits = k_or;
-    hdr->and_bits = k_and;
+    HashHeader h{};
+    h.flags = bad ? kFlagCoordRange : 0u;
+    h.nblocks = 0;
+    h.cap_mask = 15;
+    h.shift = 60;
+    h.or_bits = k_or;
+    h.and_bits = k_and;
+    const unsigned long long vary = nparts > 0 ? (k_or ^ k_and) : 0ull;
+    const int nv = __popcll(vary);
+    int w = (nv + 2) / 3;
+    if (w > kMaxDigitBits) w = kMaxDigitBits;
+    int b = 0;
+    for (int d = 0; d < 3; ++d) {
+      h.digit[d].nbits = 0;
+      while (h.digit[d].nbits < w && b < 64) {
+        if ((vary >> b) & 1ull) h.digit[d].pos[h.digit[d].nbits++] = uint8_t(b);
+        ++b;
+      }
+    }
+    h.rest_n = 0;
+    for (; b < 64; ++b)
+      if ((vary >> b) & 1ull) h.rest_pos[h.rest_n++] = uint8_t(b);
+    *hdr = h;
   }
 }
 
-__device__ inline uint32_t digit_of(uint64_t key, const DigitSel& sel) {
+__device__ inline uint32_t digit_of(uint64_t key, const uint8_t* pos, int nbits) {
   uint32_t d = 0;
-#pragma unroll
-  for (int j = 0; j < 8; ++j)
-    if (j < sel.nbits) d |= uint32_t((key >> sel.pos[j]) & 1u) << j;
+  for (int j = 0; j < nbits; ++j) d |= uint32_t((key >> pos[j]) & 1u) << j;
   return d;
 }
 
-// counts[d * nblocks + block] = number of keys of this block's tile with digit d.
+constexpr int kMaxBuckets = 1 << kMaxDigitBits;
+
+// counts[d * nblocks + block] = number of keys of this block's tile with digit d
+// (d below 2^nbits of the pass's digit).
 __global__ __launch_bounds__(kThreads) void radix_hist(const uint64_t* __restrict__ keys, int64_t n,
-                                                       DigitSel sel, uint32_t* __restrict__ counts) {
-  __shared__ uint32_t h[256];
-  h[threadIdx.x] = 0;
+                                                       const HashHeader* __restrict__ hdr, int pass,
+                                                       uint32_t* __restrict__ counts) {
+  __shared__ uint32_t h[kMaxBuckets];
+  __shared__ uint8_t s_pos[12];
+  const int nbits = hdr->digit[pass].nbits;
+  const int nb = 1 << nbits;
+  if (threadIdx.x < 12) s_pos[threadIdx.x] = hdr->digit[pass].pos[threadIdx.x];
+  for (int d = threadIdx.x; d < nb; d += kThreads) h[d] = 0;
   __syncthreads();
   const int64_t base = int64_t(blockIdx.x) * kTile;
   for (int it = 0; it < kItems; ++it) {
     const int64_t i = base + it * kThreads + threadIdx.x;
-    if (i < n) atomicAdd(&h[digit_of(keys[i], sel)], 1u);
+    if (i < n) atomicAdd(&h[digit_of(keys[i], s_pos, nbits)], 1u);
   }
   __syncthreads();
-  counts[int64_t(threadIdx.x) * gridDim.x + blockIdx.x] = h[threadIdx.x];
+  for (int d = threadIdx.x; d < nb; d += kThreads) counts[int64_t(d) * gridDim.x + blockIdx.x] = h[d];
 }
 
 // Block-wide exclusive scan of one value per thread (256 threads).
@@ -135,10 +175,15 @@ __device__ inline uint32_t block_exclusive_scan(uint32_t v, uint32_t* s_tmp, uin
 }
 
 // One workgroup per digit d: exclusive scan over blocks of counts[d][*] in
-// place; totals[d] = number of keys with digit d.
+// place; totals[d] = number of keys with digit d (0 for digits the pass lacks).
 __global__ __launch_bounds__(kThreads) void radix_colscan(uint32_t* __restrict__ counts, int nblocks,
+                                                          const HashHeader* __restrict__ hdr, int pass,
                                                           uint32_t* __restrict__ totals) {
   __shared__ uint32_t s_tmp[kThreads / 64];
+  if (int(blockIdx.x) >= (1 << hdr->digit[pass].nbits)) {
+    if (threadIdx.x == 0) totals[blockIdx.x] = 0;
+    return;
+  }
   uint32_t* col = counts + int64_t(blockIdx.x) * nblocks;
   uint32_t carry = 0;
   for (int b0 = 0; b0 < nblocks; b0 += kThreads) {
@@ -158,22 +203,40 @@ __global__ __launch_bounds__(kThreads) void radix_scatter(const uint64_t* __rest
                                                           const int32_t* __restrict__ vin,
                                                           uint64_t* __restrict__ kout,
                                                           int32_t* __restrict__ vout, int64_t n,
-                                                          DigitSel sel,
+                                                          const HashHeader* __restrict__ hdr, int pass,
                                                           const uint32_t* __restrict__ offsets,
                                                           const uint32_t* __restrict__ totals) {
-  __shared__ uint32_t base_off[256];
-  __shared__ uint32_t wcount[kThreads / 64][256];
+  constexpr int PER = kMaxBuckets / kThreads;  // digits per thread in the digit scan
+  __shared__ uint32_t base_off[kMaxBuckets];
+  __shared__ uint32_t wcount[kThreads / 64][kMaxBuckets];
   __shared__ uint32_t s_tmp[kThreads / 64];
+  __shared__ uint8_t s_pos[12];
+  const int nbits = hdr->digit[pass].nbits;
+  const int nb = 1 << nbits;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
+  if (threadIdx.x < 12) s_pos[threadIdx.x] = hdr->digit[pass].pos[threadIdx.x];
+  // exclusive scan of the digit totals: thread t owns digits t*PER .. t*PER+PER-1
+  uint32_t loc[PER], sum = 0;
+#pragma unroll
+  for (int q = 0; q < PER; ++q) {
+    loc[q] = totals[threadIdx.x * PER + q];
+    sum += loc[q];
+  }
   uint32_t all;
-  const uint32_t digit_base = block_exclusive_scan(totals[threadIdx.x], s_tmp, &all);
-  base_off[threadIdx.x] = digit_base + offsets[int64_t(threadIdx.x) * gridDim.x + blockIdx.x];
+  uint32_t run = block_exclusive_scan(sum, s_tmp, &all);
+#pragma unroll
+  for (int q = 0; q < PER; ++q) {
+    const int d = threadIdx.x * PER + q;
+    if (d < nb) base_off[d] = run + offsets[int64_t(d) * gridDim.x + blockIdx.x];
+    run += loc[q];
+  }
   const unsigned long long lt = (1ull << lane) - 1ull;
   const int64_t base = int64_t(blockIdx.x) * kTile;
   for (int it = 0; it < kItems; ++it) {
+    for (int d = threadIdx.x; d < nb; d += kThreads)
 #pragma unroll
-    for (int w = 0; w < kThreads / 64; ++w) wcount[w][threadIdx.x] = 0;
+      for (int w = 0; w < kThreads / 64; ++w) wcount[w][d] = 0;
     __syncthreads();
     const int64_t i = base + it * kThreads + threadIdx.x;
     const bool valid = i < n;
@@ -183,16 +246,13 @@ __global__ __launch_bounds__(kThreads) void radix_scatter(const uint64_t* __rest
     if (valid) {
       key = kin[i];
       val = vin[i];
-      d = digit_of(key, sel);
+      d = digit_of(key, s_pos, nbits);
     }
     unsigned long long peers = __ballot(valid);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      if (j < sel.nbits) {
-        const bool bit = (d >> j) & 1u;
-        const unsigned long long bal = __ballot(bit);
-        peers &= bit ? bal : ~bal;
-      }
+    for (int j = 0; j < nbits; ++j) {
+      const bool bit = (d >> j) & 1u;
+      const unsigned long long bal = __ballot(bit);
+      peers &= bit ? bal : ~bal;
     }
     const uint32_t rank = __popcll(peers & lt);
     if (valid && (peers & lt) == 0) wcount[wave][d] = __popcll(peers);
@@ -204,11 +264,85 @@ __global__ __launch_bounds__(kThreads) void radix_scatter(const uint64_t* __rest
       vout[pos] = val;
     }
     __syncthreads();
-    uint32_t add = 0;
+    for (int dd = threadIdx.x; dd < nb; dd += kThreads) {
+      uint32_t add = 0;
 #pragma unroll
-    for (int w = 0; w < kThreads / 64; ++w) add += wcount[w][threadIdx.x];
-    base_off[threadIdx.x] += add;
+      for (int w = 0; w < kThreads / 64; ++w) add += wcount[w][dd];
+      base_off[dd] += add;
+    }
     __syncthreads();
+  }
+}
+
+// The key bits beyond the three digits (only when more than 3 * kMaxDigitBits
+// bits vary): one workgroup sorts keys[0..n) stably by them, 8 bits per pass,
+// using tmp as the other buffer, and leaves the result in keys / rows.
+__global__ __launch_bounds__(kThreads) void radix_rest(uint64_t* __restrict__ keys, int32_t* __restrict__ rows,
+                                                       uint64_t* __restrict__ tkeys, int32_t* __restrict__ trows,
+                                                       int64_t n, const HashHeader* __restrict__ hdr) {
+  __shared__ uint32_t hist[256], base_off[256];
+  __shared__ uint32_t wcount[kThreads / 64][256];
+  __shared__ uint32_t s_tmp[kThreads / 64];
+  __shared__ uint8_t s_pos[8];
+  const int rest = hdr->rest_n;
+  if (rest == 0) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const unsigned long long lt = (1ull << lane) - 1ull;
+  uint64_t* ka = keys;
+  int32_t* ra = rows;
+  uint64_t* kb = tkeys;
+  int32_t* rb = trows;
+  for (int p0 = 0; p0 < rest; p0 += 8) {
+    const int nbits = rest - p0 < 8 ? rest - p0 : 8;
+    if (threadIdx.x < 8) s_pos[threadIdx.x] = threadIdx.x < nbits ? hdr->rest_pos[p0 + threadIdx.x] : 0;
+    hist[threadIdx.x] = 0;
+    __syncthreads();
+    for (int64_t i = threadIdx.x; i < n; i += kThreads) atomicAdd(&hist[digit_of(ka[i], s_pos, nbits)], 1u);
+    __syncthreads();
+    uint32_t all;
+    base_off[threadIdx.x] = block_exclusive_scan(hist[threadIdx.x], s_tmp, &all);
+    for (int64_t t0 = 0; t0 < n; t0 += kThreads) {
+#pragma unroll
+      for (int w = 0; w < kThreads / 64; ++w) wcount[w][threadIdx.x] = 0;
+      __syncthreads();
+      const int64_t i = t0 + threadIdx.x;
+      const bool valid = i < n;
+      uint64_t key = valid ? ka[i] : 0ull;
+      const int32_t val = valid ? ra[i] : 0;
+      const uint32_t d = digit_of(key, s_pos, nbits);
+      unsigned long long peers = __ballot(valid);
+      for (int j = 0; j < nbits; ++j) {
+        const bool bit = (d >> j) & 1u;
+        const unsigned long long bal = __ballot(bit);
+        peers &= bit ? bal : ~bal;
+      }
+      if (valid && (peers & lt) == 0) wcount[wave][d] = __popcll(peers);
+      __syncthreads();
+      if (valid) {
+        uint32_t pos = base_off[d] + __popcll(peers & lt);
+        for (int w = 0; w < wave; ++w) pos += wcount[w][d];
+        kb[pos] = key;
+        rb[pos] = val;
+      }
+      __syncthreads();
+      uint32_t add = 0;
+#pragma unroll
+      for (int w = 0; w < kThreads / 64; ++w) add += wcount[w][threadIdx.x];
+      base_off[threadIdx.x] += add;
+      __syncthreads();
+    }
+    uint64_t* kt = ka;
+    ka = kb;
+    kb = kt;
+    int32_t* rt = ra;
+    ra = rb;
+    rb = rt;
+  }
+  if (ka != keys) {  // an odd number of passes: copy back
+    for (int64_t i = threadIdx.x; i < n; i += kThreads) {
+      keys[i] = ka[i];
+      rows[i] = ra[i];
+    }
   }
 }
 
@@ -314,14 +448,6 @@ __global__ __launch_bounds__(kThreads) void table_lookup(TableRef t, const int4*
                       make_key(uint32_t(c.x), uint32_t(c.y), uint32_t(c.z), uint32_t(c.w)));
 }
 
-__global__ void header_init(HashHeader* hdr) {
-  hdr->flags = 0;
-  hdr->nblocks = 0;
-  hdr->cap_mask = 15;
-  hdr->shift = 60;
-  hdr->or_bits = 0ull;
-  hdr->and_bits = ~0ull;
-}
 
 inline unsigned grid_for(int64_t n, int per_block) { return unsigned((n + per_block - 1) / per_block); }
 
@@ -335,22 +461,26 @@ int64_t pack_partials(int64_t n) {
 
 hipError_t launch_pack(const int32_t* coords, int64_t n, uint64_t* keys, int32_t* rows,
                        unsigned long long* part, HashHeader* hdr, hipStream_t st) {
-  header_init<<<1, 1, 0, st>>>(hdr);
-  if (n > 0) {
-    const int nb = int(pack_partials(n));
-    pack_keys<<<nb, kThreads, 0, st>>>(reinterpret_cast<const int4*>(coords), n, keys, rows, part, hdr);
-    reduce_bits<<<1, kThreads, 0, st>>>(part, nb, hdr);
-  }
+  const int nb = n > 0 ? int(pack_partials(n)) : 0;
+  if (n > 0)
+    pack_keys<<<nb, kThreads, 0, st>>>(reinterpret_cast<const int4*>(coords), n, keys, rows, part);
+  reduce_bits<<<1, kThreads, 0, st>>>(part, nb, hdr);
   return hipGetLastError();
 }
 
-hipError_t launch_sort_pass(const uint64_t* kin, const int32_t* vin, uint64_t* kout, int32_t* vout,
-                            int64_t n, const DigitSel& sel, uint32_t* counts, uint32_t* totals,
-                            hipStream_t st) {
+hipError_t launch_sort(uint64_t* keys0, int32_t* rows0, uint64_t* keys1, int32_t* rows1, int64_t n,
+                       const HashHeader* hdr, uint32_t* counts, uint32_t* totals, hipStream_t st) {
   const int64_t nb = sort_blocks(n);
-  radix_hist<<<unsigned(nb), kThreads, 0, st>>>(kin, n, sel, counts);
-  radix_colscan<<<256, kThreads, 0, st>>>(counts, int(nb), totals);
-  radix_scatter<<<unsigned(nb), kThreads, 0, st>>>(kin, vin, kout, vout, n, sel, counts, totals);
+  uint64_t* k[2] = {keys0, keys1};
+  int32_t* r[2] = {rows0, rows1};
+  for (int pass = 0; pass < 3; ++pass) {
+    const int a = pass & 1;  // 0 -> 1 -> 0 -> 1
+    radix_hist<<<unsigned(nb), kThreads, 0, st>>>(k[a], n, hdr, pass, counts);
+    radix_colscan<<<kMaxBuckets, kThreads, 0, st>>>(counts, int(nb), hdr, pass, totals);
+    radix_scatter<<<unsigned(nb), kThreads, 0, st>>>(k[a], r[a], k[a ^ 1], r[a ^ 1], n, hdr, pass, counts,
+                                                     totals);
+  }
+  radix_rest<<<1, kThreads, 0, st>>>(keys1, rows1, keys0, rows0, n, hdr);
   return hipGetLastError();
 }
 

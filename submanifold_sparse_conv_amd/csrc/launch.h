@@ -9,23 +9,17 @@
 
 namespace trsc {
 
-// Radix digit of one sort pass: bits key[pos[0]], ..., key[pos[nbits-1]],
-// least significant first. The positions are the bits that differ between keys.
-struct DigitSel {
-  uint8_t pos[8];
-  int32_t nbits;
-};
-
 int64_t sort_blocks(int64_t n);    // radix-sort workgroups (tiles) for n keys
-int64_t pack_partials(int64_t n);  // OR/AND partial pairs written by the packing pass
+int64_t pack_partials(int64_t n);  // partial triples (OR, AND, range flag) of the packing pass
+constexpr int kSortBuckets = 1 << kMaxDigitBits;
+// Packs keys / rows and initialises the header (flags, digits of the sort).
 hipError_t launch_pack(const int32_t* coords, int64_t n, uint64_t* keys, int32_t* rows,
                        unsigned long long* part, HashHeader* hdr, hipStream_t st);
-hipError_t launch_sort_pass(const uint64_t* kin, const int32_t* vin, uint64_t* kout, int32_t* vout,
-                            int64_t n, const DigitSel& sel, uint32_t* counts, uint32_t* totals,
-                            hipStream_t st);
-// Block table from the sorted keys: count blocks, size the table on the device
-// (capacity <= max_cap), clear it, insert one slot per block. Also flags
-// duplicate coordinates.
+// Three LSD radix passes (digits from the header) keys0 -> keys1 -> keys0 ->
+// keys1, then the single-workgroup pass over any further bits: the sorted keys
+// and rows end in keys1 / rows1. counts: sort_blocks(n) * kSortBuckets words.
+hipError_t launch_sort(uint64_t* keys0, int32_t* rows0, uint64_t* keys1, int32_t* rows1, int64_t n,
+                       const HashHeader* hdr, uint32_t* counts, uint32_t* totals, hipStream_t st);
 hipError_t launch_blocks(const uint64_t* keys, int64_t n, BlockSlot* slots, uint32_t max_cap,
                          uint32_t* part, HashHeader* hdr, hipStream_t st);
 hipError_t launch_lookup(const TableRef& t, const int32_t* q, int64_t nq, int32_t* out, hipStream_t st);
