@@ -268,6 +268,11 @@ def cpu_baseline(wl, target_s):
     }
 
 
+def note(msg):
+    """One progress line per finished phase, on stderr (the JSON line stays alone on stdout)."""
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
 def traffic_entry():
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it
     was taken on the current gather-GEMM source; else None."""
@@ -306,6 +311,7 @@ def main():
     for _ in range(args.warmup):
         path.step()
     torch.cuda.synchronize()
+    note(f"{args.warmup} warm-up steps done")
     M = pairs_of(path.nbr)
     assert bool((path.nbr[:, 13] == torch.arange(wl.n, device=dev, dtype=torch.int32)).all())
 
@@ -320,6 +326,7 @@ def main():
     ph = np.array([[evs[i][j].elapsed_time(evs[i][j + 1]) for j in range(4)] for i in range(args.steps)])
     t_hash, t_map, t_pack, t_gemm = ph.mean(axis=0)
     assert bool(torch.isfinite(path.y.float()).all())
+    note(f"{args.steps} timed steps: {ms_step:.4f} ms per step")
 
     flops = 2.0 * wl.c_in * wl.c_out * M
     gemm_tflops = flops / (t_gemm * 1e-3) / 1e12
@@ -388,14 +395,18 @@ def main():
                        "gemm_ms_steady": tss, "voxels_per_s_forward": wl2.n / (tss * 1e-3),
                        "effective_tflops": f2 / (tss * 1e-3) / 1e12}
         del p2, c2, x2, w2
+        note(f"config {name} measured")
     if extra:
         out["also"] = extra
     if not args.no_variants and wl.dtype == "bf16":
         out["variants"] = variants(sc, torch, wl, path, M, max(5, args.gemm_reps // 2))
+        note("variants measured")
     if not args.no_chain and args.config == "L":
         out["chain"] = layer_chain(sc, torch, wl, args.chain_blocks, args.chain_channels)
+        note("layer chain measured")
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+        note("cpu baseline measured")
     print(json.dumps(out), flush=True)
 
 
