@@ -13,8 +13,7 @@ namespace trsc {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kItems = 8;
-constexpr int kTile = kThreads * kItems;  // keys per sort block
+constexpr int kMaxSortWGs = 768;  // tiles per radix pass: keys per tile grow until n fits
 constexpr int kPackBlocks = 1024;         // grid of the key-packing pass
 
 __device__ inline unsigned long long wave_or(unsigned long long v) {
@@ -73,13 +72,19 @@ __global__ __launch_bounds__(kThreads) void pack_keys(const int4* __restrict__ c
 // Initialises the header: flags, an empty-table capacity, the OR / AND of all
 // keys, and the radix digits. The key bits that differ between keys (OR ^ AND)
 // are split, least significant first, into three digits of equal width (at
-// most kMaxDigitBits); any further bits go to the single-workgroup pass.
+// most kMaxDigitBits); any further bits go to the single-workgroup pass. The
+// header is assembled in LDS (varying bit b, of rank r among them, is written
+// by thread b) and copied out in 4-byte words.
 __global__ __launch_bounds__(kThreads) void reduce_bits(const unsigned long long* __restrict__ part,
                                                         int nparts, HashHeader* hdr) {
+  static_assert(sizeof(HashHeader) % 4 == 0 && sizeof(HashHeader) / 4 <= kThreads, "header copy");
+  constexpr int HW = int(sizeof(HashHeader) / 4);
   __shared__ unsigned long long s_or[kThreads / 64], s_and[kThreads / 64];
   __shared__ unsigned long long s_bad[kThreads / 64];
+  __shared__ HashHeader s_h;
+  const int tid = threadIdx.x;
   unsigned long long k_or = 0, k_and = ~0ull, bad = 0;
-  for (int i = threadIdx.x; i < nparts; i += kThreads) {
+  for (int i = tid; i < nparts; i += kThreads) {
     k_or |= part[3 * i];
     k_and &= part[3 * i + 1];
     bad |= part[3 * i + 2];
@@ -87,42 +92,45 @@ __global__ __launch_bounds__(kThreads) void reduce_bits(const unsigned long long
   k_or = wave_or(k_or);
   k_and = wave_and(k_and);
   bad = wave_or(bad);
-  if ((threadIdx.x & 63) == 0) {
-    s_or[threadIdx.x >> 6] = k_or;
-    s_and[threadIdx.x >> 6] = k_and;
-    s_bad[threadIdx.x >> 6] = bad;
+  if ((tid & 63) == 0) {
+    s_or[tid >> 6] = k_or;
+    s_and[tid >> 6] = k_and;
+    s_bad[tid >> 6] = bad;
+  }
+  if (tid < HW) reinterpret_cast<uint32_t*>(&s_h)[tid] = 0u;
+  __syncthreads();
+  k_or = s_or[0], k_and = s_and[0], bad = s_bad[0];
+  for (int w = 1; w < kThreads / 64; ++w) {
+    k_or |= s_or[w];
+    k_and &= s_and[w];
+    bad |= s_bad[w];
+  }
+  const unsigned long long vary = nparts > 0 ? (k_or ^ k_and) : 0ull;
+  const int nv = __popcll(vary);
+  int w = (nv + 2) / 3;
+  if (w > kMaxDigitBits) w = kMaxDigitBits;
+  if (tid < 64 && ((vary >> tid) & 1ull)) {  // then w >= 1
+    const int r = __popcll(vary & ((1ull << tid) - 1ull));
+    if (r < 3 * w)
+      s_h.digit[r / w].pos[r % w] = uint8_t(tid);
+    else
+      s_h.rest_pos[r - 3 * w] = uint8_t(tid);
+  }
+  if (tid == 0) {
+    s_h.flags = bad ? kFlagCoordRange : 0u;
+    s_h.nblocks = 0;
+    s_h.cap_mask = 15;
+    s_h.shift = 60;
+    s_h.or_bits = k_or;
+    s_h.and_bits = k_and;
+    for (int d = 0; d < 3; ++d) {
+      const int left = nv - d * w;
+      s_h.digit[d].nbits = left < 0 ? 0 : (left > w ? w : left);
+    }
+    s_h.rest_n = nv > 3 * w ? nv - 3 * w : 0;
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    for (int w = 1; w < kThreads / 64; ++w) {
-      k_or |= s_or[w];
-      k_and &= s_and[w];
-      bad |= s_bad[w];
-    }
-    HashHeader h{};
-    h.flags = bad ? kFlagCoordRange : 0u;
-    h.nblocks = 0;
-    h.cap_mask = 15;
-    h.shift = 60;
-    h.or_bits = k_or;
-    h.and_bits = k_and;
-    const unsigned long long vary = nparts > 0 ? (k_or ^ k_and) : 0ull;
-    const int nv = __popcll(vary);
-    int w = (nv + 2) / 3;
-    if (w > kMaxDigitBits) w = kMaxDigitBits;
-    int b = 0;
-    for (int d = 0; d < 3; ++d) {
-      h.digit[d].nbits = 0;
-      while (h.digit[d].nbits < w && b < 64) {
-        if ((vary >> b) & 1ull) h.digit[d].pos[h.digit[d].nbits++] = uint8_t(b);
-        ++b;
-      }
-    }
-    h.rest_n = 0;
-    for (; b < 64; ++b)
-      if ((vary >> b) & 1ull) h.rest_pos[h.rest_n++] = uint8_t(b);
-    *hdr = h;
-  }
+  if (tid < HW) reinterpret_cast<uint32_t*>(hdr)[tid] = reinterpret_cast<const uint32_t*>(&s_h)[tid];
 }
 
 __device__ inline uint32_t digit_of(uint64_t key, const uint8_t* pos, int nbits) {
@@ -132,9 +140,11 @@ __device__ inline uint32_t digit_of(uint64_t key, const uint8_t* pos, int nbits)
 }
 
 constexpr int kMaxBuckets = 1 << kMaxDigitBits;
+constexpr int kColscanWGs = 1024;  // radix_colscan workgroups (each scans digits g, g + 1024, ...)
 
 // counts[d * nblocks + block] = number of keys of this block's tile with digit d
 // (d below 2^nbits of the pass's digit).
+template <int ITEMS>
 __global__ __launch_bounds__(kThreads) void radix_hist(const uint64_t* __restrict__ keys, int64_t n,
                                                        const HashHeader* __restrict__ hdr, int pass,
                                                        uint32_t* __restrict__ counts) {
@@ -145,8 +155,8 @@ __global__ __launch_bounds__(kThreads) void radix_hist(const uint64_t* __restric
   if (threadIdx.x < 12) s_pos[threadIdx.x] = hdr->digit[pass].pos[threadIdx.x];
   for (int d = threadIdx.x; d < nb; d += kThreads) h[d] = 0;
   __syncthreads();
-  const int64_t base = int64_t(blockIdx.x) * kTile;
-  for (int it = 0; it < kItems; ++it) {
+  const int64_t base = int64_t(blockIdx.x) * (kThreads * ITEMS);
+  for (int it = 0; it < ITEMS; ++it) {
     const int64_t i = base + it * kThreads + threadIdx.x;
     if (i < n) atomicAdd(&h[digit_of(keys[i], s_pos, nbits)], 1u);
   }
@@ -174,31 +184,36 @@ __device__ inline uint32_t block_exclusive_scan(uint32_t v, uint32_t* s_tmp, uin
   return before + x - v;
 }
 
-// One workgroup per digit d: exclusive scan over blocks of counts[d][*] in
-// place; totals[d] = number of keys with digit d (0 for digits the pass lacks).
+// Workgroup g scans digits g, g + gridDim.x, ...: exclusive scan over blocks
+// of counts[d][*] in place; totals[d] = number of keys with digit d (0 for
+// digits the pass lacks).
 __global__ __launch_bounds__(kThreads) void radix_colscan(uint32_t* __restrict__ counts, int nblocks,
                                                           const HashHeader* __restrict__ hdr, int pass,
                                                           uint32_t* __restrict__ totals) {
   __shared__ uint32_t s_tmp[kThreads / 64];
-  if (int(blockIdx.x) >= (1 << hdr->digit[pass].nbits)) {
-    if (threadIdx.x == 0) totals[blockIdx.x] = 0;
-    return;
+  const int nb = 1 << hdr->digit[pass].nbits;
+  for (int d = blockIdx.x; d < kMaxBuckets; d += gridDim.x) {
+    if (d >= nb) {
+      if (threadIdx.x == 0) totals[d] = 0;
+      continue;
+    }
+    uint32_t* col = counts + int64_t(d) * nblocks;
+    uint32_t carry = 0;
+    for (int b0 = 0; b0 < nblocks; b0 += kThreads) {
+      const int b = b0 + threadIdx.x;
+      const uint32_t v = b < nblocks ? col[b] : 0u;
+      uint32_t tot;
+      const uint32_t ex = block_exclusive_scan(v, s_tmp, &tot);
+      if (b < nblocks) col[b] = carry + ex;
+      carry += tot;
+    }
+    if (threadIdx.x == 0) totals[d] = carry;
   }
-  uint32_t* col = counts + int64_t(blockIdx.x) * nblocks;
-  uint32_t carry = 0;
-  for (int b0 = 0; b0 < nblocks; b0 += kThreads) {
-    const int b = b0 + threadIdx.x;
-    const uint32_t v = b < nblocks ? col[b] : 0u;
-    uint32_t tot;
-    const uint32_t ex = block_exclusive_scan(v, s_tmp, &tot);
-    if (b < nblocks) col[b] = carry + ex;
-    carry += tot;
-  }
-  if (threadIdx.x == 0) totals[blockIdx.x] = carry;
 }
 
 // Stable scatter of one radix pass. Inside a tile, key order is (iteration,
 // wave, lane); ranks among equal digits follow that order.
+template <int ITEMS>
 __global__ __launch_bounds__(kThreads) void radix_scatter(const uint64_t* __restrict__ kin,
                                                           const int32_t* __restrict__ vin,
                                                           uint64_t* __restrict__ kout,
@@ -232,8 +247,8 @@ __global__ __launch_bounds__(kThreads) void radix_scatter(const uint64_t* __rest
     run += loc[q];
   }
   const unsigned long long lt = (1ull << lane) - 1ull;
-  const int64_t base = int64_t(blockIdx.x) * kTile;
-  for (int it = 0; it < kItems; ++it) {
+  const int64_t base = int64_t(blockIdx.x) * (kThreads * ITEMS);
+  for (int it = 0; it < ITEMS; ++it) {
     for (int d = threadIdx.x; d < nb; d += kThreads)
 #pragma unroll
       for (int w = 0; w < kThreads / 64; ++w) wcount[w][d] = 0;
@@ -453,7 +468,17 @@ inline unsigned grid_for(int64_t n, int per_block) { return unsigned((n + per_bl
 
 }  // namespace
 
-int64_t sort_blocks(int64_t n) { return (n + kTile - 1) / kTile; }
+// Keys per radix tile: kThreads times the smallest power of two (<= 32) that
+// keeps a pass at no more than kMaxSortWGs workgroups.
+int sort_items(int64_t n) {
+  int it = 1;
+  while (it < 32 && (n + int64_t(kThreads) * it - 1) / (int64_t(kThreads) * it) > kMaxSortWGs) it *= 2;
+  return it;
+}
+int64_t sort_blocks(int64_t n) {
+  const int64_t tile = int64_t(kThreads) * sort_items(n);
+  return (n + tile - 1) / tile;
+}
 int64_t pack_partials(int64_t n) {
   const int64_t b = (n + kThreads - 1) / kThreads;
   return b < 1 ? 1 : (b < kPackBlocks ? b : kPackBlocks);
@@ -473,12 +498,27 @@ hipError_t launch_sort(uint64_t* keys0, int32_t* rows0, uint64_t* keys1, int32_t
   const int64_t nb = sort_blocks(n);
   uint64_t* k[2] = {keys0, keys1};
   int32_t* r[2] = {rows0, rows1};
+  const int items = sort_items(n);
   for (int pass = 0; pass < 3; ++pass) {
     const int a = pass & 1;  // 0 -> 1 -> 0 -> 1
-    radix_hist<<<unsigned(nb), kThreads, 0, st>>>(k[a], n, hdr, pass, counts);
-    radix_colscan<<<kMaxBuckets, kThreads, 0, st>>>(counts, int(nb), hdr, pass, totals);
-    radix_scatter<<<unsigned(nb), kThreads, 0, st>>>(k[a], r[a], k[a ^ 1], r[a ^ 1], n, hdr, pass, counts,
-                                                     totals);
+    switch (items) {
+#define TRSC_RADIX_PASS(IT)                                                                                   \
+  case IT:                                                                                                    \
+    radix_hist<IT><<<unsigned(nb), kThreads, 0, st>>>(k[a], n, hdr, pass, counts);                            \
+    radix_colscan<<<kColscanWGs, kThreads, 0, st>>>(counts, int(nb), hdr, pass, totals);                      \
+    radix_scatter<IT><<<unsigned(nb), kThreads, 0, st>>>(k[a], r[a], k[a ^ 1], r[a ^ 1], n, hdr, pass, counts, \
+                                                         totals);                                             \
+    break;
+      TRSC_RADIX_PASS(1)
+      TRSC_RADIX_PASS(2)
+      TRSC_RADIX_PASS(4)
+      TRSC_RADIX_PASS(8)
+      TRSC_RADIX_PASS(16)
+      TRSC_RADIX_PASS(32)
+#undef TRSC_RADIX_PASS
+      default:
+        return hipErrorInvalidValue;
+    }
   }
   radix_rest<<<1, kThreads, 0, st>>>(keys1, rows1, keys0, rows0, n, hdr);
   return hipGetLastError();
