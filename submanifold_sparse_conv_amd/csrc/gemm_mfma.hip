@@ -41,72 +41,6 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
 
-// wp[k][co][ci] = w[k][ci][co], through 64 x 64 LDS tiles; the first
-// workgroup also writes the 256 zero bytes after the packed weights (the copy
-// source of absent neighbours and of channels past c_in).
-__global__ __launch_bounds__(kThreads) void pack_weights(const uint16_t* __restrict__ w,
-                                                         uint16_t* __restrict__ wp, int c_in,
-                                                         int c_out, uint16_t* __restrict__ zeros) {
-  __shared__ uint16_t t[64][65];
-  if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && threadIdx.x < 16)
-    reinterpret_cast<uint4*>(zeros)[threadIdx.x] = make_uint4(0u, 0u, 0u, 0u);
-  const int k = blockIdx.z;
-  const int ci0 = blockIdx.y * 64, co0 = blockIdx.x * 64;
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-  const uint16_t* src = w + int64_t(k) * c_in * c_out;
-  uint16_t* dst = wp + int64_t(k) * c_in * c_out;
-  for (int y = ty; y < 64; y += 4) {
-    const int ci = ci0 + y, co = co0 + tx;
-    t[y][tx] = (ci < c_in && co < c_out) ? src[int64_t(ci) * c_out + co] : uint16_t(0);
-  }
-  __syncthreads();
-  for (int y = ty; y < 64; y += 4) {
-    const int co = co0 + y, ci = ci0 + tx;
-    if (co < c_out && ci < c_in) dst[int64_t(co) * c_in + ci] = t[tx][y];
-  }
-}
-
-// The same transpose with 16-byte accesses, for channel counts that are
-// multiples of 8 and 16-byte aligned arrays: a thread moves two 8-channel
-// pieces in, through a 64 x 66 LDS tile (4-byte words, rows 132 bytes apart so
-// that the column reads spread over the banks), and two pieces out.
-__global__ __launch_bounds__(kThreads) void pack_weights_v8(const uint16_t* __restrict__ w,
-                                                            uint16_t* __restrict__ wp, int c_in,
-                                                            int c_out, uint16_t* __restrict__ zeros) {
-  __shared__ uint32_t t[64 * 33];
-  if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && threadIdx.x < 16)
-    reinterpret_cast<uint4*>(zeros)[threadIdx.x] = make_uint4(0u, 0u, 0u, 0u);
-  const int k = blockIdx.z;
-  const int ci0 = blockIdx.y * 64, co0 = blockIdx.x * 64;
-  const uint16_t* src = w + int64_t(k) * c_in * c_out;
-  uint16_t* dst = wp + int64_t(k) * c_in * c_out;
-#pragma unroll
-  for (int m = 0; m < 2; ++m) {
-    const int q = threadIdx.x + kThreads * m;
-    const int r = q >> 3, c8 = q & 7;
-    const int ci = ci0 + r, co = co0 + 8 * c8;
-    uint4 v = make_uint4(0u, 0u, 0u, 0u);
-    if (ci < c_in && co < c_out) v = *reinterpret_cast<const uint4*>(src + int64_t(ci) * c_out + co);
-    uint32_t* row = t + r * 33 + 4 * c8;
-    row[0] = v.x, row[1] = v.y, row[2] = v.z, row[3] = v.w;
-  }
-  __syncthreads();
-  const uint16_t* th = reinterpret_cast<const uint16_t*>(t);
-#pragma unroll
-  for (int m = 0; m < 2; ++m) {
-    const int q = threadIdx.x + kThreads * m;
-    const int r = q >> 3, c8 = q & 7;
-    const int co = co0 + r, ci = ci0 + 8 * c8;
-    if (co < c_out && ci < c_in) {
-      uint32_t o[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-        o[u] = uint32_t(th[(8 * c8 + 2 * u) * 66 + r]) | (uint32_t(th[(8 * c8 + 2 * u + 1) * 66 + r]) << 16);
-      *reinterpret_cast<uint4*>(dst + int64_t(co) * c_in + ci) = make_uint4(o[0], o[1], o[2], o[3]);
-    }
-  }
-}
-
 // The two half types of the matrix cores: their MFMA and conversions.
 template <bool F16>
 struct Half;
@@ -436,20 +370,6 @@ hipError_t dispatch(const ConvArgs& a, const uint16_t* p, const uint16_t* zeros,
 }
 
 }  // namespace
-
-hipError_t launch_pack_weights(const void* w, void* wp, int c_in, int c_out, hipStream_t st) {
-  dim3 grid(unsigned((c_out + 63) / 64), unsigned((c_in + 63) / 64), 27);
-  const uint16_t* src = static_cast<const uint16_t*>(w);
-  uint16_t* dst = static_cast<uint16_t*>(wp);
-  uint16_t* zeros = dst + packed_weight_elems(c_in, c_out);
-  const bool v8 = c_in % 8 == 0 && c_out % 8 == 0 && reinterpret_cast<uintptr_t>(w) % 16 == 0 &&
-                  reinterpret_cast<uintptr_t>(wp) % 16 == 0;
-  if (v8)
-    pack_weights_v8<<<grid, kThreads, 0, st>>>(src, dst, c_in, c_out, zeros);
-  else
-    pack_weights<<<grid, kThreads, 0, st>>>(src, dst, c_in, c_out, zeros);
-  return hipGetLastError();
-}
 
 hipError_t launch_forward_mfma(const ConvArgs& a, const void* wp, hipStream_t st) {
   const uint16_t* p = static_cast<const uint16_t*>(wp);
