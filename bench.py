@@ -292,8 +292,8 @@ def main():
         copy_probe(args.copy_probe_mib)
         return
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); multi-GPU "
-              "sharding of this path is described in DESIGN.md but not built.", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the path is built "
+              "and measured for a single GPU; sharding it across GPUs is not built.", file=sys.stderr)
         sys.exit(2)
     import torch
     import submanifold_sparse_conv_amd as sc
