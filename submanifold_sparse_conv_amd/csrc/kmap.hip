@@ -157,12 +157,21 @@ __global__ __launch_bounds__(kGroupThreads) void group_rows(const int32_t* __res
   __syncthreads();
   for (int64_t t = w0 + tid; t < w1; t += kGroupThreads) atomicAdd(&hist[octant_key(mask[t])], 1u);
   __syncthreads();
-  if (tid == 0) {
-    uint32_t run = 0;
-    for (int d = 0; d < 256; ++d) {
-      base_off[d] = run;
-      run += hist[d];
+  if (tid < 256) {  // exclusive scan of the histogram: four waves, then their totals
+    const uint32_t v = hist[tid];
+    uint32_t x = v;
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t y = __shfl_up(x, o, 64);
+      if (lane >= o) x += y;
     }
+    if (lane == 63) wcount[0][wave] = x;
+    base_off[tid] = x - v;
+  }
+  __syncthreads();
+  if (tid < 256) {
+    uint32_t before = 0;
+    for (int w = 0; w < wave; ++w) before += wcount[0][w];
+    base_off[tid] += before;
   }
   __syncthreads();
   const unsigned long long lt = (1ull << lane) - 1ull;
