@@ -161,6 +161,33 @@ def test_deterministic_bits(name):
     assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
 
 
+def test_shared_map_on_two_streams():
+    # A kernel map is read-only once built: forwards on two streams over one map
+    # (different weights, running concurrently) give the bits of sequential runs.
+    wl = workload("S", 300, "shuffled")
+    say(f"[streams] config=S n={wl.n}")
+    c, x, w = to_dev(wl)
+    m = sc.build_kernel_map(sc.build_hash(c))
+    w2 = (w.float() * -0.5).to(w.dtype)
+    wp1, wp2 = sc.pack_weights(w), sc.pack_weights(w2)
+    torch.cuda.synchronize()
+    ref1 = sc.forward_packed(m, x, wp1)
+    ref2 = sc.forward_packed(m, x, wp2)
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    outs = []
+    for _ in range(3):
+        with torch.cuda.stream(s1):
+            a = sc.forward_packed(m, x, wp1)
+        with torch.cuda.stream(s2):
+            b = sc.forward_packed(m, x, wp2)
+        outs.append((a, b))
+    torch.cuda.synchronize()
+    for a, b in outs:
+        assert torch.equal(a.view(torch.int16), ref1.view(torch.int16))
+        assert torch.equal(b.view(torch.int16), ref2.view(torch.int16))
+
+
 def test_translation_invariance():
     wl = workload("S", 200, "raster")
     say("[translation] config=S")
