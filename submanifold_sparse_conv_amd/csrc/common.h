@@ -102,30 +102,31 @@ __host__ __device__ inline uint32_t home_slot(uint64_t bkey, uint32_t shift) {
 }
 
 // Occupancy bitmap and start of block `bkey` (bits = 0 when it is absent),
-// continuing a probe run whose first slot s is already loaded in (v0, v1).
+// continuing a probe run whose first slot s is already loaded: its first 16
+// bytes (key, bitmap) in v0 and its start in start0.
 __device__ inline void block_probe_from(const BlockSlot* slots, uint32_t mask, uint64_t bkey, uint32_t s,
-                                        uint4 v0, uint4 v1, uint64_t& bits, uint32_t& start) {
+                                        uint4 v0, uint32_t start0, uint64_t& bits, uint32_t& start) {
   bits = 0;
   start = 0;
   for (uint32_t probe = 0; probe <= mask; ++probe) {
     const uint64_t k = uint64_t(v0.x) | (uint64_t(v0.y) << 32);
     if (k == bkey) {
       bits = uint64_t(v0.z) | (uint64_t(v0.w) << 32);
-      start = v1.x;
+      start = start0;
       return;
     }
     if (k == kEmptyKey) return;
     s = (s + 1) & mask;
-    v0 = reinterpret_cast<const uint4*>(slots + s)[0];
-    v1 = reinterpret_cast<const uint4*>(slots + s)[1];
+    v0 = *reinterpret_cast<const uint4*>(slots + s);
+    start0 = slots[s].start;
   }
 }
 
 __device__ inline void block_find(const BlockSlot* slots, uint32_t mask, uint32_t shift, uint64_t bkey,
                                   uint64_t& bits, uint32_t& start) {
   const uint32_t s = home_slot(bkey, shift) & mask;
-  block_probe_from(slots, mask, bkey, s, reinterpret_cast<const uint4*>(slots + s)[0],
-                   reinterpret_cast<const uint4*>(slots + s)[1], bits, start);
+  block_probe_from(slots, mask, bkey, s, *reinterpret_cast<const uint4*>(slots + s), slots[s].start, bits,
+                   start);
 }
 
 // Cell index (0..63) of the in-block coordinates (x, y, z in 0..3): the low

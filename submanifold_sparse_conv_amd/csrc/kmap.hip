@@ -43,14 +43,31 @@ __device__ inline uint64_t block_move(uint64_t bkey, uint64_t amask, uint64_t lo
   return rest | (((d | ~amask) + low) & amask);
 }
 
+// Cell bits (of cell_of) contributed by one in-block coordinate on each axis.
+__device__ inline uint32_t cell_x(int x) { return (uint32_t(x & 1) << 2) | (uint32_t(x >> 1) << 5); }
+__device__ inline uint32_t cell_y(int y) { return (uint32_t(y & 1) << 1) | (uint32_t(y >> 1) << 4); }
+__device__ inline uint32_t cell_z(int z) { return uint32_t(z & 1) | (uint32_t(z >> 1) << 3); }
+
+// Each wave works alone (no workgroup barrier): its LDS region first holds,
+// for each lane, the {bitmap, start} record of each of the 8 blocks around the
+// voxel (record j of lane l at j * 64 + l), which turns the per-tap choice of
+// block into one indexed LDS read; the same bytes then stage the wave's 64 x
+// 27 output rows and their caller rows for the write-back.
 __global__ __launch_bounds__(kThreads) void kmap_kernel(const uint64_t* __restrict__ skeys, int64_t n,
                                                         TableRef t, int32_t* __restrict__ nbr,
                                                         uint32_t* __restrict__ mask_out) {
-  __shared__ int32_t res[kThreads * 27];  // odd stride: conflict-free both ways
-  __shared__ int32_t rows[kThreads];
-  const int64_t base = int64_t(xcd_remap(blockIdx.x, gridDim.x)) * kThreads;
-  const int64_t s = base + threadIdx.x;
+  constexpr int kWaves = kThreads / 64;
+  static_assert(64 * 27 * 4 + 64 * 4 <= 8 * 64 * 16, "staged rows fit in the record region");
+  __shared__ uint4 lds[kWaves][8 * 64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint4* rec = lds[wave];
+  int32_t* res = reinterpret_cast<int32_t*>(lds[wave]);  // [64][27]: odd stride, conflict-free
+  int32_t* rows = res + 64 * 27;
+  const int64_t base = int64_t(xcd_remap(blockIdx.x, gridDim.x)) * kThreads + wave * 64;
+  if (base >= n) return;
+  const int64_t s = base + lane;
   const uint32_t tmask = t.hdr->cap_mask, tshift = t.hdr->shift;
+  int32_t got[27];
   if (s < n) {
     const uint64_t key = skeys[s];
     const int32_t me = t.srows[s];
@@ -64,65 +81,116 @@ __global__ __launch_bounds__(kThreads) void kmap_kernel(const uint64_t* __restri
     const int dx = lx == 0 ? -1 : (lx == 3 ? 1 : 0);
     const int dy = ly == 0 ? -1 : (ly == 3 ? 1 : 0);
     const int dz = lz == 0 ? -1 : (lz == 3 ? 1 : 0);
-    bool okx = false, oky = false, okz = false;
+    bool okx = false;
     const uint64_t kx = dx ? block_move(bkey, kBMaskX, 4, dx, okx) : bkey;
     // Blocks (ix, iy, iz) in {0,1}^3: index 1 on an axis is the next block on
-    // that side. Probe the needed ones together (their loads overlap).
-    uint64_t bbits[8];
-    uint32_t bstart[8];
+    // that side (block 0 is the voxel's own). The home slots of all eight are
+    // loaded in straight-line code, so that the loads are in flight together
+    // (a block the voxel does not need reads its own block's slot, and the
+    // result is dropped); the rare probe run that goes past its home slot is
+    // finished afterwards.
+    uint64_t bk[8];
+    bool need[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int ix = (j >> 2) & 1, iy = (j >> 1) & 1, iz = j & 1;
-      bool need = (!ix || (dx && okx)) && (!iy || dy) && (!iz || dz);
-      uint64_t bk = ix ? kx : bkey;
-      if (need && iy) {
+      bool nd = (!ix || (dx && okx)) && (!iy || dy) && (!iz || dz);
+      uint64_t b = ix ? kx : bkey;
+      if (nd && iy) {
         bool ok;
-        bk = block_move(bk, kBMaskY, 2, dy, ok);
-        need = ok;
+        b = block_move(b, kBMaskY, 2, dy, ok);
+        nd = ok;
       }
-      if (need && iz) {
+      if (nd && iz) {
         bool ok;
-        bk = block_move(bk, kBMaskZ, 1, dz, ok);
-        need = ok;
+        b = block_move(b, kBMaskZ, 1, dz, ok);
+        nd = ok;
       }
-      bbits[j] = 0;
-      bstart[j] = 0;
-      if (need) {
-        const uint32_t hs = home_slot(bk, tshift) & tmask;
-        const uint4 v0 = reinterpret_cast<const uint4*>(t.slots + hs)[0];
-        const uint4 v1 = reinterpret_cast<const uint4*>(t.slots + hs)[1];
-        block_probe_from(t.slots, tmask, bk, hs, v0, v1, bbits[j], bstart[j]);
-      }
+      bk[j] = b;
+      need[j] = nd;
     }
-    // The 27 neighbours: bit test in the block's bitmap, then the sorted
-    // position start + popcount and its caller row.
+    const uint32_t hs0 = home_slot(bkey, tshift) & tmask;
+    uint4 v0[8];
+    uint32_t st0[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t h = need[j] ? home_slot(bk[j], tshift) & tmask : hs0;
+      v0[j] = *reinterpret_cast<const uint4*>(t.slots + h);
+      st0[j] = t.slots[h].start;
+    }
+    uint64_t bbits[8];
+    uint32_t bstart[8];
+    uint32_t longer = 0;  // blocks whose home slot holds another key
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint64_t k = uint64_t(v0[j].x) | (uint64_t(v0[j].y) << 32);
+      const bool hit = need[j] && k == bk[j];
+      bbits[j] = hit ? (uint64_t(v0[j].z) | (uint64_t(v0[j].w) << 32)) : 0ull;
+      bstart[j] = hit ? st0[j] : 0u;
+      longer |= uint32_t(need[j] && !hit && k != kEmptyKey) << j;
+    }
+    if (longer) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if ((longer >> j) & 1u) block_find(t.slots, tmask, tshift, bk[j], bbits[j], bstart[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      rec[j * 64 + lane] = uint4{uint32_t(bbits[j]), uint32_t(bbits[j] >> 32), bstart[j], 0u};
+
+    // The 27 neighbours: the record of the tap's block (an offset per axis:
+    // the neighbour block on the side the tap leaves by), a bit test in its
+    // bitmap, then the sorted position start + popcount.
+    const int rxm = dx < 0 ? 4 * 64 : 0, rxp = dx > 0 ? 4 * 64 : 0;
+    const int rym = dy < 0 ? 2 * 64 : 0, ryp = dy > 0 ? 2 * 64 : 0;
+    const int rzm = dz < 0 ? 64 : 0, rzp = dz > 0 ? 64 : 0;
+    const uint32_t cx[3] = {cell_x((lx + 3) & 3), cell_x(lx), cell_x((lx + 1) & 3)};
+    const uint32_t cy[3] = {cell_y((ly + 3) & 3), cell_y(ly), cell_y((ly + 1) & 3)};
+    const uint32_t cz[3] = {cell_z((lz + 3) & 3), cell_z(lz), cell_z((lz + 1) & 3)};
     uint32_t msk = 0;
     int32_t spos[27];
 #pragma unroll
     for (int k = 0; k < 27; ++k) {
+      if (k == 13) continue;
       const int ox = k / 9 - 1, oy = (k / 3) % 3 - 1, oz = k % 3 - 1;
-      const int nx = lx + ox, ny = ly + oy, nz = lz + oz;
-      const int j = ((nx < 0 || nx > 3) ? 4 : 0) | ((ny < 0 || ny > 3) ? 2 : 0) | ((nz < 0 || nz > 3) ? 1 : 0);
-      const uint32_t c = cell_of(uint32_t(nx) & 3u, uint32_t(ny) & 3u, uint32_t(nz) & 3u);
-      const uint64_t bits = bbits[j];
-      spos[k] = ((bits >> c) & 1u) ? int32_t(bstart[j] + __popcll(bits & ((1ull << c) - 1ull))) : -1;
-      msk |= uint32_t(spos[k] >= 0) << k;
+      const int r = (ox < 0 ? rxm : ox > 0 ? rxp : 0) + (oy < 0 ? rym : oy > 0 ? ryp : 0) +
+                    (oz < 0 ? rzm : oz > 0 ? rzp : 0);
+      const uint4 e = rec[r + lane];
+      const uint64_t bits = uint64_t(e.x) | (uint64_t(e.y) << 32);
+      const uint32_t c = cx[ox + 1] | cy[oy + 1] | cz[oz + 1];
+      const uint32_t hit = uint32_t(bits >> c) & 1u;
+      // start + popcount, or -1 for a miss, without a branch
+      spos[k] = int32_t(e.z + __popcll(bits & ((1ull << c) - 1ull))) | (int32_t(hit) - 1);
+      msk |= hit << k;
     }
+    msk |= 1u << 13;
+    // Caller rows of the 26 neighbours, loaded together and unconditionally (a
+    // missing neighbour reads the voxel's own entry, and its result is
+    // dropped); positions are below 2^30, so a 32-bit byte offset from the
+    // row array reaches them.
+    const char* srow_bytes = reinterpret_cast<const char*>(t.srows);
 #pragma unroll
     for (int k = 0; k < 27; ++k) {
-      const int32_t r = k == 13 ? me : (spos[k] >= 0 ? t.srows[spos[k]] : -1);
-      res[threadIdx.x * 27 + k] = r;
+      if (k == 13) continue;
+      const uint32_t q = spos[k] >= 0 ? uint32_t(spos[k]) : uint32_t(s);
+      got[k] = *reinterpret_cast<const int32_t*>(srow_bytes + q * 4u);
     }
-    rows[threadIdx.x] = me;
+#pragma unroll
+    for (int k = 0; k < 27; ++k) got[k] = k == 13 ? me : (spos[k] >= 0 ? got[k] : -1);
     mask_out[s] = msk;
+    // Every lane of the wave has read its records (LDS executes a wave's
+    // instructions in order); the staging below reuses the bytes.
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+#pragma unroll
+    for (int k = 0; k < 27; ++k) res[lane * 27 + k] = got[k];
+    rows[lane] = me;
   }
-  __syncthreads();
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
   const int64_t left = n - base;
-  const int nvox = left < kThreads ? int(left) : kThreads;
-  for (int e = threadIdx.x; e < nvox * 27; e += kThreads) {
+  const int nv = left < 64 ? int(left) : 64;
+  for (int e = lane; e < nv * 27; e += 64) {
     const int v = e / 27;
-    const int k = e - v * 27;
-    nbr[int64_t(rows[v]) * 27 + k] = res[e];
+    nbr[int64_t(rows[v]) * 27 + (e - v * 27)] = res[e];
   }
 }
 
@@ -149,13 +217,30 @@ __global__ __launch_bounds__(kGroupThreads) void group_rows(const int32_t* __res
   constexpr int WAVES = kGroupThreads / 64;
   __shared__ uint32_t hist[256];
   __shared__ uint32_t base_off[256];
+  __shared__ uint32_t wtot[256 / 64];
   __shared__ uint32_t wcount[WAVES][256];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t w0 = int64_t(blockIdx.x) * kGroupWindow;
   const int64_t w1 = w0 + kGroupWindow < n ? w0 + kGroupWindow : n;
-  if (tid < 256) hist[tid] = 0;
+  // The window's masks and rows, loaded once (all loads in flight together).
+  constexpr int PER = kGroupWindow / kGroupThreads;
+  static_assert(PER * kGroupThreads == kGroupWindow, "window = whole passes of the workgroup");
+  uint32_t mv[PER];
+  int32_t rv[PER];
+#pragma unroll
+  for (int it = 0; it < PER; ++it) {
+    const int64_t t = w0 + it * kGroupThreads + tid;
+    mv[it] = t < w1 ? mask[t] : 0u;
+    rv[it] = t < w1 ? srows[t] : 0;
+  }
+  if (tid < 256) {
+    hist[tid] = 0;
+    for (int w = 0; w < WAVES; ++w) wcount[w][tid] = 0;
+  }
   __syncthreads();
-  for (int64_t t = w0 + tid; t < w1; t += kGroupThreads) atomicAdd(&hist[octant_key(mask[t])], 1u);
+#pragma unroll
+  for (int it = 0; it < PER; ++it)
+    if (w0 + it * kGroupThreads + tid < w1) atomicAdd(&hist[octant_key(mv[it])], 1u);
   __syncthreads();
   if (tid < 256) {  // exclusive scan of the histogram: four waves, then their totals
     const uint32_t v = hist[tid];
@@ -164,30 +249,23 @@ __global__ __launch_bounds__(kGroupThreads) void group_rows(const int32_t* __res
       const uint32_t y = __shfl_up(x, o, 64);
       if (lane >= o) x += y;
     }
-    if (lane == 63) wcount[0][wave] = x;
+    if (lane == 63) wtot[wave] = x;
     base_off[tid] = x - v;
   }
   __syncthreads();
   if (tid < 256) {
     uint32_t before = 0;
-    for (int w = 0; w < wave; ++w) before += wcount[0][w];
+    for (int w = 0; w < wave; ++w) before += wtot[w];
     base_off[tid] += before;
   }
   __syncthreads();
   const unsigned long long lt = (1ull << lane) - 1ull;
-  for (int64_t r0 = w0; r0 < w1; r0 += kGroupThreads) {
-    if (tid < 256)
-      for (int w = 0; w < WAVES; ++w) wcount[w][tid] = 0;
-    __syncthreads();
-    const int64_t t = r0 + tid;
+#pragma unroll
+  for (int it = 0; it < PER; ++it) {
+    const int64_t t = w0 + it * kGroupThreads + tid;
     const bool valid = t < w1;
-    uint32_t m = 0, d = 0;
-    int32_t row = 0;
-    if (valid) {
-      m = mask[t];
-      row = srows[t];
-      d = octant_key(m);
-    }
+    const uint32_t m = mv[it], d = octant_key(m);
+    const int32_t row = rv[it];
     unsigned long long peers = __ballot(valid);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -204,9 +282,12 @@ __global__ __launch_bounds__(kGroupThreads) void group_rows(const int32_t* __res
       gmask[w0 + pos] = m;
     }
     __syncthreads();
-    if (tid < 256) {
+    if (tid < 256) {  // advance the digit offsets; clear the counts for the next pass
       uint32_t add = 0;
-      for (int w = 0; w < WAVES; ++w) add += wcount[w][tid];
+      for (int w = 0; w < WAVES; ++w) {
+        add += wcount[w][tid];
+        wcount[w][tid] = 0;
+      }
       base_off[tid] += add;
     }
     __syncthreads();
