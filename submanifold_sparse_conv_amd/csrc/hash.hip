@@ -420,20 +420,32 @@ __global__ __launch_bounds__(kThreads) void block_clear(BlockSlot* __restrict__ 
   }
 }
 
-// The thread at each block head builds the block's occupancy bitmap from the
-// following sorted keys (at most 64) and inserts {block key, bitmap, start}.
+// The lane at each block head inserts {block key, occupancy bitmap, start}.
+// The bitmap is a segmented OR over the lanes of the wave that hold the same
+// block (sorted keys make a block one run of lanes); only a block that runs
+// past the wave's last lane is finished by its head with a short serial loop.
 __global__ __launch_bounds__(kThreads) void block_insert(const uint64_t* __restrict__ keys, int64_t n,
                                                          BlockSlot* __restrict__ slots, HashHeader* hdr) {
   const int64_t t = int64_t(blockIdx.x) * kThreads + threadIdx.x;
-  if (t >= n) return;
-  const uint64_t k = keys[t];
+  const int lane = threadIdx.x & 63;
+  const bool valid = t < n;
+  const uint64_t k = valid ? keys[t] : ~0ull;
   const uint64_t bkey = k >> 6;
-  if (t > 0 && (keys[t - 1] >> 6) == bkey) return;
-  uint64_t bits = 0;
-  for (int64_t u = t; u < n && u < t + 64; ++u) {
-    const uint64_t ku = keys[u];
-    if ((ku >> 6) != bkey) break;
-    bits |= 1ull << (ku & 63u);
+  const bool head = valid && (t == 0 || (keys[t - 1] >> 6) != bkey);
+  uint64_t bits = valid ? (1ull << (k & 63u)) : 0ull;
+  for (int o = 1; o < 64; o <<= 1) {  // bits of lanes [lane, lane + 2o) of the same block
+    const uint64_t ob = __shfl_down(bits, o, 64);
+    const uint64_t okey = __shfl_down(bkey, o, 64);
+    if (lane + o < 64 && okey == bkey) bits |= ob;
+  }
+  const uint64_t last_key = __shfl(bkey, 63, 64);
+  if (!head) return;
+  if (last_key == bkey) {  // the block may continue in the next wave
+    for (int64_t u = t - lane + 64; u < n && u < t + 64; ++u) {
+      const uint64_t ku = keys[u];
+      if ((ku >> 6) != bkey) break;
+      bits |= 1ull << (ku & 63u);
+    }
   }
   const uint32_t mask = hdr->cap_mask, shift = hdr->shift;
   uint32_t s = home_slot(bkey, shift) & mask;
