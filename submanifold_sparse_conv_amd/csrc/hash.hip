@@ -156,10 +156,15 @@ __global__ __launch_bounds__(kThreads) void radix_hist(const uint64_t* __restric
   for (int d = threadIdx.x; d < nb; d += kThreads) h[d] = 0;
   __syncthreads();
   const int64_t base = int64_t(blockIdx.x) * (kThreads * ITEMS);
+  uint64_t kv[ITEMS];  // the tile's keys, loaded before any is counted
+#pragma unroll
   for (int it = 0; it < ITEMS; ++it) {
     const int64_t i = base + it * kThreads + threadIdx.x;
-    if (i < n) atomicAdd(&h[digit_of(keys[i], s_pos, nbits)], 1u);
+    kv[it] = i < n ? keys[i] : 0ull;
   }
+#pragma unroll
+  for (int it = 0; it < ITEMS; ++it)
+    if (base + it * kThreads + threadIdx.x < n) atomicAdd(&h[digit_of(kv[it], s_pos, nbits)], 1u);
   __syncthreads();
   for (int d = threadIdx.x; d < nb; d += kThreads) counts[int64_t(d) * gridDim.x + blockIdx.x] = h[d];
 }
@@ -199,12 +204,25 @@ __global__ __launch_bounds__(kThreads) void radix_colscan(uint32_t* __restrict__
     }
     uint32_t* col = counts + int64_t(d) * nblocks;
     uint32_t carry = 0;
-    for (int b0 = 0; b0 < nblocks; b0 += kThreads) {
-      const int b = b0 + threadIdx.x;
-      const uint32_t v = b < nblocks ? col[b] : 0u;
+    // CPT consecutive entries per thread: one scan covers a whole pass of up to
+    // kMaxSortWGs tiles, its loads all in flight together.
+    constexpr int CPT = (kMaxSortWGs + kThreads - 1) / kThreads;
+    for (int b0 = 0; b0 < nblocks; b0 += kThreads * CPT) {
+      uint32_t v[CPT], sum = 0;
+#pragma unroll
+      for (int q = 0; q < CPT; ++q) {
+        const int b = b0 + threadIdx.x * CPT + q;
+        v[q] = b < nblocks ? col[b] : 0u;
+        sum += v[q];
+      }
       uint32_t tot;
-      const uint32_t ex = block_exclusive_scan(v, s_tmp, &tot);
-      if (b < nblocks) col[b] = carry + ex;
+      uint32_t ex = carry + block_exclusive_scan(sum, s_tmp, &tot);
+#pragma unroll
+      for (int q = 0; q < CPT; ++q) {
+        const int b = b0 + threadIdx.x * CPT + q;
+        if (b < nblocks) col[b] = ex;
+        ex += v[q];
+      }
       carry += tot;
     }
     if (threadIdx.x == 0) totals[d] = carry;
@@ -248,6 +266,15 @@ __global__ __launch_bounds__(kThreads) void radix_scatter(const uint64_t* __rest
   }
   const unsigned long long lt = (1ull << lane) - 1ull;
   const int64_t base = int64_t(blockIdx.x) * (kThreads * ITEMS);
+  uint64_t kv[ITEMS];  // the tile's keys and rows, loaded before the first is ranked
+  int32_t vv[ITEMS];
+#pragma unroll
+  for (int it = 0; it < ITEMS; ++it) {
+    const int64_t i = base + it * kThreads + threadIdx.x;
+    kv[it] = i < n ? kin[i] : 0ull;
+    vv[it] = i < n ? vin[i] : 0;
+  }
+#pragma unroll
   for (int it = 0; it < ITEMS; ++it) {
     for (int d = threadIdx.x; d < nb; d += kThreads)
 #pragma unroll
@@ -255,14 +282,9 @@ __global__ __launch_bounds__(kThreads) void radix_scatter(const uint64_t* __rest
     __syncthreads();
     const int64_t i = base + it * kThreads + threadIdx.x;
     const bool valid = i < n;
-    uint64_t key = 0;
-    int32_t val = 0;
-    uint32_t d = 0;
-    if (valid) {
-      key = kin[i];
-      val = vin[i];
-      d = digit_of(key, s_pos, nbits);
-    }
+    const uint64_t key = kv[it];
+    const int32_t val = vv[it];
+    const uint32_t d = valid ? digit_of(key, s_pos, nbits) : 0u;
     unsigned long long peers = __ballot(valid);
     for (int j = 0; j < nbits; ++j) {
       const bool bit = (d >> j) & 1u;
