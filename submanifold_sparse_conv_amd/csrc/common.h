@@ -5,6 +5,8 @@
 
 #include <cstdint>
 
+#include "tr_sparseconv.h"
+
 namespace trsc {
 
 // ---------------------------------------------------------------------------
@@ -165,6 +167,19 @@ __device__ inline void copy16_to_lds(const void* g, void* lds_base) {
 // of row r sits at chunk position c ^ (r & 7), so eight consecutive rows read
 // at one logical chunk hit eight different bank groups.
 __device__ inline int swz(int row, int chunk) { return chunk ^ (row & 7); }
+
+// Epilogue activation in fp32. SiLU(v) = v / (1 + e^-v), with e^-v taken as
+// 2^(-v log2 e) on the hardware base-2 exponential and the quotient as a
+// product with the hardware reciprocal (each about 1 ulp): a handful of
+// instructions per element instead of a library exp and an IEEE divide. At
+// v < -88 the reciprocal of the overflowed denominator is 0 and the result is
+// -0 (the exact value is below 1e-36 in magnitude).
+constexpr int kActNone = TR_SC_ACT_NONE, kActRelu = TR_SC_ACT_RELU, kActSilu = TR_SC_ACT_SILU;
+__device__ __forceinline__ float activate(float v, int act) {
+  if (act == kActRelu) return v < 0.f ? 0.f : v;
+  if (act == kActSilu) return v * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(v * -1.4426950408889634f));
+  return v;
+}
 
 // Workgroup barrier without the release fence of __syncthreads(): that fence
 // waits for every outstanding global_load_lds (they count as LDS stores), even

@@ -91,12 +91,6 @@ __device__ __forceinline__ void split_terms(const uint4 (&raw)[2], typename H::v
   }
 }
 
-__device__ __forceinline__ float activate(float v, int act) {
-  if (act == kActRelu) return v < 0.f ? 0.f : v;
-  if (act == kActSilu) return v / (1.f + expf(-v));
-  return v;
-}
-
 struct RowsArgs {
   const int32_t* nbr;
   const int32_t* srows;

@@ -10,12 +10,6 @@ namespace {
 
 constexpr int kThreads = 256;
 
-__device__ __forceinline__ float activate(float v, int act) {
-  if (act == kActRelu) return v < 0.f ? 0.f : v;
-  if (act == kActSilu) return v / (1.f + expf(-v));
-  return v;
-}
-
 // fp32 x, w, y; the fused epilogue of the matrix-core path, in fp32:
 // y = act(sum + bias) + residual.
 __global__ __launch_bounds__(kThreads) void fwd_simple(const int32_t* __restrict__ nbr, int64_t n,

@@ -33,7 +33,6 @@ hipError_t launch_kmap(const uint64_t* skeys, int64_t n, const TableRef& t, int3
 
 // Forward kernels. `srows` is the row order of the tiles (position -> caller
 // row), `mask` the 27-bit neighbour mask of the voxel at each position.
-constexpr int kActNone = TR_SC_ACT_NONE, kActRelu = TR_SC_ACT_RELU, kActSilu = TR_SC_ACT_SILU;
 struct Epilogue {
   const float* bias;     // [c_out] or null
   const void* residual;  // [n, c_out] in the output type, or null
