@@ -229,6 +229,55 @@ def test_coordinate_extremes():
     np.testing.assert_array_equal(h.lookup(c).cpu().numpy(), np.arange(len(pts)))
 
 
+def _colliding_blocks(count, log2_cap, rng):
+    """`count` distinct 4x4x4 block coordinates (batch 0) whose block keys
+    (Z-order key >> 6) share one home slot of a 2^log2_cap-slot table under the
+    table's multiplicative hash (top bits of key * 0x9E3779B97F4A7C15 mod 2^64),
+    plus one more such block to leave absent."""
+    shift = np.uint64(64 - log2_cap)
+    chosen, target = [], None
+    while len(chosen) < count + 1:
+        bc = rng.integers(0, 1 << 14, size=(8192, 3)).astype(np.int64)
+        c4 = np.column_stack([np.zeros(len(bc), np.int64), bc * 4])
+        bkey = morton_keys_numpy(c4) >> np.uint64(6)
+        home = (bkey * np.uint64(0x9E3779B97F4A7C15)) >> shift
+        if target is None:
+            target = home[0]
+        for j in np.nonzero(home == target)[0]:
+            if len(chosen) <= count and not any((bc[j] == c).all() for c in chosen):
+                chosen.append(bc[j])
+    return np.array(chosen[:count]), chosen[count]
+
+
+def test_colliding_blocks():
+    # 64 occupied blocks (table capacity 128) whose keys all hash to one home
+    # slot: probe runs up to 64 slots long, for the kernel map, for lookups of
+    # present voxels and for an absent block on the same home slot.
+    say("[edge] 64 blocks on one home slot of a 128-slot table")
+    rng = np.random.default_rng(77)
+    blocks, absent = _colliding_blocks(64, 7, rng)
+    pts = []
+    for bc in blocks:
+        cells = rng.choice(64, size=int(rng.integers(1, 6)), replace=False)
+        for cell in cells:  # in-block (x, y, z) from the cell's bits; corners reach neighbours
+            lx, ly, lz = (cell >> 2 & 1) | (cell >> 5 & 1) << 1, (cell >> 1 & 1) | (cell >> 4 & 1) << 1, \
+                (cell & 1) | (cell >> 3 & 1) << 1
+            pts.append([0, 4 * bc[0] + lx, 4 * bc[1] + ly, 4 * bc[2] + lz])
+    coords = np.array(pts, np.int32)
+    wl = W.custom(coords, 8, 8, "f32", seed=3)
+    c, x, w = to_dev(wl)
+    h, m, y = run_all(c, x, w)
+    assert sc.status(h) == 0
+    nbr, ref = oracle.conv(coords, wl.x, wl.w)
+    np.testing.assert_array_equal(m.nbr.cpu().numpy(), nbr)
+    assert max_rel(y.cpu().numpy(), ref) <= TOL["f32"]
+    q = np.concatenate([coords, [[0, 4 * absent[0] + a, 4 * absent[1] + b, 4 * absent[2] + d]
+                                 for a in range(4) for b in range(4) for d in range(4)]]).astype(np.int32)
+    got = h.lookup(torch.from_numpy(q).to(DEV)).cpu().numpy()
+    np.testing.assert_array_equal(got, oracle.Table(coords).lookup(q))
+    np.testing.assert_array_equal(got[:len(coords)], np.arange(len(coords)))
+
+
 def test_errors():
     say("[edge] error codes")
     dup = torch.tensor([[0, 1, 2, 3], [0, 5, 5, 5], [0, 1, 2, 3]], dtype=torch.int32, device=DEV)
