@@ -278,6 +278,30 @@ def test_colliding_blocks():
     np.testing.assert_array_equal(got[:len(coords)], np.arange(len(coords)))
 
 
+@pytest.mark.parametrize("n", [2_400_000, 3_200_000, 7_000_000])
+def test_large_sorts(n):
+    # Radix tiles of 16 and 32 keys per thread, and more tiles than one pass of
+    # the column scan covers (n > 768 tiles of 8192 keys): the Morton order
+    # bit-exact, and sampled kernel-map rows against the oracle's table.
+    rng = np.random.default_rng(n)
+    idx = rng.choice(2 * 256 ** 3, size=n, replace=False)
+    b, r = np.divmod(idx, 256 ** 3)
+    x, r = np.divmod(r, 256 * 256)
+    y, z = np.divmod(r, 256)
+    coords = np.stack([b, x, y, z], 1).astype(np.int32)
+    say(f"[large sort] n={n} in 2 x 256^3")
+    h = sc.build_hash(torch.from_numpy(coords).to(DEV))
+    perm = h.sorted_rows().cpu().numpy()
+    np.testing.assert_array_equal(perm, np.argsort(morton_keys_numpy(coords), kind="stable"))
+    m = sc.build_kernel_map(h)
+    rows = sample_rows(n, 20000, seed=n)
+    got = m.nbr[torch.from_numpy(rows).to(DEV)].cpu().numpy()
+    offs = np.array([[0, k // 9 - 1, (k // 3) % 3 - 1, k % 3 - 1] for k in range(27)], np.int32)
+    q = (coords[rows][:, None, :] + offs[None]).reshape(-1, 4).astype(np.int32)
+    ref = oracle.Table(coords).lookup(q).reshape(len(rows), 27)
+    np.testing.assert_array_equal(got, ref)
+
+
 def test_errors():
     say("[edge] error codes")
     dup = torch.tensor([[0, 1, 2, 3], [0, 5, 5, 5], [0, 1, 2, 3]], dtype=torch.int32, device=DEV)
