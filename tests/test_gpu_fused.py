@@ -114,6 +114,16 @@ def test_fused_config_sizes(name, w_t, x_t, y_t):
              rows=rows)
 
 
+def test_fused_decoder_level():
+    # The layer chain's shape: the 256^3 set subdivided with every child kept
+    # (3,149,760 voxels at 512^3), C 64->64 fp16, bias + SiLU + residual.
+    base = W.make("L", with_values=False).coords.astype(np.int64)
+    octs = np.array([[0, o >> 2, (o >> 1) & 1, o & 1] for o in range(8)], np.int64)
+    coords = (base[:, None, :] * np.array([1, 2, 2, 2]) + octs[None]).reshape(-1, 4).astype(np.int32)
+    rows = sample_rows(len(coords), 3000, 21)
+    run_case(coords, 64, 64, "f16", "f16", "f16", "silu", True, True, seed=21, rows=rows)
+
+
 def test_fp16_identity_bitexact():
     rng = np.random.default_rng(8)
     coords = grid(2000, 16, 1, 7)
