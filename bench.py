@@ -25,7 +25,9 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 matrix peak
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fwd_mfma.json")
-GEMM_SOURCE = os.path.join(ROOT, "submanifold_sparse_conv_amd", "csrc", "gemm_mfma.hip")
+# the gather-GEMM kernel and the headers it includes: counters taken on other sources are stale
+GEMM_SOURCES = [os.path.join(ROOT, "submanifold_sparse_conv_amd", "csrc", f)
+                for f in ("gemm_mfma.hip", "common.h", "launch.h")]
 
 WORKLOAD_NAMES = {
     "T": "16^3 sphere shell (radius 6, thickness 1), C 8->8 fp32",
@@ -71,9 +73,13 @@ def copy_probe(mib):
     print(json.dumps({"copy_probe_bytes_read": n * 4, "copy_probe_bytes_written": n * 4, "reps": 5}))
 
 
-def sha_of(path):
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+def sha_of(paths):
+    """SHA-256 of the files' bytes, concatenated in the order given."""
+    h = hashlib.sha256()
+    for path in paths:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def to_device(wl, torch):
@@ -281,7 +287,7 @@ def traffic_entry():
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("source_sha256") != sha_of(GEMM_SOURCE):
+    if t.get("source_sha256") != sha_of(GEMM_SOURCES):
         return None
     return t.get("bytes_per_launch")
 
