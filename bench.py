@@ -214,9 +214,9 @@ def layer_chain(sc, torch, wl, blocks, ch, reps=5):
         for b in range(blocks):
             sc.forward_fused(m, x, ws[2 * b], bias=bs[2 * b], act="silu", out=t)
             sc.forward_fused(m, t, ws[2 * b + 1], bias=bs[2 * b + 1], residual=x, out=x)
-        return fine, m, x
+        return fine, children, m, x
 
-    fine, m, x = level()
+    fine, children, m, x = level()
     torch.cuda.synchronize()
     nf = int(fine.shape[0])
     M = pairs_of(m.nbr)
@@ -231,6 +231,24 @@ def layer_chain(sc, torch, wl, blocks, ch, reps=5):
     t = torch.empty_like(x)
     t_conv = time_reps(torch, lambda: sc.forward_fused(m, x, ws[0], bias=bs[0], act="silu", out=t), 4 * reps)
     flops = 2.0 * ch * ch * M
+    # The level moves on their own (subdivide and downsample include the read-back
+    # of the produced row count), against their algorithmic bytes.
+    nc = wl.n
+    hf = sc.build_hash(fine, check_status=False)
+    xf2, xc2 = torch.empty_like(x), torch.empty_like(xc)
+    moves = {
+        "subdivide": (lambda: sc.subdivide(coarse), nc * 16 + nf * 16 + nc * 32),
+        "channel2spatial": (lambda: sc.channel2spatial(children, xc, nf, out=xf2),
+                            nc * 8 * ch * 2 + nc * 32 + nf * ch * 2),
+        "downsample": (lambda: sc.downsample(hf), nf * 12 + nc * 48),
+        "spatial2channel": (lambda: sc.spatial2channel(children, x, out=xc2),
+                            nf * ch * 2 + nc * 32 + nc * 8 * ch * 2),
+    }
+    levels = {}
+    for name, (fn, nbytes) in moves.items():
+        ms = time_reps(torch, fn, reps)
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        levels[name] = {"ms": ms, "algorithmic_bytes": nbytes, "gbs": gbs, "frac_hbm": gbs / PEAK_HBM_GBS}
     return {"workload": f"256^3 fBm shell subdivided (all children kept) -> {nf} voxels at 512^3, "
                         f"{blocks} residual blocks of two 3x3x3 convs, C {ch}->{ch} fp16",
             "n_voxels": nf, "pairs_M": M, "convs": 2 * blocks,
@@ -238,7 +256,8 @@ def layer_chain(sc, torch, wl, blocks, ch, reps=5):
             "ms_hash_and_map": t_map, "ms_per_conv": t_conv,
             "map_share_of_level": t_map / float(np.median(t_level)),
             "conv_effective_tflops": flops / (t_conv * 1e-3) / 1e12,
-            "voxel_layers_per_s": nf * 2 * blocks / (float(np.median(t_level)) * 1e-3)}
+            "voxel_layers_per_s": nf * 2 * blocks / (float(np.median(t_level)) * 1e-3),
+            "level_moves": levels}
 
 
 def cpu_baseline(wl, target_s):
