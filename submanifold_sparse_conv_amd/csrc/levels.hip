@@ -246,10 +246,98 @@ hipError_t launch_subdivide(const int32_t* coords, const uint8_t* keep, int64_t 
   return hipGetLastError();
 }
 
+// The same moves through an LDS tile of whole parent rows (kTileBytes), so that
+// both sides of the move are read and written in contiguous 16-byte pieces
+// across the lanes: the parent rows as one contiguous block, each child row
+// as consecutive pieces. A parent row holds 8C elements, element c * 8 + o at
+// 16-byte piece (c * 8 + o) * sizeof(T) / 16; pieces are stored XOR-swizzled
+// within each 128-byte run (piece p at p ^ ((p >> 3) & 7)) so that the lanes
+// of one LDS access, which step through the channel groups of a child row,
+// fall on different banks.
+constexpr int kTileBytes = 16384;
+
+__device__ inline int swz_piece(int p) { return p ^ ((p >> 3) & 7); }
+
+template <typename T, bool kToFine>
+__global__ __launch_bounds__(kThreads) void regroup_tile(const int32_t* __restrict__ children, int64_t n_coarse,
+                                                         T* __restrict__ xc, T* __restrict__ xf, int c_fine,
+                                                         int per_wg) {
+  constexpr int E = int(sizeof(T)), V = 16 / E;
+  __shared__ __attribute__((aligned(16))) unsigned char tile[kTileBytes];
+  const int row_pieces = c_fine * 8 * E / 16;   // 16-byte pieces per parent row
+  const int groups = c_fine / V;                // 16-byte pieces per child row
+  const int64_t q0 = int64_t(blockIdx.x) * per_wg;
+  const int np = int(n_coarse - q0 < per_wg ? n_coarse - q0 : per_wg);
+  const int pieces = np * row_pieces;
+  uint4* const tp = reinterpret_cast<uint4*>(tile);
+  uint4* const gc = reinterpret_cast<uint4*>(xc + q0 * 8 * c_fine);
+  auto elem_at = [&](int q, int c, int o) -> T* {  // element c * 8 + o of parent row q in the tile
+    const int byte = (c * 8 + o) * E;
+    return reinterpret_cast<T*>(tile + (q * row_pieces + swz_piece(byte >> 4)) * 16 + (byte & 15));
+  };
+  // swz_piece only permutes pieces within aligned runs of 8, and a parent row is a whole
+  // number of such runs (c_fine * 8 * E / 16 = c_fine * E / 2 with V | c_fine), so every
+  // row's pieces stay inside its own slot of the tile.
+  if constexpr (kToFine) {
+    for (int p = threadIdx.x; p < pieces; p += kThreads) {
+      const int q = p / row_pieces, k = p - q * row_pieces;
+      tp[q * row_pieces + swz_piece(k)] = gc[p];
+    }
+    __syncthreads();
+    for (int t = threadIdx.x; t < np * 8 * groups; t += kThreads) {
+      const int g = t % groups, qo = t / groups, o = qo & 7, q = qo >> 3;
+      const int32_t child = children[(q0 + q) * 8 + o];
+      if (child < 0) continue;
+      alignas(16) T out[V];
+#pragma unroll
+      for (int c = 0; c < V; ++c) out[c] = *elem_at(q, g * V + c, o);
+      *reinterpret_cast<uint4*>(xf + int64_t(child) * c_fine + g * V) = *reinterpret_cast<const uint4*>(out);
+    }
+  } else {
+    for (int t = threadIdx.x; t < np * 8 * groups; t += kThreads) {
+      const int g = t % groups, qo = t / groups, o = qo & 7, q = qo >> 3;
+      const int32_t child = children[(q0 + q) * 8 + o];
+      alignas(16) T in[V];
+      *reinterpret_cast<uint4*>(in) = child >= 0
+                                          ? *reinterpret_cast<const uint4*>(xf + int64_t(child) * c_fine + g * V)
+                                          : make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+      for (int c = 0; c < V; ++c) *elem_at(q, g * V + c, o) = in[c];
+    }
+    __syncthreads();
+    for (int p = threadIdx.x; p < pieces; p += kThreads) {
+      const int q = p / row_pieces, k = p - q * row_pieces;
+      gc[p] = tp[q * row_pieces + swz_piece(k)];
+    }
+  }
+}
+
 hipError_t launch_regroup(const int32_t* children, int64_t n_coarse, void* xc, void* xf, int c_fine, int elem_bytes,
                           bool to_fine, hipStream_t st) {
   const int64_t items = n_coarse * (c_fine / (16 / elem_bytes));
   if (items == 0) return hipSuccess;
+  const int64_t row_bytes = int64_t(c_fine) * 8 * elem_bytes;
+  if (row_bytes <= kTileBytes && row_bytes % 128 == 0) {  // whole parent rows fit the tile
+    const int per_wg = int(kTileBytes / row_bytes);
+    const int64_t g = (n_coarse + per_wg - 1) / per_wg;
+    if (g > 0x7FFFFFFF) return hipErrorInvalidValue;
+    if (elem_bytes == 2) {
+      if (to_fine)
+        regroup_tile<uint16_t, true><<<unsigned(g), kThreads, 0, st>>>(
+            children, n_coarse, static_cast<uint16_t*>(xc), static_cast<uint16_t*>(xf), c_fine, per_wg);
+      else
+        regroup_tile<uint16_t, false><<<unsigned(g), kThreads, 0, st>>>(
+            children, n_coarse, static_cast<uint16_t*>(xc), static_cast<uint16_t*>(xf), c_fine, per_wg);
+    } else {
+      if (to_fine)
+        regroup_tile<float, true><<<unsigned(g), kThreads, 0, st>>>(
+            children, n_coarse, static_cast<float*>(xc), static_cast<float*>(xf), c_fine, per_wg);
+      else
+        regroup_tile<float, false><<<unsigned(g), kThreads, 0, st>>>(
+            children, n_coarse, static_cast<float*>(xc), static_cast<float*>(xf), c_fine, per_wg);
+    }
+    return hipGetLastError();
+  }
   const unsigned grid = unsigned((items + kThreads - 1) / kThreads);
   if (elem_bytes == 2) {
     if (to_fine)

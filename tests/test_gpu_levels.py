@@ -55,10 +55,13 @@ def test_subdivide_bitexact(name, density):
 
 
 @pytest.mark.parametrize("dt", ["bf16", "f16", "f32"])
-@pytest.mark.parametrize("c_fine", [8, 64])
+@pytest.mark.parametrize("c_fine", [8, 64, 1024, 1032])
 def test_regroup_bitexact(dt, c_fine):
-    if dt == "f32" and c_fine == 8:
-        c_fine = 4
+    # Parent rows of 8 * c_fine elements: up to 16 KiB they move through the LDS
+    # tile (1024 half / 512 float channels: one row per tile); longer rows take
+    # the register path.
+    if dt == "f32":
+        c_fine = {8: 4, 64: 64, 1024: 512, 1032: 516}[c_fine]
     rng = np.random.default_rng(3)
     coords = W.random_sparse(rng, 5000, D=30, B=2)
     keep = keep_masks(len(coords), 8, 0.4)
