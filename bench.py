@@ -24,6 +24,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 matrix peak
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+PEAK_FP32_VECTOR_TFLOPS = 157.3  # MI355X fp32 vector (256 CUs, 2.4 GHz)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fwd_mfma.json")
 # the gather-GEMM kernel and the headers it includes: counters taken on other sources are stale
 GEMM_SOURCES = [os.path.join(ROOT, "submanifold_sparse_conv_amd", "csrc", f)
@@ -369,7 +370,16 @@ def main():
                             + (c[:, 3] >> 2)).size)
     hash_bytes = 16 * wl.n + 12 * wl.n + 32 * nblocks
     map_bytes = 12 * wl.n + 4 * wl.n + 32 * nblocks + 108 * wl.n + 4 * wl.n + 8 * wl.n
-    traffic = traffic_entry()
+    # the committed counters were taken on the 256^3 config's launch
+    traffic = traffic_entry() if args.config == "L" else None
+    if wl.dtype == "bf16":
+        roof = {"kernel": "fwd_rows (gather-GEMM)", "bound": "mfma", "achieved": gemm_tflops,
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": gemm_tflops / PEAK_BF16_TFLOPS,
+                "traffic": traffic}
+    else:  # fp32 features and weights: the plain FMA kernel
+        roof = {"kernel": "fwd_simple (fp32 FMA)", "bound": "alu", "achieved": gemm_tflops,
+                "peak": PEAK_FP32_VECTOR_TFLOPS, "unit": "TFLOP/s",
+                "frac": gemm_tflops / PEAK_FP32_VECTOR_TFLOPS, "traffic": None}
 
     out = {
         "metric": "sparse-conv voxels/s (whole path: hash + kernel map + gather-GEMM)",
@@ -395,9 +405,7 @@ def main():
                          "gbs": (hash_bytes + map_bytes) / ((t_hash + t_map) * 1e-3) / 1e9,
                          "frac": (hash_bytes + map_bytes) / ((t_hash + t_map) * 1e-3) / 1e9 / PEAK_HBM_GBS,
                          "map_only_gbs": map_bytes / (t_map * 1e-3) / 1e9},
-        "roofline": {"kernel": "fwd_rows (gather-GEMM)", "bound": "mfma", "achieved": gemm_tflops,
-                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": gemm_tflops / PEAK_BF16_TFLOPS,
-                     "traffic": traffic},
+        "roofline": roof,
     }
     extra = {}
     for name in [a for a in args.also.split(",") if a and a != args.config]:
