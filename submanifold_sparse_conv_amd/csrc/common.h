@@ -168,6 +168,14 @@ __device__ inline void copy16_to_lds(const void* g, void* lds_base) {
 // at one logical chunk hit eight different bank groups.
 __device__ inline int swz(int row, int chunk) { return chunk ^ (row & 7); }
 
+// 16-byte store marked non-temporal: outputs written once and not read again by
+// the kernel, kept from displacing the gathered rows and weights in the caches.
+__device__ __forceinline__ void store_stream(uint4* dst, uint4 v) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 w = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(dst));
+}
+
 // Epilogue activation in fp32. SiLU(v) = v / (1 + e^-v), with e^-v taken as
 // 2^(-v log2 e) on the hardware base-2 exponential and the quotient as a
 // product with the hardware reciprocal (each about 1 ulp): a handful of

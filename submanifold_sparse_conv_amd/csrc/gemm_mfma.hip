@@ -303,7 +303,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_rows(const RowsArgs p) {
             uint16_t* oh = reinterpret_cast<uint16_t*>(&o);
 #pragma unroll
             for (int e = 0; e < 8; ++e) oh[e] = H::narrow(v[e]);
-            *reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.y) + off) = o;
+            store_stream(reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.y) + off), o);
           }
         }
       } else {
@@ -320,7 +320,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_rows(const RowsArgs p) {
               const float4 rr = *reinterpret_cast<const float4*>(static_cast<const float*>(p.residual) + off);
               v.x += rr.x, v.y += rr.y, v.z += rr.z, v.w += rr.w;
             }
-            *reinterpret_cast<float4*>(static_cast<float*>(p.y) + off) = v;
+            store_stream(reinterpret_cast<uint4*>(static_cast<float*>(p.y) + off),
+                         uint4{__float_as_uint(v.x), __float_as_uint(v.y), __float_as_uint(v.z), __float_as_uint(v.w)});
           }
         }
       }
