@@ -107,8 +107,9 @@ struct RowsArgs {
 };
 
 // Wave w of the workgroup owns rows [16*FM*w, 16*FM*(w+1)) of the tile and all
-// TN = 16*FN output channels. The gather indices of a tap are fetched one tap
-// ahead, the A fragments and the weight slice one stage ahead.
+// TN = 16*FN output channels. The tile's rows of the neighbour table are copied
+// into LDS once; a tap's gather indices are read from there one tap ahead, the
+// A fragments and the weight slice are loaded one stage ahead.
 template <int FM, int FN, bool F16, int XT>
 __global__ __launch_bounds__(kThreads, 2) void fwd_rows(const RowsArgs p) {
   typedef Half<F16> H;
@@ -122,6 +123,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_rows(const RowsArgs p) {
   __shared__ __attribute__((aligned(1024))) unsigned char bbuf1[BBUF];
   __shared__ int32_t s_taps[27];
   __shared__ uint32_t s_mask;
+  __shared__ int32_t s_idx[TM * 27];  // the tile's neighbour rows, [row][tap]
 
   const int c_in = p.c_in, c_out = p.c_out;
   const int tile = xcd_remap(blockIdx.x, gridDim.x);
@@ -146,6 +148,28 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_rows(const RowsArgs p) {
   __syncthreads();
   const uint32_t tmask = __builtin_amdgcn_readfirstlane(s_mask);
   if (tid < 27 && ((tmask >> tid) & 1u)) s_taps[__popc(tmask & ((1u << tid) - 1u))] = tid;
+  // The tile's rows of the neighbour table, 27 taps each, copied once into LDS:
+  // two threads per row, 14 and 13 taps, their loads in flight together.
+  {
+    const int64_t rows_left = p.n - t0;
+    const int nrows = rows_left < TM ? int(rows_left) : TM;
+    const int h = tid & 1;
+    for (int r = tid >> 1; r < TM; r += kThreads / 2) {
+      const bool ok = r < nrows;
+      const int32_t cr = ok ? p.srows[t0 + r] : 0;
+      int32_t v[14];
+#pragma unroll
+      for (int j = 0; j < 14; ++j) {
+        const int k = h * 14 + j;
+        v[j] = (ok && k < 27) ? p.nbr[int64_t(cr) * 27 + k] : -1;
+      }
+#pragma unroll
+      for (int j = 0; j < 14; ++j) {
+        const int k = h * 14 + j;
+        if (k < 27) s_idx[r * 27 + k] = v[j];
+      }
+    }
+  }
   __syncthreads();
   const int ntaps = __popc(tmask);
   const int nchunks = (c_in + KC - 1) / KC;
@@ -155,7 +179,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_rows(const RowsArgs p) {
   auto fetch_idx = [&](int ti, int32_t (&dst)[FM]) {
     const int k = s_taps[ti];
 #pragma unroll
-    for (int i = 0; i < FM; ++i) dst[i] = crow[i] >= 0 ? p.nbr[int64_t(crow[i]) * 27 + k] : -1;
+    for (int i = 0; i < FM; ++i) dst[i] = s_idx[(wave * WM + i * 16 + lr) * 27 + k];
   };
   // Issue stage st: A fragments into registers, weight slice into LDS.
   auto issue = [&](int st, uint4 (&a)[FM][2][AV], unsigned char* bdst) {
