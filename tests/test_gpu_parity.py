@@ -117,7 +117,8 @@ def test_forward_parity(name, off, order):
 
 
 SMALL_SHAPES = [(8, 8, "f32"), (3, 5, "f32"), (8, 8, "bf16"), (16, 8, "bf16"), (64, 64, "bf16"),
-                (32, 96, "bf16"), (128, 128, "bf16"), (64, 32, "bf16"), (256, 64, "bf16")]
+                (32, 96, "bf16"), (128, 128, "bf16"), (64, 32, "bf16"), (256, 64, "bf16"),
+                (136, 64, "bf16"), (72, 128, "bf16")]  # a last 64-channel chunk of 8 or 8 of 72
 
 
 @pytest.mark.parametrize("n", [1, 63, 64, 65, 257, 1000, 4097])
