@@ -162,7 +162,7 @@ size_t tr_sparseconv_forward_workspace_bytes(int c_in, int c_out, int dtype);
  *        c_in % 8 == 0 and c_out % 8 == 0.
  *        TR_SC_F32: fp32 inputs, fp32 accumulation and output; any c >= 1.
  * No atomics: the result is the same bit for bit on every call. x and y must
- * not overlap. */
+ * not overlap; y == x is rejected with TR_SC_ERR_INVALID_ARG. */
 int tr_sparseconv_forward(const tr_sc_kmap* m, const void* x, const void* w, void* y,
                           int c_in, int c_out, int dtype, void* workspace,
                           size_t ws_bytes, void* stream);

@@ -274,6 +274,7 @@ bool misaligned16(const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 !=
 int run_forward(const char* who, const tr_sc_kmap* m, const void* x, int x_dtype, const void* wp, int w_dtype,
                 void* y, int y_dtype, const Epilogue& epi, int c_in, int c_out, hipStream_t st) {
   if (x == nullptr || wp == nullptr || y == nullptr) return fail(TR_SC_ERR_INVALID_ARG, "%s: NULL tensor", who);
+  if (x == y) return fail(TR_SC_ERR_INVALID_ARG, "%s: x and y are the same buffer", who);
   if (int64_t(m->n) * c_out >= (int64_t(1) << 40) || int64_t(m->n) * c_in >= (int64_t(1) << 40))
     return fail(TR_SC_ERR_UNSUPPORTED, "%s: tensor too large", who);
   ConvArgs a{m->nbr, m->grows, m->gmask, m->n, x, wp, y, c_in, c_out, x_dtype, w_dtype, y_dtype, epi};

@@ -324,6 +324,11 @@ def test_errors():
         sc.forward(m, torch.zeros((1, 12), dtype=torch.bfloat16, device=DEV),
                    torch.zeros((27, 12, 8), dtype=torch.bfloat16, device=DEV))
     assert e.value.code == -6
+    x8 = torch.zeros((1, 8), dtype=torch.bfloat16, device=DEV)
+    wp8 = sc.pack_weights(torch.zeros((27, 8, 8), dtype=torch.bfloat16, device=DEV))
+    with pytest.raises(sc.TrSparseConvError) as e:  # in place: other rows would read x while y is written
+        sc.forward_packed(m, x8, wp8, out=x8)
+    assert e.value.code == -1
 
 
 @pytest.mark.parametrize("name", ["S", "X"])
