@@ -148,18 +148,10 @@ class KernelMap:
                                                    ctypes.byref(m)))
         self._m = m
         self._destroy = L.tr_sparseconv_kmap_destroy
-        self._fws = {}
 
     @property
     def handle(self) -> ctypes.c_void_p:
         return self._m
-
-    def forward_workspace(self, c_in: int, c_out: int, dtype: int) -> Workspace:
-        key = (c_in, c_out, dtype)
-        if key not in self._fws:
-            nbytes = _lib.lib().tr_sparseconv_forward_workspace_bytes(c_in, c_out, dtype)
-            self._fws[key] = Workspace(nbytes, self.device)
-        return self._fws[key]
 
     def __del__(self):
         m, destroy = getattr(self, "_m", None), getattr(self, "_destroy", None)
@@ -360,18 +352,31 @@ def subdivide(coords: torch.Tensor, keep: torch.Tensor | None = None, workspace:
     return fine[:f.value], children[:n]
 
 
+def _require_children(children: torch.Tensor) -> None:
+    _require(children, "children", torch.int32, 2)
+    if int(children.shape[1]) != 8:
+        raise ValueError(f"children must be [M, 8], got {tuple(children.shape)}")
+
+
 def channel2spatial(children: torch.Tensor, x_coarse: torch.Tensor, n_fine: int,
                     out: torch.Tensor | None = None) -> torch.Tensor:
     """x_fine [n_fine, C] from x_coarse [M, 8C]: channel c * 8 + o of parent q
     goes to channel c of its child o (children [M, 8])."""
-    _require(children, "children", torch.int32, 2)
+    _require_children(children)
     _require(x_coarse, "x_coarse", x_coarse.dtype, 2)
     if x_coarse.dtype not in _DTYPES or x_coarse.shape[1] % 8:
         raise ValueError("x_coarse must be [M, 8C] of a supported dtype")
+    if int(x_coarse.shape[0]) != int(children.shape[0]):
+        raise ValueError(f"x_coarse has {int(x_coarse.shape[0])} rows, children {int(children.shape[0])}")
     c_fine = int(x_coarse.shape[1]) // 8
+    n_fine = int(n_fine)
+    if n_fine < 0:
+        raise ValueError(f"n_fine = {n_fine}")
     if out is None:
         out = torch.empty((n_fine, c_fine), dtype=x_coarse.dtype, device=x_coarse.device)
     _require(out, "out", x_coarse.dtype, 2)
+    if tuple(out.shape) != (n_fine, c_fine):
+        raise ValueError(f"out must be [{n_fine}, {c_fine}], got {tuple(out.shape)}")
     with torch.cuda.device(x_coarse.device):
         check(_lib.lib().tr_sparseconv_channel2spatial(_ptr(children), int(children.shape[0]), _ptr(x_coarse),
                                                        _ptr(out), c_fine, _DTYPES[x_coarse.dtype],
@@ -381,14 +386,17 @@ def channel2spatial(children: torch.Tensor, x_coarse: torch.Tensor, n_fine: int,
 
 def spatial2channel(children: torch.Tensor, x_fine: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
     """x_coarse [M, 8C] from x_fine [F, C]; absent children give zeros."""
-    _require(children, "children", torch.int32, 2)
+    _require_children(children)
     if x_fine.dtype not in _DTYPES:
         raise ValueError(f"unsupported dtype {x_fine.dtype}")
     _require(x_fine, "x_fine", x_fine.dtype, 2)
     c_fine = int(x_fine.shape[1])
+    n_coarse = int(children.shape[0])
     if out is None:
-        out = torch.empty((int(children.shape[0]), 8 * c_fine), dtype=x_fine.dtype, device=x_fine.device)
+        out = torch.empty((n_coarse, 8 * c_fine), dtype=x_fine.dtype, device=x_fine.device)
     _require(out, "out", x_fine.dtype, 2)
+    if tuple(out.shape) != (n_coarse, 8 * c_fine):
+        raise ValueError(f"out must be [{n_coarse}, {8 * c_fine}], got {tuple(out.shape)}")
     with torch.cuda.device(x_fine.device):
         check(_lib.lib().tr_sparseconv_spatial2channel(_ptr(children), int(children.shape[0]), _ptr(x_fine),
                                                        _ptr(out), c_fine, _DTYPES[x_fine.dtype],
@@ -431,7 +439,10 @@ def forward(m: KernelMap, x: torch.Tensor, w: torch.Tensor, out: torch.Tensor | 
         if tuple(out.shape) != (n, c_out):
             raise ValueError(f"out must be [{n}, {c_out}]")
     dt = _DTYPES[x.dtype]
-    ws = m.forward_workspace(c_in, c_out, dt)
+    # A fresh packing buffer per call, from torch's stream-ordered allocator:
+    # calls on other streams (same map, other weights) never share it, and it
+    # returns to the pool of this stream only, behind the launch that reads it.
+    ws = Workspace(_lib.lib().tr_sparseconv_forward_workspace_bytes(c_in, c_out, dt), x.device)
     with torch.cuda.device(x.device):
         check(_lib.lib().tr_sparseconv_forward(m.handle, _ptr(x), _ptr(w), _ptr(out), c_in, c_out, dt,
                                                ws.ptr, ws.nbytes, _stream(x.device)))

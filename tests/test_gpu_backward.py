@@ -3,8 +3,10 @@
 Data gradient (tr_sparseconv_backward_data) element by element with the output
 type's tolerance; weight gradient (tr_sparseconv_backward_weights, fp32 out)
 with the fp32 tolerance for sums over K voxel pairs (tests.helpers.tol_f32).
-At the full workload sizes: sampled rows of dx and sampled (tap, channel) rows
-of dw, each computed one by one by the oracle.
+At the workload sizes: every row of dx (sampled rows and the ragged tail at the
+1024-wide config) and sampled (tap, channel) rows of dw, each computed one by
+one by the oracle. The oracle is always given its own kernel map, which the
+GPU's map must equal bit for bit.
 """
 import functools
 
@@ -37,7 +39,11 @@ def setup(coords, c_in, c_out, w_t, dy_t, seed):
     rng = np.random.default_rng(seed + 1)
     dy = ROUND[dy_t](rng.standard_normal((wl.n, c_out), dtype=np.float32))
     m = sc.build_kernel_map(sc.build_hash(torch.from_numpy(wl.coords).to(DEV)))
-    return wl, dy, m
+    # the expected gradients use the oracle's own kernel map, and the GPU's map
+    # must equal it bit for bit
+    nbr = oracle.kernel_map(wl.coords)
+    np.testing.assert_array_equal(m.nbr.cpu().numpy(), nbr)
+    return wl, dy, m, nbr
 
 
 def sel_sample(c_in, k_count, seed):
@@ -47,12 +53,11 @@ def sel_sample(c_in, k_count, seed):
     return np.stack([ks, cis], 1).astype(np.int32)
 
 
-def check_dgrad(wl, dy, m, w_t, dy_t, dx_t, rows=None):
+def check_dgrad(wl, dy, m, nbr, w_t, dy_t, dx_t, rows=None):
     w = torch.from_numpy(wl.w).to(DEV).to(TD[w_t])
     dx = sc.backward_data(m, torch.from_numpy(dy).to(DEV).to(TD[dy_t]), sc.pack_weights_dgrad(w),
                           out_dtype=TD[dx_t])
     torch.cuda.synchronize()
-    nbr = m.nbr.cpu().numpy()
     rows = np.arange(wl.n) if rows is None else rows
     ref = oracle.backward_data(nbr, dy, wl.w, rows=rows)
     got = dx.float().cpu().numpy()[rows]
@@ -63,11 +68,10 @@ def check_dgrad(wl, dy, m, w_t, dy_t, dx_t, rows=None):
     assert err <= tol
 
 
-def check_wgrad(wl, dy, m, t, sel=None):
+def check_wgrad(wl, dy, m, nbr, t, sel=None):
     x = torch.from_numpy(wl.x).to(DEV).to(TD[t])
     dw = sc.backward_weights(m, x, torch.from_numpy(dy).to(DEV).to(TD[t]))
     torch.cuda.synchronize()
-    nbr = m.nbr.cpu().numpy()
     if sel is None:
         ref = oracle.backward_weights(nbr, wl.x, dy).reshape(-1, wl.c_out)
         got = dw.cpu().numpy().reshape(-1, wl.c_out)
@@ -91,39 +95,41 @@ SHAPES = [(64, 64), (32, 96), (16, 8), (136, 128)]
 @pytest.mark.parametrize("c_in,c_out", SHAPES)
 def test_dgrad_small(w_t, dy_t, dx_t, c_in, c_out):
     say(f"[dgrad] c={c_in}->{c_out} w={w_t} dy={dy_t} dx={dx_t}")
-    wl, dy, m = setup(grid(1500, 14, 2, 3), c_in, c_out, w_t, dy_t, 21)
-    check_dgrad(wl, dy, m, w_t, dy_t, dx_t)
+    wl, dy, m, nbr = setup(grid(1500, 14, 2, 3), c_in, c_out, w_t, dy_t, 21)
+    check_dgrad(wl, dy, m, nbr, w_t, dy_t, dx_t)
 
 
 @pytest.mark.parametrize("t", ["bf16", "f16", "f32"])
 @pytest.mark.parametrize("c_in,c_out", SHAPES)
 def test_wgrad_small(t, c_in, c_out):
     say(f"[wgrad] c={c_in}->{c_out} {t}")
-    wl, dy, m = setup(grid(1500, 14, 2, 3), c_in, c_out, t, t, 22)
-    check_wgrad(wl, dy, m, t)
+    wl, dy, m, nbr = setup(grid(1500, 14, 2, 3), c_in, c_out, t, t, 22)
+    check_wgrad(wl, dy, m, nbr, t)
 
 
 @pytest.mark.parametrize("n,D", [(20000, 40), (70000, 64)])
 def test_wgrad_many_splits(n, D):
     # enough voxels for several position ranges and rounds of 1024 per workgroup
     say(f"[wgrad-splits] n~{n} D={D}")
-    wl, dy, m = setup(grid(n, D, 1, 4), 64, 128, "bf16", "bf16", 23)
-    check_wgrad(wl, dy, m, "bf16")
+    wl, dy, m, nbr = setup(grid(n, D, 1, 4), 64, 128, "bf16", "bf16", 23)
+    check_wgrad(wl, dy, m, nbr, "bf16")
 
 
-@pytest.mark.parametrize("name,t", [("S", "bf16"), ("L", "bf16"), ("L", "f16"), ("X", "bf16"), ("W", "bf16")])
+@pytest.mark.parametrize("name,t", [("T", "f32"), ("S", "bf16"), ("L", "bf16"), ("L", "f16"), ("X", "bf16"),
+                                         ("W", "bf16")])
 def test_backward_config_sizes(name, t):
     wl0 = W.make(name, with_values=False)
     say(f"[backward] config={name} n={wl0.n} c={wl0.c_in}->{wl0.c_out} {t}")
-    wl, dy, m = setup(wl0.coords, wl0.c_in, wl0.c_out, t, t, wl0.seed + 400)
-    rows = sample_rows(wl.n, 150 if wl.c_in >= 1024 else 3000, wl.seed) if wl.n > 20000 else None
-    check_dgrad(wl, dy, m, t, t, t, rows=rows)
+    wl, dy, m, nbr = setup(wl0.coords, wl0.c_in, wl0.c_out, t, t, wl0.seed + 400)
+    # every row of dx, except at the 1024-wide config (sampled rows and the tail)
+    rows = sample_rows(wl.n, 1500, wl.seed) if wl.c_in >= 1024 else None
+    check_dgrad(wl, dy, m, nbr, t, t, t, rows=rows)
     sel = sel_sample(wl.c_in, 13 if wl.c_in >= 1024 else 29, wl.seed) if wl.n > 20000 else None
-    check_wgrad(wl, dy, m, t, sel=sel)
+    check_wgrad(wl, dy, m, nbr, t, sel=sel)
 
 
 def test_backward_deterministic_and_adjoint():
-    wl, dy, m = setup(grid(30000, 48, 1, 5), 64, 64, "bf16", "bf16", 24)
+    wl, dy, m, _ = setup(grid(30000, 48, 1, 5), 64, 64, "bf16", "bf16", 24)
     x = torch.from_numpy(wl.x).to(DEV).bfloat16()
     g = torch.from_numpy(dy).to(DEV).bfloat16()
     w = torch.from_numpy(wl.w).to(DEV).bfloat16()
@@ -144,10 +150,10 @@ def test_backward_deterministic_and_adjoint():
 def test_backward_edge_cases():
     # one voxel: only the centre tap; dw[13] = x^T dy, all other taps zero
     for t in ("bf16", "f32"):
-        wl, dy, m = setup(np.array([[0, 5, 6, 7]], np.int32), 16, 24, t, t, 25)
-        dw = check_wgrad(wl, dy, m, t)
+        wl, dy, m, nbr = setup(np.array([[0, 5, 6, 7]], np.int32), 16, 24, t, t, 25)
+        dw = check_wgrad(wl, dy, m, nbr, t)
         assert float(dw[:13].abs().max()) == 0.0 and float(dw[14:].abs().max()) == 0.0
-        check_dgrad(wl, dy, m, t, t, t)
+        check_dgrad(wl, dy, m, nbr, t, t, t)
     # no voxels: dw all zero, dx empty
     m = sc.build_kernel_map(sc.build_hash(torch.zeros((0, 4), dtype=torch.int32, device=DEV)))
     e = torch.zeros((0, 16), dtype=torch.bfloat16, device=DEV)

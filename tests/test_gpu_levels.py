@@ -113,3 +113,28 @@ def test_level_edge_cases():
     coarse, ch = sc.downsample(sc.build_hash(top))
     assert coarse.cpu().tolist() == [[65535, 32767, 32767, 32767]]
     assert ch.cpu().tolist() == [[-1, -1, 1, -1, -1, -1, -1, 0]]   # octants 4*0 + 2*1 + 0 and 7
+
+
+def test_regroup_shape_errors():
+    # mis-sized operands are refused on the host, before anything is launched
+    children = torch.full((5, 8), -1, dtype=torch.int32, device=DEV)
+    xc = torch.zeros((5, 64), dtype=torch.bfloat16, device=DEV)
+    bad = [
+        lambda: sc.channel2spatial(children[:, :7].contiguous(), xc, 3),       # children not [M, 8]
+        lambda: sc.channel2spatial(children, xc[:4], 3),                      # x_coarse rows != M
+        lambda: sc.channel2spatial(children, xc[:, :60].contiguous(), 3),     # 8C not a multiple of 8
+        lambda: sc.channel2spatial(children, xc, 3,
+                                   out=torch.zeros((2, 8), dtype=torch.bfloat16, device=DEV)),  # rows
+        lambda: sc.channel2spatial(children, xc, 3,
+                                   out=torch.zeros((3, 16), dtype=torch.bfloat16, device=DEV)),  # channels
+        lambda: sc.channel2spatial(children, xc, -1),
+        lambda: sc.spatial2channel(children[:, :4].contiguous(), torch.zeros((3, 8), dtype=torch.bfloat16,
+                                                                              device=DEV)),
+        lambda: sc.spatial2channel(children, torch.zeros((3, 8), dtype=torch.bfloat16, device=DEV),
+                                   out=torch.zeros((4, 64), dtype=torch.bfloat16, device=DEV)),  # rows
+        lambda: sc.spatial2channel(children, torch.zeros((3, 8), dtype=torch.bfloat16, device=DEV),
+                                   out=torch.zeros((5, 32), dtype=torch.bfloat16, device=DEV)),  # channels
+    ]
+    for i, f in enumerate(bad):
+        with pytest.raises(ValueError):
+            f()
