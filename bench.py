@@ -47,7 +47,9 @@ def parse():
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=50)
     p.add_argument("--config", default="L", choices=list(WORKLOAD_NAMES))
-    p.add_argument("--also", default="S", help="extra configs measured forward-only, comma list ('' = none)")
+    p.add_argument("--also", default="T,S,W,X",
+                   help="other configs measured the same way (path phases + steady forward), comma list ('' = none)")
+    p.add_argument("--no-ceilings", action="store_true", help="skip the measured MFMA / copy ceilings")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-variants", action="store_true",
                    help="skip the fused-epilogue / fp16 / mixed-precision / backward timings")
@@ -287,11 +289,115 @@ def cpu_baseline(wl, target_s):
         "value": wl.n / total,
         "unit": "voxels/s",
         "cores": oracle.num_threads(),
+        "cpu_model": cpu_model(),
+        "host_cpus": os.cpu_count(),
         "kind": "oracle",
         "sample": (f"full unordered_map build ({t1 - t0:.2f} s, serial) and kernel map "
                    f"({t2 - t1:.2f} s) over all {wl.n} voxels; fp64 forward over {k} random rows "
                    f"({t4 - t3:.2f} s) scaled to all rows ({t_fwd_all:.2f} s)"),
     }
+
+
+def block_count(coords):
+    """Occupied 4x4x4 blocks of a voxel set (per object)."""
+    c = coords.astype(np.int64)
+    return int(np.unique(((c[:, 0] * 16384 + (c[:, 1] >> 2)) * 16384 + (c[:, 2] >> 2)) * 16384
+                         + (c[:, 3] >> 2)).size)
+
+
+def hash_map_bytes(n, nblocks):
+    """Algorithmic bytes of the topology passes under two conventions.
+
+    "block table" (what this library moves): hash = coordinates read (16 B) +
+    sorted key and row written (12 B) per voxel + one 32-byte slot per occupied
+    4x4x4 block; map = sorted key and row read, the row order read once more,
+    nbr (108 B), mask and the tile order (row + mask) written per voxel, the
+    block table read once.
+    "per-voxel table" (a table of P = pow2 >= 2N slots of 12 B, as a one-slot-
+    per-voxel hash would move): hash = 16 + 12 B per voxel + 12 B per slot; map
+    = 12 B per voxel read + the table read + nbr (108 B) and mask (4 B) written.
+    """
+    P = 1
+    while P < 2 * max(n, 1):
+        P *= 2
+    blk = {"hash": 16 * n + 12 * n + 32 * nblocks,
+           "map": 12 * n + 4 * n + 32 * nblocks + 108 * n + 4 * n + 8 * n}
+    vox = {"hash": 16 * n + 12 * n + 12 * P, "map": 12 * n + 12 * P + 108 * n + 4 * n}
+    return blk, vox
+
+
+def config_record(name, wl, M, phases, t_fwd_steady):
+    """One config's path phases (ms), steady forward, effective TFLOP/s and
+    fraction of the peak of its arithmetic, and the topology passes' GB/s."""
+    t_hash, t_map, t_pack, t_gemm = (float(v) for v in phases)
+    flops = 2.0 * wl.c_in * wl.c_out * M
+    tf = flops / (t_fwd_steady * 1e-3) / 1e12
+    half = wl.dtype == "bf16"
+    blk, vox = hash_map_bytes(wl.n, block_count(wl.coords))
+    t_hm = (t_hash + t_map) * 1e-3
+
+    def gbs(b):
+        return {"bytes": b["hash"] + b["map"], "gbs": (b["hash"] + b["map"]) / t_hm / 1e9,
+                "frac": (b["hash"] + b["map"]) / t_hm / 1e9 / PEAK_HBM_GBS,
+                "hash_gbs": b["hash"] / (t_hash * 1e-3) / 1e9, "map_gbs": b["map"] / (t_map * 1e-3) / 1e9}
+    return {"workload": WORKLOAD_NAMES[name], "n_voxels": wl.n, "pairs_M": M, "c_in": wl.c_in,
+            "c_out": wl.c_out, "dtype": "bf16" if half else "f32",
+            "ms": {"build_hash": t_hash, "build_kernel_map": t_map, "pack_weights": t_pack,
+                   "gather_gemm_in_path": t_gemm, "forward_steady": t_fwd_steady},
+            "voxels_per_s_path": wl.n / ((t_hash + t_map + t_pack + t_gemm) * 1e-3),
+            "voxels_per_s_forward": wl.n / (t_fwd_steady * 1e-3),
+            "effective_tflops": tf,
+            "peak_tflops": PEAK_BF16_TFLOPS if half else PEAK_FP32_VECTOR_TFLOPS,
+            "frac_peak": tf / (PEAK_BF16_TFLOPS if half else PEAK_FP32_VECTOR_TFLOPS),
+            "hash_map_hbm": {"block_table": gbs(blk), "per_voxel_table": gbs(vox)}}
+
+
+def measure_ceilings(sc, torch):
+    """The chip's measured ceilings beside the published peaks: a loop of
+    independent bf16 32x32x16 matrix multiply-accumulates, and a 1 GiB
+    device-to-device streaming copy (best of five launches each)."""
+    import ctypes
+    L = sc._lib.lib()
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    grid, iters = 4096, 2000
+    buf = torch.empty(grid * 256, device="cuda")
+    flops = L.tr_sparseconv_ceiling_mfma_flops(grid, iters)
+
+    def best(fn, reps=5):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record()
+            fn()
+            e.record()
+            torch.cuda.synchronize()
+            ts.append(s.elapsed_time(e))
+        return min(ts)
+    ms_m = best(lambda: sc.check(L.tr_sparseconv_ceiling_mfma(ctypes.c_void_p(buf.data_ptr()), grid, iters, st)))
+    nbytes = 1 << 30
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    ms_c = best(lambda: sc.check(L.tr_sparseconv_ceiling_copy(ctypes.c_void_p(a.data_ptr()),
+                                                               ctypes.c_void_p(b.data_ptr()), nbytes, 1024, st)))
+    mfma = flops / (ms_m * 1e-3) / 1e12
+    copy = 2 * nbytes / (ms_c * 1e-3) / 1e9
+    return {"mfma_bf16_tflops": {"measured": mfma, "spec": PEAK_BF16_TFLOPS, "frac_of_spec": mfma / PEAK_BF16_TFLOPS,
+                                 "probe": f"{grid} x 4 waves x {iters} x 4 v_mfma_f32_32x32x16_bf16"},
+            "hbm_gbs": {"measured": copy, "spec": PEAK_HBM_GBS, "frac_of_spec": copy / PEAK_HBM_GBS,
+                        "probe": "1 GiB device copy, 16-byte accesses, bytes read + written"}}
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def note(msg):
@@ -360,18 +466,9 @@ def main():
     # the per-kernel average must cover the timed steps' launches only)
     t_gemm_ss = measure_forward_only(sc, torch, path, args.gemm_reps) if args.gemm_reps > 0 else t_gemm
 
-    # Algorithmic bytes of the topology passes. Hash: coordinates read, sorted
-    # key + row written, one 32-byte slot per occupied 4x4x4 block written.
-    # Map: sorted key + row read, the row order read once more for neighbour
-    # rows, the block table read once, nbr (108 B), mask and the tile order
-    # (row + mask) written.
-    c = wl.coords.astype(np.int64)
-    nblocks = int(np.unique(((c[:, 0] * 16384 + (c[:, 1] >> 2)) * 16384 + (c[:, 2] >> 2)) * 16384
-                            + (c[:, 3] >> 2)).size)
-    hash_bytes = 16 * wl.n + 12 * wl.n + 32 * nblocks
-    map_bytes = 12 * wl.n + 4 * wl.n + 32 * nblocks + 108 * wl.n + 4 * wl.n + 8 * wl.n
     # the committed counters were taken on the 256^3 config's launch
     traffic = traffic_entry() if args.config == "L" else None
+    main_cfg = config_record(args.config, wl, M, (t_hash, t_map, t_pack, t_gemm), t_gemm_ss)
     if wl.dtype == "bf16":
         roof = {"kernel": "fwd_rows (gather-GEMM)", "bound": "mfma", "achieved": gemm_tflops,
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": gemm_tflops / PEAK_BF16_TFLOPS,
@@ -401,36 +498,37 @@ def main():
         "forward": {"voxels_per_s_steady": wl.n / (t_gemm_ss * 1e-3), "ms_steady": t_gemm_ss,
                     "effective_tflops": flops / (t_gemm_ss * 1e-3) / 1e12,
                     "frac_bf16_peak": flops / (t_gemm_ss * 1e-3) / 1e12 / PEAK_BF16_TFLOPS},
-        "hash_map_hbm": {"algorithmic_bytes": hash_bytes + map_bytes, "blocks_4x4x4": nblocks,
-                         "gbs": (hash_bytes + map_bytes) / ((t_hash + t_map) * 1e-3) / 1e9,
-                         "frac": (hash_bytes + map_bytes) / ((t_hash + t_map) * 1e-3) / 1e9 / PEAK_HBM_GBS,
-                         "map_only_gbs": map_bytes / (t_map * 1e-3) / 1e9},
+        "hash_map_hbm": main_cfg["hash_map_hbm"],
         "roofline": roof,
     }
-    extra = {}
+    configs = {args.config: main_cfg}
     for name in [a for a in args.also.split(",") if a and a != args.config]:
         wl2 = W.make(name)
         c2, x2, w2 = to_device(wl2, torch)
         p2 = Path(sc, torch, c2, x2, w2)
-        for _ in range(2):
+        for _ in range(3):
             p2.step()
         torch.cuda.synchronize()
         M2 = pairs_of(p2.nbr)
-        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(10)]
-        for i in range(10):
+        reps = 20
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(reps)]
+        for i in range(reps):
             p2.step(ev[i])
         torch.cuda.synchronize()
-        st = np.array([[ev[i][j].elapsed_time(ev[i][j + 1]) for j in range(4)] for i in range(10)]).mean(0)
-        tss = measure_forward_only(sc, torch, p2, args.gemm_reps) if args.gemm_reps > 0 else float(st[3])
-        f2 = 2.0 * wl2.c_in * wl2.c_out * M2
-        extra[name] = {"workload": WORKLOAD_NAMES[name], "n_voxels": wl2.n, "pairs_M": M2,
-                       "ms_path": float(st.sum()), "voxels_per_s_path": wl2.n / (st.sum() * 1e-3),
-                       "gemm_ms_steady": tss, "voxels_per_s_forward": wl2.n / (tss * 1e-3),
-                       "effective_tflops": f2 / (tss * 1e-3) / 1e12}
+        ph2 = np.array([[ev[i][j].elapsed_time(ev[i][j + 1]) for j in range(4)] for i in range(reps)])
+        tss = measure_forward_only(sc, torch, p2, args.gemm_reps) if args.gemm_reps > 0 else float(
+            np.median(ph2[:, 3]))
+        configs[name] = config_record(name, wl2, M2, tuple(np.median(ph2, axis=0)), tss)
         del p2, c2, x2, w2
         note(f"config {name} measured")
-    if extra:
-        out["also"] = extra
+    out["configs"] = configs
+    if not args.no_ceilings:
+        out["ceilings"] = measure_ceilings(sc, torch)
+        if wl.dtype == "bf16":
+            mp = out["ceilings"]["mfma_bf16_tflops"]["measured"]
+            out["roofline"]["measured_peak"] = mp
+            out["roofline"]["frac_of_measured_peak"] = gemm_tflops / mp
+        note("ceilings measured")
     if not args.no_variants and wl.dtype == "bf16":
         out["variants"] = variants(sc, torch, wl, path, M, max(5, args.gemm_reps // 2))
         note("variants measured")

@@ -293,6 +293,27 @@ int tr_sparseconv_channel2spatial(const int32_t* children, int64_t n_coarse, con
 int tr_sparseconv_spatial2channel(const int32_t* children, int64_t n_coarse, const void* x_fine,
                                   void* x_coarse, int c_fine, int dtype, void* stream);
 
+/* ------------------------------------------------------------------------
+ * Measured ceilings (for the benchmark's roofline fractions; they compute
+ * nothing of the convolution). Both enqueue one kernel on `stream`.
+ * ------------------------------------------------------------------------ */
+
+/* bf16 matrix-core ceiling: `grid` workgroups of four waves, each wave issuing
+ * `iters` rounds of four independent 32x32x16 bf16 multiply-accumulates.
+ * out: device float [grid * 256], receives one value per thread (caller-owned).
+ * tr_sparseconv_ceiling_mfma_flops gives the flops of one launch (0 for
+ * non-positive arguments). Errors: TR_SC_ERR_INVALID_ARG for a null out or
+ * non-positive grid / iters; TR_SC_ERR_HIP if the launch fails. */
+int64_t tr_sparseconv_ceiling_mfma_flops(int grid, int iters);
+int tr_sparseconv_ceiling_mfma(float* out, int grid, int iters, void* stream);
+
+/* HBM streaming ceiling: dst[0, bytes) = src[0, bytes) with 16-byte accesses
+ * by `grid` workgroups of 256 threads (grid-stride). src and dst are
+ * caller-owned device buffers, 16-byte aligned, not overlapping; bytes a
+ * multiple of 16. Errors: TR_SC_ERR_INVALID_ARG otherwise; TR_SC_ERR_HIP if the
+ * launch fails. */
+int tr_sparseconv_ceiling_copy(const void* src, void* dst, size_t bytes, int grid, void* stream);
+
 /* Message of the last failed call on this thread ("" if none). */
 const char* tr_sparseconv_last_error(void);
 

@@ -67,6 +67,9 @@ SIGNATURES = [
     ("tr_sparseconv_subdivide", _I, [_P, _I64, _P, _P, _P, _I64, _P, _SZ, _P, ctypes.POINTER(ctypes.c_int64)]),
     ("tr_sparseconv_channel2spatial", _I, [_P, _I64, _P, _P, _I, _I, _P]),
     ("tr_sparseconv_spatial2channel", _I, [_P, _I64, _P, _P, _I, _I, _P]),
+    ("tr_sparseconv_ceiling_mfma_flops", _I64, [_I, _I]),
+    ("tr_sparseconv_ceiling_mfma", _I, [_P, _I, _I, _P]),
+    ("tr_sparseconv_ceiling_copy", _I, [_P, _P, _SZ, _I, _P]),
 ]
 
 _lib = None

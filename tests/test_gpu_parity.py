@@ -153,6 +153,24 @@ def test_forward_wide_all_rows(n):
     assert err <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("c_in,c_out", [(64, 64), (72, 48)])
+def test_forward_large_64wide_all_rows(c_in, c_out):
+    # 64-wide layers over more than 65,536 voxels take the LDS-staged gather
+    # path; every row against the oracle, with a ragged last tile
+    rng = np.random.default_rng(c_in * 31 + c_out)
+    coords = W.random_sparse(rng, 70001, D=48, B=1)
+    coords = coords[rng.permutation(len(coords))]
+    wl = W.custom(coords, c_in, c_out, "bf16", seed=c_in + 5)
+    say(f"[large 64-wide] n={wl.n} c={c_in}->{c_out} bf16")
+    c, x, w = to_dev(wl)
+    _, m, y = run_all(c, x, w)
+    nbr, ref = oracle.conv(coords, wl.x, wl.w)
+    np.testing.assert_array_equal(m.nbr.cpu().numpy(), nbr)
+    err = max_rel(y.float().cpu().numpy(), ref)
+    say(f"    max_rel={err:.3e}")
+    assert err <= TOL["bf16"]
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("c", [8, 64, 128])
 def test_identity_kernel_bitexact(dtype, c):
