@@ -167,6 +167,20 @@ int tr_sparseconv_forward(const tr_sc_kmap* m, const void* x, const void* w, voi
                           int c_in, int c_out, int dtype, void* workspace,
                           size_t ws_bytes, void* stream);
 
+/* tr_sparseconv_forward for callers that cannot allocate device memory or
+ * pass a workspace (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation). Same arguments, result bits and errors as
+ * tr_sparseconv_forward, without the workspace: the packed weights go to a
+ * scratch array inside the library, 8 MiB per GPU, held until the process
+ * ends; the call itself allocates nothing. Limit: half-precision weights need
+ * 27 * c_in * c_out * 2 + 256 bytes <= 8 MiB (c_in * c_out <= 155,339, e.g.
+ * 384 x 384), else TR_SC_ERR_WORKSPACE and nothing is enqueued (fp32 reads w in
+ * place and has no limit). Every call on one GPU shares that GPU's array:
+ * calls that overlap in time on one GPU (two streams or threads) race; `stream`
+ * must belong to the current device. */
+int tr_sparseconv_forward_noalloc(const tr_sc_kmap* m, const void* x, const void* w, void* y,
+                                  int c_in, int c_out, int dtype, void* stream);
+
 /* The two halves of tr_sparseconv_forward, for callers that reuse one set of
  * weights across many calls (a layer applied to many inputs):
  *

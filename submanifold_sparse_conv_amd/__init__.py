@@ -21,7 +21,7 @@ __all__ = ["build_hash", "build_kernel_map", "forward", "pack_weights", "forward
            "pack_weights_dgrad", "backward_data", "backward_weights", "downsample", "subdivide",
            "channel2spatial", "spatial2channel",
            "status", "hash_lookup", "hash_sorted_rows", "HashTable", "KernelMap", "PackedWeights",
-           "TrSparseConvError", "version", "forward_workspace_bytes", "Workspace"]
+           "TrSparseConvError", "version", "forward_workspace_bytes", "Workspace", "forward_noalloc"]
 
 _DTYPES = {torch.float32: _lib.F32, torch.bfloat16: _lib.BF16, torch.float16: _lib.F16}
 _ACTS = {"none": _lib.ACT_NONE, "relu": _lib.ACT_RELU, "silu": _lib.ACT_SILU}
@@ -446,4 +446,26 @@ def forward(m: KernelMap, x: torch.Tensor, w: torch.Tensor, out: torch.Tensor | 
     with torch.cuda.device(x.device):
         check(_lib.lib().tr_sparseconv_forward(m.handle, _ptr(x), _ptr(w), _ptr(out), c_in, c_out, dt,
                                                ws.ptr, ws.nbytes, _stream(x.device)))
+    return out
+
+
+def forward_noalloc(m: KernelMap, x: torch.Tensor, w: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """forward() without a workspace (tr_sparseconv_forward_noalloc): the packed
+    weights go to the library's per-GPU scratch array, so the call allocates no
+    device memory of its own (pass `out` to allocate nothing at all). Calls that
+    overlap in time on one GPU race on that array."""
+    if x.dtype not in _DTYPES:
+        raise ValueError(f"unsupported dtype {x.dtype}")
+    _require(x, "x", x.dtype, 2)
+    _require(w, "w", x.dtype, 3)
+    n, c_in = int(x.shape[0]), int(x.shape[1])
+    if n != m.n:
+        raise ValueError(f"x has {n} rows, kernel map has {m.n}")
+    if w.shape[0] != 27 or w.shape[1] != c_in:
+        raise ValueError(f"w must be [27, {c_in}, C_out], got {tuple(w.shape)}")
+    c_out = int(w.shape[2])
+    out = _out(out, n, c_out, x)
+    with torch.cuda.device(x.device):
+        check(_lib.lib().tr_sparseconv_forward_noalloc(m.handle, _ptr(x), _ptr(w), _ptr(out), c_in, c_out,
+                                                       _DTYPES[x.dtype], _stream(x.device)))
     return out

@@ -54,6 +54,7 @@ SIGNATURES = [
     ("tr_sparseconv_kmap_destroy", None, [_P]),
     ("tr_sparseconv_forward_workspace_bytes", _SZ, [_I, _I, _I]),
     ("tr_sparseconv_forward", _I, [_P, _P, _P, _P, _I, _I, _I, _P, _SZ, _P]),
+    ("tr_sparseconv_forward_noalloc", _I, [_P, _P, _P, _P, _I, _I, _I, _P]),
     ("tr_sparseconv_packed_weights_bytes", _SZ, [_I, _I, _I]),
     ("tr_sparseconv_pack_weights", _I, [_P, _I, _I, _I, _P, _SZ, _P]),
     ("tr_sparseconv_forward_packed", _I, [_P, _P, _P, _P, _I, _I, _I, _P]),

@@ -4,6 +4,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "common.h"
@@ -338,6 +339,74 @@ int tr_sparseconv_forward(const tr_sc_kmap* m, const void* x, const void* w, voi
   hipError_t e = launch_pack_weights(w, workspace, c_in, c_out, st);
   if (e != hipSuccess) return hip_fail(e, "forward: pack");
   return run_forward("forward", m, x, dtype, workspace, dtype, y, dtype, none, c_in, c_out, st);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// tr_sparseconv_forward without a workspace argument and without allocating:
+// the packed weights go to `scratch`, a file-scope device array. Each GPU the
+// library runs on holds its own copy of the array (at its own address) until
+// the process ends. In host code the array's name is only a stand-in: the
+// device address of the current GPU's copy is resolved once per device with
+// hipGetSymbolAddress and kept in g_scratch_ptr; only that address is passed to
+// kernels. Calls on one GPU share its copy: calls that overlap in time on one
+// GPU (two streams, two threads) race on it.
+// ---------------------------------------------------------------------------
+constexpr size_t kNoAllocScratchBytes = size_t(8) << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+
+constexpr int kMaxScratchDevices = 64;
+std::once_flag g_scratch_once[kMaxScratchDevices];
+void* g_scratch_ptr[kMaxScratchDevices];
+hipError_t g_scratch_err[kMaxScratchDevices];
+
+// Device address of the current device's copy of `scratch`, resolved on the
+// first call on that device, with that device current.
+hipError_t scratch_of_current_device(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* p = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = g_scratch_err[dev] == hipSuccess ? p : nullptr;
+  });
+  *ptr = g_scratch_ptr[dev];
+  return g_scratch_err[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+int tr_sparseconv_forward_noalloc(const tr_sc_kmap* m, const void* x, const void* w, void* y, int c_in,
+                                  int c_out, int dtype, void* stream) {
+  if (m == nullptr || m->magic != kKmapMagic)
+    return fail(TR_SC_ERR_INVALID_ARG, "forward_noalloc: bad kernel-map handle");
+  const int c = check_channels("forward_noalloc", c_in, c_out, dtype);
+  if (c != TR_SC_OK) return c;
+  const size_t need = tr_sparseconv_forward_workspace_bytes(c_in, c_out, dtype);
+  if (need > kNoAllocScratchBytes)
+    return fail(TR_SC_ERR_WORKSPACE,
+                "forward_noalloc: packed weights of %zu bytes exceed the %zu-byte scratch array "
+                "(27 * c_in * c_out * 2 + 256 bytes must fit)",
+                need, kNoAllocScratchBytes);
+  if (m->n == 0) return TR_SC_OK;
+  if (w == nullptr) return fail(TR_SC_ERR_INVALID_ARG, "forward_noalloc: NULL tensor");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const Epilogue none{nullptr, nullptr, kActNone};
+  if (dtype == TR_SC_F32)  // the fp32 path reads w in place: no scratch
+    return run_forward("forward_noalloc", m, x, dtype, w, dtype, y, dtype, none, c_in, c_out, st);
+  void* wp = nullptr;
+  hipError_t e = scratch_of_current_device(&wp);
+  if (e != hipSuccess) return hip_fail(e, "forward_noalloc: scratch address");
+  e = launch_pack_weights(w, wp, c_in, c_out, st);
+  if (e != hipSuccess) return hip_fail(e, "forward_noalloc: pack");
+  return run_forward("forward_noalloc", m, x, dtype, wp, dtype, y, dtype, none, c_in, c_out, st);
 }
 
 int tr_sparseconv_forward_fused(const tr_sc_kmap* m, const void* x, int x_dtype, const void* wp, int w_dtype,
