@@ -50,6 +50,7 @@ def parse():
     p.add_argument("--also", default="T,S,W,X",
                    help="other configs measured the same way (path phases + steady forward), comma list ('' = none)")
     p.add_argument("--no-ceilings", action="store_true", help="skip the measured MFMA / copy ceilings")
+    p.add_argument("--no-wide-keys", action="store_true", help="skip the hash build over keys with > 33 varying bits")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-variants", action="store_true",
                    help="skip the fused-epilogue / fp16 / mixed-precision / backward timings")
@@ -298,6 +299,24 @@ def cpu_baseline(wl, target_s):
     }
 
 
+def wide_keys(sc, torch, wl, reps=5):
+    """build_hash over keys with many varying bits: the voxels of the workload
+    spread over 64 object ids whose values span 16 bits (b = (row % 64) *
+    1021), so 16 + 24 = 40 key bits vary and the sort needs four radix passes
+    (bits beyond four 11-bit digits, 44, would go to a single-workgroup pass)."""
+    c = wl.coords.copy()
+    c[:, 0] = (np.arange(wl.n) % 64) * 1021
+    vary = np.bitwise_or.reduce(c, axis=0) ^ np.bitwise_and.reduce(c, axis=0)
+    nbits = int(sum(bin(int(v)).count("1") for v in vary))
+    cd = torch.from_numpy(c).cuda()
+    ws = sc.Workspace(sc._lib.lib().tr_sparseconv_hash_workspace_bytes(wl.n), cd.device)
+    sc.build_hash(cd, workspace=ws)  # checks the status once
+    ms = time_reps(torch, lambda: sc.build_hash(cd, check_status=False, workspace=ws), reps)
+    return {"n_voxels": wl.n, "varying_key_bits": nbits, "radix_passes": min(4, (nbits + 10) // 11),
+            "bits_in_single_workgroup_pass": max(0, nbits - 44),
+            "ms_build_hash": ms}
+
+
 def block_count(coords):
     """Occupied 4x4x4 blocks of a voxel set (per object)."""
     c = coords.astype(np.int64)
@@ -529,6 +548,9 @@ def main():
             out["roofline"]["measured_peak"] = mp
             out["roofline"]["frac_of_measured_peak"] = gemm_tflops / mp
         note("ceilings measured")
+    if args.config == "L" and not args.no_wide_keys:
+        out["hash_wide_keys"] = wide_keys(sc, torch, wl)
+        note("wide-key hash measured")
     if not args.no_variants and wl.dtype == "bf16":
         out["variants"] = variants(sc, torch, wl, path, M, max(5, args.gemm_reps // 2))
         note("variants measured")

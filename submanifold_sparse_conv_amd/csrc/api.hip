@@ -133,7 +133,7 @@ int tr_sparseconv_build_hash(const int32_t* coords, int64_t n, void* workspace, 
   // No host wait: the digits of the sort are chosen on the device from the key
   // bits that vary; range and duplicate errors are left in the header for
   // tr_sparseconv_status.
-  hipError_t e = launch_pack(coords, n, keys[0], rows[0], parts, hdr, st);
+  hipError_t e = launch_pack(coords, n, keys[0], rows[0], keys[1], rows[1], parts, hdr, st);
   if (e != hipSuccess) return hip_fail(e, "build_hash: pack");
   const int cur = 1;
   if (n > 0) {

@@ -76,6 +76,7 @@ constexpr uint32_t kFlagCapacity = 4u;
 
 // One radix digit: key bits pos[0..nbits) (least significant first).
 constexpr int kMaxDigitBits = 11;
+constexpr int kSortPasses = 4;
 struct DigitBits {
   uint8_t pos[12];
   int32_t nbits;
@@ -88,8 +89,8 @@ struct alignas(256) HashHeader {
   uint32_t shift;               // 64 - log2(capacity)
   unsigned long long or_bits;   // OR of all voxel keys
   unsigned long long and_bits;  // AND of all voxel keys
-  DigitBits digit[3];           // the three radix passes over the key bits that vary
-  int32_t rest_n;               // varying bits beyond the three digits (sorted by radix_rest)
+  DigitBits digit[kSortPasses]; // the radix passes over the key bits that vary (empty ones first)
+  int32_t rest_n;               // varying bits beyond the passes' digits (sorted by radix_rest)
   uint8_t rest_pos[64];
 };
 

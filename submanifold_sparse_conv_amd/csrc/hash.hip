@@ -25,11 +25,15 @@ __device__ inline unsigned long long wave_and(unsigned long long v) {
   return v;
 }
 
-// keys[i] = key of coords[i]; rows[i] = i. Each block leaves the OR and AND of
-// its keys and an out-of-range flag in part[3 * block + {0, 1, 2}].
+// keys[i] = keys2[i] = key of coords[i]; rows[i] = rows2[i] = i (the first
+// radix pass that has bits reads whichever of the two buffers its parity
+// gives). Each block leaves the OR and AND of its keys and an out-of-range
+// flag in part[3 * block + {0, 1, 2}].
 __global__ __launch_bounds__(kThreads) void pack_keys(const int4* __restrict__ coords, int64_t n,
                                                       uint64_t* __restrict__ keys,
                                                       int32_t* __restrict__ rows,
+                                                      uint64_t* __restrict__ keys2,
+                                                      int32_t* __restrict__ rows2,
                                                       unsigned long long* __restrict__ part) {
   __shared__ unsigned long long s_or[kThreads / 64], s_and[kThreads / 64];
   __shared__ int s_bad[kThreads / 64];
@@ -43,6 +47,8 @@ __global__ __launch_bounds__(kThreads) void pack_keys(const int4* __restrict__ c
     const uint64_t key = b ? 0ull : make_key(uint32_t(c.x), uint32_t(c.y), uint32_t(c.z), uint32_t(c.w));
     keys[i] = key;
     rows[i] = int32_t(i);
+    keys2[i] = key;
+    rows2[i] = int32_t(i);
     k_or |= key;
     k_and &= key;
   }
@@ -70,11 +76,14 @@ __global__ __launch_bounds__(kThreads) void pack_keys(const int4* __restrict__ c
 }
 
 // Initialises the header: flags, an empty-table capacity, the OR / AND of all
-// keys, and the radix digits. The key bits that differ between keys (OR ^ AND)
-// are split, least significant first, into three digits of equal width (at
-// most kMaxDigitBits); any further bits go to the single-workgroup pass. The
-// header is assembled in LDS (varying bit b, of rank r among them, is written
-// by thread b) and copied out in 4-byte words.
+// keys, and the radix digits. The nv key bits that differ between keys (OR ^
+// AND) are split, least significant first, into P = ceil(nv / kMaxDigitBits)
+// digits (at most kSortPasses) of ceil(nv / P) bits, the last one the rest.
+// They go to the last P passes, so that the last pass that moves data is always
+// the last pass (its output buffer is the result); the passes before them have
+// no bits and return at once. Bits beyond kSortPasses * kMaxDigitBits go to the
+// single-workgroup pass. The header is assembled in LDS (varying bit b, of rank
+// r among them, is written by thread b) and copied out in 4-byte words.
 __global__ __launch_bounds__(kThreads) void reduce_bits(const unsigned long long* __restrict__ part,
                                                         int nparts, HashHeader* hdr) {
   static_assert(sizeof(HashHeader) % 4 == 0 && sizeof(HashHeader) / 4 <= kThreads, "header copy");
@@ -107,14 +116,17 @@ __global__ __launch_bounds__(kThreads) void reduce_bits(const unsigned long long
   }
   const unsigned long long vary = nparts > 0 ? (k_or ^ k_and) : 0ull;
   const int nv = __popcll(vary);
-  int w = (nv + 2) / 3;
-  if (w > kMaxDigitBits) w = kMaxDigitBits;
+  int np = (nv + kMaxDigitBits - 1) / kMaxDigitBits;  // passes with bits
+  if (np > kSortPasses) np = kSortPasses;
+  int w = np > 0 ? (nv + np - 1) / np : 0;
+  if (w > kMaxDigitBits) w = kMaxDigitBits;           // more bits than the passes hold: the rest pass
+  const int first = kSortPasses - np;                 // the first pass with bits
   if (tid < 64 && ((vary >> tid) & 1ull)) {  // then w >= 1
     const int r = __popcll(vary & ((1ull << tid) - 1ull));
-    if (r < 3 * w)
-      s_h.digit[r / w].pos[r % w] = uint8_t(tid);
+    if (r < np * w)
+      s_h.digit[first + r / w].pos[r % w] = uint8_t(tid);
     else
-      s_h.rest_pos[r - 3 * w] = uint8_t(tid);
+      s_h.rest_pos[r - np * w] = uint8_t(tid);
   }
   if (tid == 0) {
     s_h.flags = bad ? kFlagCoordRange : 0u;
@@ -123,11 +135,11 @@ __global__ __launch_bounds__(kThreads) void reduce_bits(const unsigned long long
     s_h.shift = 60;
     s_h.or_bits = k_or;
     s_h.and_bits = k_and;
-    for (int d = 0; d < 3; ++d) {
-      const int left = nv - d * w;
+    for (int d = 0; d < kSortPasses; ++d) {
+      const int left = d < first ? 0 : nv - (d - first) * w;
       s_h.digit[d].nbits = left < 0 ? 0 : (left > w ? w : left);
     }
-    s_h.rest_n = nv > 3 * w ? nv - 3 * w : 0;
+    s_h.rest_n = nv > np * w ? nv - np * w : 0;
   }
   __syncthreads();
   if (tid < HW) reinterpret_cast<uint32_t*>(hdr)[tid] = reinterpret_cast<const uint32_t*>(&s_h)[tid];
@@ -150,7 +162,8 @@ __global__ __launch_bounds__(kThreads) void radix_hist(const uint64_t* __restric
                                                        uint32_t* __restrict__ counts) {
   __shared__ uint32_t h[kMaxBuckets];
   __shared__ uint8_t s_pos[12];
-  const int nbits = hdr->digit[pass].nbits;
+  const int nbits = min(hdr->digit[pass].nbits, kMaxDigitBits);  // never more buckets than the LDS holds
+  if (nbits == 0) return;  // a pass without bits moves nothing
   const int nb = 1 << nbits;
   if (threadIdx.x < 12) s_pos[threadIdx.x] = hdr->digit[pass].pos[threadIdx.x];
   for (int d = threadIdx.x; d < nb; d += kThreads) h[d] = 0;
@@ -196,7 +209,9 @@ __global__ __launch_bounds__(kThreads) void radix_colscan(uint32_t* __restrict__
                                                           const HashHeader* __restrict__ hdr, int pass,
                                                           uint32_t* __restrict__ totals) {
   __shared__ uint32_t s_tmp[kThreads / 64];
-  const int nb = 1 << hdr->digit[pass].nbits;
+  const int nbits = min(hdr->digit[pass].nbits, kMaxDigitBits);
+  if (nbits == 0) return;
+  const int nb = 1 << nbits;
   for (int d = blockIdx.x; d < kMaxBuckets; d += gridDim.x) {
     if (d >= nb) {
       if (threadIdx.x == 0) totals[d] = 0;
@@ -244,7 +259,8 @@ __global__ __launch_bounds__(kThreads) void radix_scatter(const uint64_t* __rest
   __shared__ uint32_t wcount[kThreads / 64][kMaxBuckets];
   __shared__ uint32_t s_tmp[kThreads / 64];
   __shared__ uint8_t s_pos[12];
-  const int nbits = hdr->digit[pass].nbits;
+  const int nbits = min(hdr->digit[pass].nbits, kMaxDigitBits);  // never more buckets than the LDS holds
+  if (nbits == 0) return;
   const int nb = 1 << nbits;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -311,9 +327,10 @@ __global__ __launch_bounds__(kThreads) void radix_scatter(const uint64_t* __rest
   }
 }
 
-// The key bits beyond the three digits (only when more than 3 * kMaxDigitBits
-// bits vary): one workgroup sorts keys[0..n) stably by them, 8 bits per pass,
-// using tmp as the other buffer, and leaves the result in keys / rows.
+// The key bits beyond the passes' digits (only when more than kSortPasses *
+// kMaxDigitBits bits vary): one workgroup sorts keys[0..n) stably by them, 8
+// bits per pass, using tmp as the other buffer, and leaves the result in keys /
+// rows.
 __global__ __launch_bounds__(kThreads) void radix_rest(uint64_t* __restrict__ keys, int32_t* __restrict__ rows,
                                                        uint64_t* __restrict__ tkeys, int32_t* __restrict__ trows,
                                                        int64_t n, const HashHeader* __restrict__ hdr) {
@@ -384,8 +401,8 @@ __global__ __launch_bounds__(kThreads) void radix_rest(uint64_t* __restrict__ ke
 }
 
 // Each workgroup counts the block heads among its sorted keys (first key of
-// each 4x4x4 block) into part[block] and flags adjacent equal keys (duplicate
-// coordinates: equal keys are adjacent after the sort).
+// each 4x4x4 block) into part[workgroup] and flags adjacent equal keys
+// (duplicate coordinates: equal keys are adjacent after the sort).
 __global__ __launch_bounds__(kThreads) void block_count(const uint64_t* __restrict__ keys, int64_t n,
                                                         uint32_t* __restrict__ part, HashHeader* hdr) {
   __shared__ uint32_t s_cnt[kThreads / 64];
@@ -408,33 +425,32 @@ __global__ __launch_bounds__(kThreads) void block_count(const uint64_t* __restri
   }
 }
 
-// One workgroup: number of blocks, table capacity (power of two >= 2x blocks,
-// at least 16, at most max_cap) and hash shift, into the header.
-__global__ __launch_bounds__(kThreads) void block_size(const uint32_t* __restrict__ part, int nparts,
-                                                       uint32_t max_cap, HashHeader* hdr) {
+// Every workgroup adds up the block counts (nparts partials, from L2), derives
+// the table capacity (power of two >= 2x the blocks, at least 16, at most
+// max_cap) and hash shift, and clears its share of the slots; the first one
+// records them in the header. (One atomic counter for the blocks, or a
+// separate single-workgroup sizing kernel, each cost more at 0.4M voxels.)
+__global__ __launch_bounds__(kThreads) void block_clear(BlockSlot* __restrict__ slots, uint32_t max_cap,
+                                                        const uint32_t* __restrict__ part, int nparts,
+                                                        HashHeader* hdr) {
   __shared__ uint32_t s_cnt[kThreads / 64];
   uint32_t c = 0;
   for (int i = threadIdx.x; i < nparts; i += kThreads) c += part[i];
   for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o, 64);
   if ((threadIdx.x & 63) == 0) s_cnt[threadIdx.x >> 6] = c;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t nb = 0;
-    for (int w = 0; w < kThreads / 64; ++w) nb += s_cnt[w];
-    uint32_t cap = 16, lg = 4;
-    while (cap < 2u * nb && cap < max_cap) {
-      cap <<= 1;
-      ++lg;
-    }
+  uint32_t nb = 0;
+  for (int w = 0; w < kThreads / 64; ++w) nb += s_cnt[w];
+  uint32_t cap = 16, lg = 4;
+  while (cap < 2u * nb && cap < max_cap) {
+    cap <<= 1;
+    ++lg;
+  }
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
     hdr->nblocks = nb;
     hdr->cap_mask = cap - 1;
     hdr->shift = 64 - lg;
   }
-}
-
-__global__ __launch_bounds__(kThreads) void block_clear(BlockSlot* __restrict__ slots,
-                                                        const HashHeader* __restrict__ hdr) {
-  const uint32_t cap = hdr->cap_mask + 1u;
   for (uint32_t i = blockIdx.x * kThreads + threadIdx.x; i < cap; i += gridDim.x * kThreads) {
     uint4* p = reinterpret_cast<uint4*>(slots + i);
     p[0] = make_uint4(0xFFFFFFFFu, 0xFFFFFFFFu, 0u, 0u);
@@ -518,11 +534,11 @@ int64_t pack_partials(int64_t n) {
   return b < 1 ? 1 : (b < kPackBlocks ? b : kPackBlocks);
 }
 
-hipError_t launch_pack(const int32_t* coords, int64_t n, uint64_t* keys, int32_t* rows,
-                       unsigned long long* part, HashHeader* hdr, hipStream_t st) {
+hipError_t launch_pack(const int32_t* coords, int64_t n, uint64_t* keys, int32_t* rows, uint64_t* keys2,
+                       int32_t* rows2, unsigned long long* part, HashHeader* hdr, hipStream_t st) {
   const int nb = n > 0 ? int(pack_partials(n)) : 0;
   if (n > 0)
-    pack_keys<<<nb, kThreads, 0, st>>>(reinterpret_cast<const int4*>(coords), n, keys, rows, part);
+    pack_keys<<<nb, kThreads, 0, st>>>(reinterpret_cast<const int4*>(coords), n, keys, rows, keys2, rows2, part);
   reduce_bits<<<1, kThreads, 0, st>>>(part, nb, hdr);
   return hipGetLastError();
 }
@@ -533,8 +549,8 @@ hipError_t launch_sort(uint64_t* keys0, int32_t* rows0, uint64_t* keys1, int32_t
   uint64_t* k[2] = {keys0, keys1};
   int32_t* r[2] = {rows0, rows1};
   const int items = sort_items(n);
-  for (int pass = 0; pass < 3; ++pass) {
-    const int a = pass & 1;  // 0 -> 1 -> 0 -> 1
+  for (int pass = 0; pass < kSortPasses; ++pass) {
+    const int a = (pass + 1) & 1;  // 1 -> 0 -> 1 -> 0 -> 1: the last pass writes keys1
     switch (items) {
 #define TRSC_RADIX_PASS(IT)                                                                                   \
   case IT:                                                                                                    \
@@ -560,11 +576,10 @@ hipError_t launch_sort(uint64_t* keys0, int32_t* rows0, uint64_t* keys1, int32_t
 
 hipError_t launch_blocks(const uint64_t* keys, int64_t n, BlockSlot* slots, uint32_t max_cap,
                          uint32_t* part, HashHeader* hdr, hipStream_t st) {
-  const int nb = int(pack_partials(n));
+  const int nb = n > 0 ? int(pack_partials(n)) : 0;
   if (n > 0) block_count<<<nb, kThreads, 0, st>>>(keys, n, part, hdr);
-  block_size<<<1, kThreads, 0, st>>>(part, n > 0 ? nb : 0, max_cap, hdr);
   const uint32_t cb = (max_cap + kThreads - 1) / kThreads;
-  block_clear<<<cb < 2048u ? cb : 2048u, kThreads, 0, st>>>(slots, hdr);
+  block_clear<<<cb < 2048u ? cb : 2048u, kThreads, 0, st>>>(slots, max_cap, part, nb, hdr);
   if (n > 0) block_insert<<<grid_for(n, kThreads), kThreads, 0, st>>>(keys, n, slots, hdr);
   return hipGetLastError();
 }

@@ -12,12 +12,14 @@ namespace trsc {
 int64_t sort_blocks(int64_t n);    // radix-sort workgroups (tiles) for n keys
 int64_t pack_partials(int64_t n);  // partial triples (OR, AND, range flag) of the packing pass
 constexpr int kSortBuckets = 1 << kMaxDigitBits;
-// Packs keys / rows and initialises the header (flags, digits of the sort).
-hipError_t launch_pack(const int32_t* coords, int64_t n, uint64_t* keys, int32_t* rows,
-                       unsigned long long* part, HashHeader* hdr, hipStream_t st);
-// Three LSD radix passes (digits from the header) keys0 -> keys1 -> keys0 ->
-// keys1, then the single-workgroup pass over any further bits: the sorted keys
-// and rows end in keys1 / rows1. counts: sort_blocks(n) * kSortBuckets words.
+// Packs keys / rows (into both sort buffers) and initialises the header
+// (flags, digits of the sort).
+hipError_t launch_pack(const int32_t* coords, int64_t n, uint64_t* keys, int32_t* rows, uint64_t* keys2,
+                       int32_t* rows2, unsigned long long* part, HashHeader* hdr, hipStream_t st);
+// kSortPasses LSD radix passes (digits from the header; the leading ones may be
+// empty) keys1 -> keys0 -> keys1 -> keys0 -> keys1, then the single-workgroup
+// pass over any further bits: the sorted keys and rows end in keys1 / rows1.
+// counts: sort_blocks(n) * kSortBuckets words.
 hipError_t launch_sort(uint64_t* keys0, int32_t* rows0, uint64_t* keys1, int32_t* rows1, int64_t n,
                        const HashHeader* hdr, uint32_t* counts, uint32_t* totals, hipStream_t st);
 hipError_t launch_blocks(const uint64_t* keys, int64_t n, BlockSlot* slots, uint32_t max_cap,

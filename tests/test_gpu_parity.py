@@ -366,6 +366,22 @@ def test_large_sorts(n):
     np.testing.assert_array_equal(got, ref)
 
 
+def test_wide_keys_morton_order():
+    # 40 varying key bits (object ids spread over 16 bits): the last 7 go
+    # through the single-workgroup rest pass of the sort
+    wl = workload("L")
+    c = wl.coords.copy()
+    c[:, 0] = (np.arange(wl.n) % 64) * 1021
+    c = c[np.random.default_rng(5).permutation(wl.n)]
+    say(f"[wide keys] n={wl.n}")
+    h = sc.build_hash(torch.from_numpy(c).to(DEV))
+    perm = h.sorted_rows().cpu().numpy()
+    np.testing.assert_array_equal(perm, np.argsort(morton_keys_numpy(c), kind="stable"))
+    m = sc.build_kernel_map(h)
+    rows = sample_rows(wl.n, 20000, seed=9)
+    np.testing.assert_array_equal(m.nbr.cpu().numpy()[rows], oracle.kernel_map(c)[rows])
+
+
 def test_errors():
     say("[edge] error codes")
     dup = torch.tensor([[0, 1, 2, 3], [0, 5, 5, 5], [0, 1, 2, 3]], dtype=torch.int32, device=DEV)
