@@ -137,7 +137,7 @@ int tr_sparseconv_build_hash(const int32_t* coords, int64_t n, void* workspace, 
   if (e != hipSuccess) return hip_fail(e, "build_hash: pack");
   const int cur = 1;
   if (n > 0) {
-    e = launch_sort(keys[0], rows[0], keys[1], rows[1], n, hdr, counts, totals, st);
+    e = launch_sort(keys[0], rows[0], keys[1], rows[1], n, hdr, parts, counts, totals, st);
     if (e != hipSuccess) return hip_fail(e, "build_hash: sort");
   }
   e = launch_blocks(keys[cur], n, slots, l.cap, reinterpret_cast<uint32_t*>(parts), hdr, st);

@@ -13,8 +13,10 @@ namespace trsc {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kSmallDigitBits = 8;  // digits up to this width are ranked in one sweep per tile
 constexpr int kMaxSortWGs = 768;  // tiles per radix pass: keys per tile grow until n fits
-constexpr int kPackBlocks = 1024;         // grid of the key-packing pass
+constexpr int kPackBlocks = 256;          // grid of the key-packing pass (its partials are read by
+                                          // every workgroup of the first histogram pass)
 
 __device__ inline unsigned long long wave_or(unsigned long long v) {
   for (int o = 32; o > 0; o >>= 1) v |= __shfl_xor(v, o, 64);
@@ -75,22 +77,21 @@ __global__ __launch_bounds__(kThreads) void pack_keys(const int4* __restrict__ c
   }
 }
 
-// Initialises the header: flags, an empty-table capacity, the OR / AND of all
-// keys, and the radix digits. The nv key bits that differ between keys (OR ^
-// AND) are split, least significant first, into P = ceil(nv / kMaxDigitBits)
-// digits (at most kSortPasses) of ceil(nv / P) bits, the last one the rest.
-// They go to the last P passes, so that the last pass that moves data is always
-// the last pass (its output buffer is the result); the passes before them have
-// no bits and return at once. Bits beyond kSortPasses * kMaxDigitBits go to the
-// single-workgroup pass. The header is assembled in LDS (varying bit b, of rank
-// r among them, is written by thread b) and copied out in 4-byte words.
-__global__ __launch_bounds__(kThreads) void reduce_bits(const unsigned long long* __restrict__ part,
-                                                        int nparts, HashHeader* hdr) {
-  static_assert(sizeof(HashHeader) % 4 == 0 && sizeof(HashHeader) / 4 <= kThreads, "header copy");
+// The header: flags, an empty-table capacity, the OR / AND of all keys, and the
+// radix digits, from the packing pass's partials; built by a whole workgroup
+// in LDS (s_h). The nv key bits that differ between keys (OR ^ AND) are split,
+// least significant first, into P digits, the last one the rest: P =
+// ceil(nv / 8) digits of at most 8 bits while that is at most kSortPasses (the
+// scatter then ranks a tile in one sweep), else P = ceil(nv / kMaxDigitBits)
+// digits of ceil(nv / P) bits (at most kSortPasses). They go to the last P
+// passes, so that the last pass that moves data is always the last pass (its
+// output buffer is the result); the passes before them have no bits and return
+// at once. Bits beyond kSortPasses * kMaxDigitBits go to the single-workgroup
+// pass. Varying bit b, of rank r among them, is written by thread b.
+__device__ void build_header(const unsigned long long* __restrict__ part, int nparts, HashHeader& s_h) {
   constexpr int HW = int(sizeof(HashHeader) / 4);
   __shared__ unsigned long long s_or[kThreads / 64], s_and[kThreads / 64];
   __shared__ unsigned long long s_bad[kThreads / 64];
-  __shared__ HashHeader s_h;
   const int tid = threadIdx.x;
   unsigned long long k_or = 0, k_and = ~0ull, bad = 0;
   for (int i = tid; i < nparts; i += kThreads) {
@@ -116,11 +117,12 @@ __global__ __launch_bounds__(kThreads) void reduce_bits(const unsigned long long
   }
   const unsigned long long vary = nparts > 0 ? (k_or ^ k_and) : 0ull;
   const int nv = __popcll(vary);
-  int np = (nv + kMaxDigitBits - 1) / kMaxDigitBits;  // passes with bits
+  int np = (nv + kSmallDigitBits - 1) / kSmallDigitBits;  // passes with bits
+  if (np > kSortPasses) np = (nv + kMaxDigitBits - 1) / kMaxDigitBits;
   if (np > kSortPasses) np = kSortPasses;
   int w = np > 0 ? (nv + np - 1) / np : 0;
-  if (w > kMaxDigitBits) w = kMaxDigitBits;           // more bits than the passes hold: the rest pass
-  const int first = kSortPasses - np;                 // the first pass with bits
+  if (w > kMaxDigitBits) w = kMaxDigitBits;  // more bits than the passes hold: the rest pass
+  const int first = kSortPasses - np;        // the first pass with bits
   if (tid < 64 && ((vary >> tid) & 1ull)) {  // then w >= 1
     const int r = __popcll(vary & ((1ull << tid) - 1ull));
     if (r < np * w)
@@ -142,7 +144,21 @@ __global__ __launch_bounds__(kThreads) void reduce_bits(const unsigned long long
     s_h.rest_n = nv > np * w ? nv - np * w : 0;
   }
   __syncthreads();
-  if (tid < HW) reinterpret_cast<uint32_t*>(hdr)[tid] = reinterpret_cast<const uint32_t*>(&s_h)[tid];
+}
+
+__device__ inline void store_header(const HashHeader& s_h, HashHeader* hdr) {
+  static_assert(sizeof(HashHeader) % 4 == 0 && sizeof(HashHeader) / 4 <= kThreads, "header copy");
+  constexpr int HW = int(sizeof(HashHeader) / 4);
+  if (threadIdx.x < HW)
+    reinterpret_cast<uint32_t*>(hdr)[threadIdx.x] = reinterpret_cast<const uint32_t*>(&s_h)[threadIdx.x];
+}
+
+// The header of an empty voxel set (no histogram pass runs then).
+__global__ __launch_bounds__(kThreads) void reduce_bits(const unsigned long long* __restrict__ part,
+                                                        int nparts, HashHeader* hdr) {
+  __shared__ HashHeader s_h;
+  build_header(part, nparts, s_h);
+  store_header(s_h, hdr);
 }
 
 __device__ inline uint32_t digit_of(uint64_t key, const uint8_t* pos, int nbits) {
@@ -155,17 +171,30 @@ constexpr int kMaxBuckets = 1 << kMaxDigitBits;
 constexpr int kColscanWGs = 1024;  // radix_colscan workgroups (each scans digits g, g + 1024, ...)
 
 // counts[d * nblocks + block] = number of keys of this block's tile with digit d
-// (d below 2^nbits of the pass's digit).
+// (d below 2^nbits of the pass's digit). The histogram of pass 0, the first one
+// launched, also builds the header from the packing pass's partials: every
+// workgroup derives the digits itself, and workgroup 0 stores the header for
+// the kernels that follow.
 template <int ITEMS>
 __global__ __launch_bounds__(kThreads) void radix_hist(const uint64_t* __restrict__ keys, int64_t n,
-                                                       const HashHeader* __restrict__ hdr, int pass,
-                                                       uint32_t* __restrict__ counts) {
+                                                       HashHeader* hdr, int pass, uint32_t* __restrict__ counts,
+                                                       const unsigned long long* __restrict__ part, int nparts) {
   __shared__ uint32_t h[kMaxBuckets];
   __shared__ uint8_t s_pos[12];
-  const int nbits = min(hdr->digit[pass].nbits, kMaxDigitBits);  // never more buckets than the LDS holds
+  __shared__ HashHeader s_h;
+  int nbits;
+  if (pass == 0) {
+    build_header(part, nparts, s_h);
+    if (blockIdx.x == 0) store_header(s_h, hdr);
+    nbits = s_h.digit[0].nbits;
+    if (threadIdx.x < 12) s_pos[threadIdx.x] = s_h.digit[0].pos[threadIdx.x];
+  } else {
+    nbits = hdr->digit[pass].nbits;
+    if (threadIdx.x < 12) s_pos[threadIdx.x] = hdr->digit[pass].pos[threadIdx.x];
+  }
+  nbits = min(nbits, kMaxDigitBits);  // never more buckets than the LDS holds
   if (nbits == 0) return;  // a pass without bits moves nothing
   const int nb = 1 << nbits;
-  if (threadIdx.x < 12) s_pos[threadIdx.x] = hdr->digit[pass].pos[threadIdx.x];
   for (int d = threadIdx.x; d < nb; d += kThreads) h[d] = 0;
   __syncthreads();
   const int64_t base = int64_t(blockIdx.x) * (kThreads * ITEMS);
@@ -245,7 +274,18 @@ __global__ __launch_bounds__(kThreads) void radix_colscan(uint32_t* __restrict__
 }
 
 // Stable scatter of one radix pass. Inside a tile, key order is (iteration,
-// wave, lane); ranks among equal digits follow that order.
+// wave, lane); ranks among equal digits follow that order. Each thread first
+// holds the base offsets of its digits: the digits below them over all tiles
+// (scan of the totals) plus this digit in the tiles before this one (colscan).
+//
+// Digits of at most kSmallDigitBits bits: a wave ranks each of its keys among
+// the equal digits of the same (iteration, wave) with ballots, the first lane
+// of each digit stores the digit's count for that (iteration, wave), and the
+// thread that owns the digit turns its counts into positions in (iteration,
+// wave) order, items kChunk at a time: four barriers per chunk.
+// Wider digits (up to kMaxDigitBits, 2048 buckets, whose counts per (iteration,
+// wave) would not fit the LDS): the same ranking one iteration at a time, with
+// per-wave counts.
 template <int ITEMS>
 __global__ __launch_bounds__(kThreads) void radix_scatter(const uint64_t* __restrict__ kin,
                                                           const int32_t* __restrict__ vin,
@@ -254,10 +294,15 @@ __global__ __launch_bounds__(kThreads) void radix_scatter(const uint64_t* __rest
                                                           const HashHeader* __restrict__ hdr, int pass,
                                                           const uint32_t* __restrict__ offsets,
                                                           const uint32_t* __restrict__ totals) {
-  constexpr int PER = kMaxBuckets / kThreads;  // digits per thread in the digit scan
-  __shared__ uint32_t base_off[kMaxBuckets];
-  __shared__ uint32_t wcount[kThreads / 64][kMaxBuckets];
-  __shared__ uint32_t s_tmp[kThreads / 64];
+  constexpr int PER = kMaxBuckets / kThreads;  // digits per thread in the digit scan (wide digits)
+  constexpr int kSmall = 1 << kSmallDigitBits;
+  static_assert(kSmall == kThreads, "one small digit per thread");
+  constexpr int kChunk = ITEMS < 8 ? ITEMS : 8;  // items ranked per sweep (small digits)
+  constexpr int kWaves = kThreads / 64;
+  constexpr int kWideWords = kMaxBuckets * (1 + kWaves);
+  constexpr int kSmallWords = kChunk * kWaves * kSmall;
+  __shared__ uint32_t lds[kWideWords > kSmallWords ? kWideWords : kSmallWords];
+  __shared__ uint32_t s_tmp[kWaves];
   __shared__ uint8_t s_pos[12];
   const int nbits = min(hdr->digit[pass].nbits, kMaxDigitBits);  // never more buckets than the LDS holds
   if (nbits == 0) return;
@@ -265,6 +310,70 @@ __global__ __launch_bounds__(kThreads) void radix_scatter(const uint64_t* __rest
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   if (threadIdx.x < 12) s_pos[threadIdx.x] = hdr->digit[pass].pos[threadIdx.x];
+  const unsigned long long lt = (1ull << lane) - 1ull;
+  const int64_t base = int64_t(blockIdx.x) * (kThreads * ITEMS);
+  uint64_t kv[ITEMS];  // the tile's keys and rows, loaded before the first is ranked
+  int32_t vv[ITEMS];
+#pragma unroll
+  for (int it = 0; it < ITEMS; ++it) {
+    const int64_t i = base + it * kThreads + threadIdx.x;
+    kv[it] = i < n ? kin[i] : 0ull;
+    vv[it] = i < n ? vin[i] : 0;
+  }
+  if (nbits <= kSmallDigitBits) {
+    // thread d owns digit d: run = its next position
+    const int d_own = threadIdx.x;
+    const uint32_t tot = d_own < nb ? totals[d_own] : 0u;
+    uint32_t all;
+    uint32_t run = block_exclusive_scan(tot, s_tmp, &all);  // also makes s_pos visible
+    if (d_own < nb) run += offsets[int64_t(d_own) * gridDim.x + blockIdx.x];
+    uint32_t(*cnt)[kWaves][kSmall] = reinterpret_cast<uint32_t(*)[kWaves][kSmall]>(lds);
+#pragma unroll
+    for (int c0 = 0; c0 < ITEMS; c0 += kChunk) {
+      for (int q = threadIdx.x; q < kSmallWords; q += kThreads) lds[q] = 0u;
+      __syncthreads();
+      uint32_t dg[kChunk], rank[kChunk];
+#pragma unroll
+      for (int c = 0; c < kChunk; ++c) {
+        const int it = c0 + c;
+        const bool valid = base + it * kThreads + threadIdx.x < n;
+        const uint32_t d = valid ? digit_of(kv[it], s_pos, nbits) : 0u;
+        unsigned long long peers = __ballot(valid);
+        for (int j = 0; j < nbits; ++j) {
+          const bool bit = (d >> j) & 1u;
+          const unsigned long long bal = __ballot(bit);
+          peers &= bit ? bal : ~bal;
+        }
+        dg[c] = d;
+        rank[c] = valid ? __popcll(peers & lt) : ~0u;
+        if (valid && (peers & lt) == 0) cnt[c][wave][d] = __popcll(peers);
+      }
+      __syncthreads();
+      if (d_own < nb) {
+#pragma unroll
+        for (int c = 0; c < kChunk; ++c)
+#pragma unroll
+          for (int w = 0; w < kWaves; ++w) {
+            const uint32_t v = cnt[c][w][d_own];
+            cnt[c][w][d_own] = run;
+            run += v;
+          }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int c = 0; c < kChunk; ++c) {
+        if (rank[c] != ~0u) {
+          const uint32_t pos = cnt[c][wave][dg[c]] + rank[c];
+          kout[pos] = kv[c0 + c];
+          vout[pos] = vv[c0 + c];
+        }
+      }
+      __syncthreads();  // the next chunk clears the counts
+    }
+    return;
+  }
+  uint32_t* base_off = lds;
+  uint32_t(*wcount)[kMaxBuckets] = reinterpret_cast<uint32_t(*)[kMaxBuckets]>(lds + kMaxBuckets);
   // exclusive scan of the digit totals: thread t owns digits t*PER .. t*PER+PER-1
   uint32_t loc[PER], sum = 0;
 #pragma unroll
@@ -280,21 +389,11 @@ __global__ __launch_bounds__(kThreads) void radix_scatter(const uint64_t* __rest
     if (d < nb) base_off[d] = run + offsets[int64_t(d) * gridDim.x + blockIdx.x];
     run += loc[q];
   }
-  const unsigned long long lt = (1ull << lane) - 1ull;
-  const int64_t base = int64_t(blockIdx.x) * (kThreads * ITEMS);
-  uint64_t kv[ITEMS];  // the tile's keys and rows, loaded before the first is ranked
-  int32_t vv[ITEMS];
-#pragma unroll
-  for (int it = 0; it < ITEMS; ++it) {
-    const int64_t i = base + it * kThreads + threadIdx.x;
-    kv[it] = i < n ? kin[i] : 0ull;
-    vv[it] = i < n ? vin[i] : 0;
-  }
 #pragma unroll
   for (int it = 0; it < ITEMS; ++it) {
     for (int d = threadIdx.x; d < nb; d += kThreads)
 #pragma unroll
-      for (int w = 0; w < kThreads / 64; ++w) wcount[w][d] = 0;
+      for (int w = 0; w < kWaves; ++w) wcount[w][d] = 0;
     __syncthreads();
     const int64_t i = base + it * kThreads + threadIdx.x;
     const bool valid = i < n;
@@ -320,7 +419,7 @@ __global__ __launch_bounds__(kThreads) void radix_scatter(const uint64_t* __rest
     for (int dd = threadIdx.x; dd < nb; dd += kThreads) {
       uint32_t add = 0;
 #pragma unroll
-      for (int w = 0; w < kThreads / 64; ++w) add += wcount[w][dd];
+      for (int w = 0; w < kWaves; ++w) add += wcount[w][dd];
       base_off[dd] += add;
     }
     __syncthreads();
@@ -460,16 +559,22 @@ __global__ __launch_bounds__(kThreads) void block_clear(BlockSlot* __restrict__ 
 
 // The lane at each block head inserts {block key, occupancy bitmap, start}.
 // The bitmap is a segmented OR over the lanes of the wave that hold the same
-// block (sorted keys make a block one run of lanes); only a block that runs
-// past the wave's last lane is finished by its head with a short serial loop.
+// block (sorted keys make a block one run of lanes). A block that runs past the
+// wave's last lane continues in at most the next 63 keys: the wave loads those
+// 64 keys in one coalesced load and ORs in the bits of the leading ones that
+// belong to the same block.
 __global__ __launch_bounds__(kThreads) void block_insert(const uint64_t* __restrict__ keys, int64_t n,
                                                          BlockSlot* __restrict__ slots, HashHeader* hdr) {
   const int64_t t = int64_t(blockIdx.x) * kThreads + threadIdx.x;
   const int lane = threadIdx.x & 63;
+  const int64_t wave0 = t - lane;
+  if (wave0 >= n) return;  // whole wave past the end
   const bool valid = t < n;
   const uint64_t k = valid ? keys[t] : ~0ull;
   const uint64_t bkey = k >> 6;
-  const bool head = valid && (t == 0 || (keys[t - 1] >> 6) != bkey);
+  uint64_t prev = __shfl_up(k, 1, 64);
+  if (lane == 0) prev = t > 0 ? keys[t - 1] : ~k;
+  const bool head = valid && (t == 0 || (prev >> 6) != bkey);
   uint64_t bits = valid ? (1ull << (k & 63u)) : 0ull;
   for (int o = 1; o < 64; o <<= 1) {  // bits of lanes [lane, lane + 2o) of the same block
     const uint64_t ob = __shfl_down(bits, o, 64);
@@ -477,20 +582,23 @@ __global__ __launch_bounds__(kThreads) void block_insert(const uint64_t* __restr
     if (lane + o < 64 && okey == bkey) bits |= ob;
   }
   const uint64_t last_key = __shfl(bkey, 63, 64);
-  if (!head) return;
-  if (last_key == bkey) {  // the block may continue in the next wave
-    for (int64_t u = t - lane + 64; u < n && u < t + 64; ++u) {
-      const uint64_t ku = keys[u];
-      if ((ku >> 6) != bkey) break;
-      bits |= 1ull << (ku & 63u);
-    }
+  uint64_t tail = 0;  // bits of the last lane's block in the next wave's keys
+  if (wave0 + 64 < n) {  // wave-uniform: lane 63 is valid and keys follow
+    const int64_t u = wave0 + 64 + lane;
+    const bool uv = u < n;
+    const uint64_t ku = uv ? keys[u] : 0ull;
+    const unsigned long long other = __ballot(!uv || (ku >> 6) != last_key);
+    const int run = other ? __ffsll(static_cast<long long>(other)) - 1 : 64;
+    tail = wave_or(lane < run ? (1ull << (ku & 63u)) : 0ull);
   }
+  if (!head) return;
+  if (last_key == bkey) bits |= tail;
   const uint32_t mask = hdr->cap_mask, shift = hdr->shift;
   uint32_t s = home_slot(bkey, shift) & mask;
   for (uint32_t probe = 0; probe <= mask; ++probe) {
     unsigned long long* kp = reinterpret_cast<unsigned long long*>(&slots[s].bkey);
-    const unsigned long long prev = atomicCAS(kp, kEmptyKey, bkey);
-    if (prev == kEmptyKey) {
+    const unsigned long long prev_key = atomicCAS(kp, kEmptyKey, bkey);
+    if (prev_key == kEmptyKey) {
       slots[s].bits = bits;
       slots[s].start = uint32_t(t);
       return;
@@ -536,15 +644,18 @@ int64_t pack_partials(int64_t n) {
 
 hipError_t launch_pack(const int32_t* coords, int64_t n, uint64_t* keys, int32_t* rows, uint64_t* keys2,
                        int32_t* rows2, unsigned long long* part, HashHeader* hdr, hipStream_t st) {
-  const int nb = n > 0 ? int(pack_partials(n)) : 0;
-  if (n > 0)
-    pack_keys<<<nb, kThreads, 0, st>>>(reinterpret_cast<const int4*>(coords), n, keys, rows, keys2, rows2, part);
-  reduce_bits<<<1, kThreads, 0, st>>>(part, nb, hdr);
+  if (n > 0)  // the first histogram pass of the sort builds the header
+    pack_keys<<<int(pack_partials(n)), kThreads, 0, st>>>(reinterpret_cast<const int4*>(coords), n, keys, rows,
+                                                          keys2, rows2, part);
+  else
+    reduce_bits<<<1, kThreads, 0, st>>>(part, 0, hdr);
   return hipGetLastError();
 }
 
 hipError_t launch_sort(uint64_t* keys0, int32_t* rows0, uint64_t* keys1, int32_t* rows1, int64_t n,
-                       const HashHeader* hdr, uint32_t* counts, uint32_t* totals, hipStream_t st) {
+                       HashHeader* hdr, const unsigned long long* part, uint32_t* counts, uint32_t* totals,
+                       hipStream_t st) {
+  const int nparts = int(pack_partials(n));
   const int64_t nb = sort_blocks(n);
   uint64_t* k[2] = {keys0, keys1};
   int32_t* r[2] = {rows0, rows1};
@@ -554,7 +665,7 @@ hipError_t launch_sort(uint64_t* keys0, int32_t* rows0, uint64_t* keys1, int32_t
     switch (items) {
 #define TRSC_RADIX_PASS(IT)                                                                                   \
   case IT:                                                                                                    \
-    radix_hist<IT><<<unsigned(nb), kThreads, 0, st>>>(k[a], n, hdr, pass, counts);                            \
+    radix_hist<IT><<<unsigned(nb), kThreads, 0, st>>>(k[a], n, hdr, pass, counts, part, nparts);              \
     radix_colscan<<<kColscanWGs, kThreads, 0, st>>>(counts, int(nb), hdr, pass, totals);                      \
     radix_scatter<IT><<<unsigned(nb), kThreads, 0, st>>>(k[a], r[a], k[a ^ 1], r[a ^ 1], n, hdr, pass, counts, \
                                                          totals);                                             \

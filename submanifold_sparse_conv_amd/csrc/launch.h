@@ -12,8 +12,9 @@ namespace trsc {
 int64_t sort_blocks(int64_t n);    // radix-sort workgroups (tiles) for n keys
 int64_t pack_partials(int64_t n);  // partial triples (OR, AND, range flag) of the packing pass
 constexpr int kSortBuckets = 1 << kMaxDigitBits;
-// Packs keys / rows (into both sort buffers) and initialises the header
-// (flags, digits of the sort).
+// Packs keys / rows (into both sort buffers) and the partials (OR, AND, range
+// flag) from which the sort's first histogram pass builds the header (flags,
+// digits of the sort); for n = 0 it writes the header itself.
 hipError_t launch_pack(const int32_t* coords, int64_t n, uint64_t* keys, int32_t* rows, uint64_t* keys2,
                        int32_t* rows2, unsigned long long* part, HashHeader* hdr, hipStream_t st);
 // kSortPasses LSD radix passes (digits from the header; the leading ones may be
@@ -21,7 +22,8 @@ hipError_t launch_pack(const int32_t* coords, int64_t n, uint64_t* keys, int32_t
 // pass over any further bits: the sorted keys and rows end in keys1 / rows1.
 // counts: sort_blocks(n) * kSortBuckets words.
 hipError_t launch_sort(uint64_t* keys0, int32_t* rows0, uint64_t* keys1, int32_t* rows1, int64_t n,
-                       const HashHeader* hdr, uint32_t* counts, uint32_t* totals, hipStream_t st);
+                       HashHeader* hdr, const unsigned long long* part, uint32_t* counts, uint32_t* totals,
+                       hipStream_t st);
 hipError_t launch_blocks(const uint64_t* keys, int64_t n, BlockSlot* slots, uint32_t max_cap,
                          uint32_t* part, HashHeader* hdr, hipStream_t st);
 hipError_t launch_lookup(const TableRef& t, const int32_t* q, int64_t nq, int32_t* out, hipStream_t st);
