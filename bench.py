@@ -2,7 +2,9 @@
 """Benchmark of the submanifold sparse 3D convolution hot path on one MI355X.
 
 One step = the whole path over one synthetic voxel set: build_hash (Morton
-sort + open-addressing table), build_kernel_map (27 neighbours per voxel),
+order + open-addressing table of 4x4x4 blocks, given the workload's grid;
+`hash_without_grid_ms` times the build without it), build_kernel_map (27
+neighbours per voxel),
 pack_weights and the gather-GEMM (forward_packed). Inputs are resident in HBM
 before the timed region. Prints ONE JSON line.
 
@@ -131,15 +133,25 @@ class TimingEvent:
             TimingEvent._hip.hipEventDestroy(self.e)
 
 
-class Path:
-    """Pre-allocated buffers and one step of the hot path."""
+def grid_of(wl):
+    """(log2 of the grid side, object count) of a workload: the grid its
+    coordinates lie in, which the hash build is given."""
+    g = max(int(wl.D - 1).bit_length(), 2)
+    return g, max(int(wl.B), 1)
 
-    def __init__(self, sc, torch, coords, x, w):
+
+class Path:
+    """Pre-allocated buffers and one step of the hot path. The hash is built
+    with the workload's grid (build_hash(grid_log2=..., batch=...)), as a
+    decoder level knows its resolution."""
+
+    def __init__(self, sc, torch, coords, x, w, grid):
         self.sc, self.torch = sc, torch
         self.coords, self.x, self.w = coords, x, w
+        self.grid = grid
         n = int(coords.shape[0])
         L = sc._lib.lib()
-        self.hws = sc.Workspace(L.tr_sparseconv_hash_workspace_bytes(n), coords.device)
+        self.hws = sc.Workspace(L.tr_sparseconv_hash_grid_workspace_bytes(n, grid[0], grid[1]), coords.device)
         self.kws = sc.Workspace(L.tr_sparseconv_kmap_workspace_bytes(n), coords.device)
         self.nbr = torch.empty((n, 27), dtype=torch.int32, device=coords.device)
         self.y = torch.empty((n, int(w.shape[2])), dtype=x.dtype, device=x.device)
@@ -151,7 +163,8 @@ class Path:
         sc = self.sc
         if ev is not None:
             ev[0].record()
-        self.h = sc.build_hash(self.coords, check_status=False, workspace=self.hws)
+        self.h = sc.build_hash(self.coords, check_status=False, workspace=self.hws, grid_log2=self.grid[0],
+                               batch=self.grid[1])
         if ev is not None:
             ev[1].record()
         self.m = sc.build_kernel_map(self.h, nbr=self.nbr, workspace=self.kws)
@@ -252,10 +265,12 @@ def layer_chain(sc, torch, wl, blocks, ch, reps=5):
           for _ in range(2 * blocks)]
     bs = [torch.randn(ch, device=dev, generator=g) * 0.1 for _ in range(2 * blocks)]
 
+    fg, fb = grid_of(wl)[0] + 1, grid_of(wl)[1]  # the fine level: twice the side
+
     def level():
         fine, children = sc.subdivide(coarse)
         x = sc.channel2spatial(children, xc, int(fine.shape[0]))
-        h = sc.build_hash(fine, check_status=False)
+        h = sc.build_hash(fine, check_status=False, grid_log2=fg, batch=fb)
         m = sc.build_kernel_map(h)
         t = torch.empty_like(x)
         for b in range(blocks):
@@ -274,7 +289,8 @@ def layer_chain(sc, torch, wl, blocks, ch, reps=5):
         level()
         torch.cuda.synchronize()
         t_level.append((time.perf_counter() - t0) * 1e3)
-    t_map = time_reps(torch, lambda: sc.build_kernel_map(sc.build_hash(fine, check_status=False)), reps)
+    t_map = time_reps(torch, lambda: sc.build_kernel_map(sc.build_hash(fine, check_status=False, grid_log2=fg,
+                                                                        batch=fb)), reps)
     t = torch.empty_like(x)
     t_conv = time_reps(torch, lambda: sc.forward_fused(m, x, ws[0], bias=bs[0], act="silu", out=t), 4 * reps)
     flops = 2.0 * ch * ch * M
@@ -388,7 +404,15 @@ def hash_map_bytes(n, nblocks):
     return blk, vox
 
 
-def config_record(name, wl, M, phases, t_fwd_steady):
+def hash_without_grid(sc, torch, coords, reps=50):
+    """build_hash over the same voxels without the grid (the radix-sorted
+    build), ms back to back."""
+    L = sc._lib.lib()
+    ws = sc.Workspace(L.tr_sparseconv_hash_workspace_bytes(int(coords.shape[0])), coords.device)
+    return time_reps(torch, lambda: sc.build_hash(coords, check_status=False, workspace=ws), reps)
+
+
+def config_record(name, wl, M, phases, t_fwd_steady, t_hash_no_grid=None):
     """One config's path phases (ms), steady forward, effective TFLOP/s and
     fraction of the peak of its arithmetic, and the topology passes' GB/s."""
     t_hash, t_map, t_pack, t_gemm = (float(v) for v in phases)
@@ -404,8 +428,10 @@ def config_record(name, wl, M, phases, t_fwd_steady):
                 "hash_gbs": b["hash"] / (t_hash * 1e-3) / 1e9, "map_gbs": b["map"] / (t_map * 1e-3) / 1e9}
     return {"workload": WORKLOAD_NAMES[name], "n_voxels": wl.n, "pairs_M": M, "c_in": wl.c_in,
             "c_out": wl.c_out, "dtype": "bf16" if half else "f32",
+            "grid": {"log2_side": grid_of(wl)[0], "objects": grid_of(wl)[1]},
             "ms": {"build_hash": t_hash, "build_kernel_map": t_map, "pack_weights": t_pack,
-                   "gather_gemm_in_path": t_gemm, "forward_steady": t_fwd_steady},
+                   "gather_gemm_in_path": t_gemm, "forward_steady": t_fwd_steady,
+                   "build_hash_without_grid": t_hash_no_grid},
             "voxels_per_s_path": wl.n / ((t_hash + t_map + t_pack + t_gemm) * 1e-3),
             "voxels_per_s_forward": wl.n / (t_fwd_steady * 1e-3),
             "effective_tflops": tf,
@@ -501,7 +527,7 @@ def main():
 
     wl = W.make(args.config)
     coords, x, w = to_device(wl, torch)
-    path = Path(sc, torch, coords, x, w)
+    path = Path(sc, torch, coords, x, w, grid_of(wl))
     for _ in range(args.warmup):
         path.step()
     torch.cuda.synchronize()
@@ -541,7 +567,8 @@ def main():
 
     # the committed counters were taken on the 256^3 config's launch
     traffic = traffic_entry() if args.config == "L" else None
-    main_cfg = config_record(args.config, wl, M, (t_hash, t_map, t_pack, t_gemm), t_gemm_ss)
+    main_cfg = config_record(args.config, wl, M, (t_hash, t_map, t_pack, t_gemm), t_gemm_ss,
+                             hash_without_grid(sc, torch, coords))
     if wl.dtype == "bf16":
         roof = {"kernel": "fwd_rows (gather-GEMM)", "bound": "mfma", "achieved": gemm_tflops,
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": gemm_tflops / PEAK_BF16_TFLOPS,
@@ -574,6 +601,7 @@ def main():
         "forward": {"voxels_per_s_steady": wl.n / (t_gemm_ss * 1e-3), "ms_steady": t_gemm_ss,
                     "effective_tflops": flops / (t_gemm_ss * 1e-3) / 1e12,
                     "frac_bf16_peak": flops / (t_gemm_ss * 1e-3) / 1e12 / PEAK_BF16_TFLOPS},
+        "hash_without_grid_ms": main_cfg["ms"]["build_hash_without_grid"],
         "hash_map_hbm": main_cfg["hash_map_hbm"],
         "roofline": roof,
     }
@@ -581,7 +609,7 @@ def main():
     for name in [a for a in args.also.split(",") if a and a != args.config]:
         wl2 = W.make(name)
         c2, x2, w2 = to_device(wl2, torch)
-        p2 = Path(sc, torch, c2, x2, w2)
+        p2 = Path(sc, torch, c2, x2, w2, grid_of(wl2))
         for _ in range(3):
             p2.step()
         torch.cuda.synchronize()
@@ -594,7 +622,8 @@ def main():
         ph2 = np.array([[ev[i][j].elapsed_time(ev[i][j + 1]) for j in range(4)] for i in range(reps)])
         tss = measure_forward_only(sc, torch, p2, args.gemm_reps) if args.gemm_reps > 0 else float(
             np.median(ph2[:, 3]))
-        configs[name] = config_record(name, wl2, M2, tuple(np.median(ph2, axis=0)), tss)
+        configs[name] = config_record(name, wl2, M2, tuple(np.median(ph2, axis=0)), tss,
+                                      hash_without_grid(sc, torch, c2))
         del p2, c2, x2, w2
         note(f"config {name} measured")
     out["configs"] = configs

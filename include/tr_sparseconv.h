@@ -105,6 +105,23 @@ size_t tr_sparseconv_hash_workspace_bytes(int64_t n);
 int tr_sparseconv_build_hash(const int32_t* coords, int64_t n, void* workspace,
                              size_t ws_bytes, void* stream, tr_sc_hash** out);
 
+/* The same hash for voxels in a known grid: spatial components in
+ * [0, 2^grid_log2), object index b in [0, batch) -- the resolution of a level,
+ * which every level of the pages' decoders has ("Running TRELLIS.2 on a Mac
+ * (1/3)", the resolutions of the cascade). The result is the same as
+ * tr_sparseconv_build_hash's: the same Morton order (tr_sparseconv_hash_sorted_rows),
+ * the same lookups and kernel map. When the grid's occupancy bitmap
+ * (batch * 2^(3 grid_log2) bits) is at most 32 MB, the order comes from that
+ * bitmap (a voxel's position is the number of occupied cells before its own)
+ * in five kernels instead of the radix sort's passes; otherwise this is
+ * tr_sparseconv_build_hash with the grid's bounds as the range check.
+ * grid_log2 in [2, 16], batch in [1, 65536] (else TR_SC_ERR_INVALID_ARG).
+ * Coordinates outside the grid and duplicates are reported by
+ * tr_sparseconv_status as TR_SC_ERR_COORD_RANGE and TR_SC_ERR_DUPLICATE. */
+size_t tr_sparseconv_hash_grid_workspace_bytes(int64_t n, int grid_log2, int batch);
+int tr_sparseconv_build_hash_grid(const int32_t* coords, int64_t n, int grid_log2, int batch,
+                                  void* workspace, size_t ws_bytes, void* stream, tr_sc_hash** out);
+
 /* Device-found errors of the build, read from the workspace status word:
  * TR_SC_OK, TR_SC_ERR_COORD_RANGE, TR_SC_ERR_DUPLICATE or TR_SC_ERR_CAPACITY.
  * Synchronises `stream`. */

@@ -70,21 +70,32 @@ def _require(t: torch.Tensor, name: str, dtype=None, ndim=None):
 
 
 class HashTable:
-    """Coordinate hash (tr_sparseconv_build_hash). Keeps its workspace alive."""
+    """Coordinate hash (tr_sparseconv_build_hash, or tr_sparseconv_build_hash_grid
+    when the grid is given: spatial components < 2^grid_log2, object index <
+    batch). Keeps its workspace alive."""
 
     def __init__(self, coords: torch.Tensor, check_status: bool = True,
-                 workspace: Workspace | None = None):
+                 workspace: Workspace | None = None, grid_log2: int | None = None, batch: int = 1):
         _require(coords, "coords", torch.int32, 2)
         if coords.shape[1] != 4:
             raise ValueError(f"coords must be [N, 4], got {tuple(coords.shape)}")
         L = _lib.lib()
         self.device = coords.device
         self.n = int(coords.shape[0])
-        self._ws = _workspace(L.tr_sparseconv_hash_workspace_bytes(self.n), self.device, workspace)
         h = ctypes.c_void_p()
-        with torch.cuda.device(self.device):
-            check(L.tr_sparseconv_build_hash(_ptr(coords), self.n, self._ws.ptr, self._ws.nbytes,
-                                             _stream(self.device), ctypes.byref(h)))
+        if grid_log2 is None:
+            self._ws = _workspace(L.tr_sparseconv_hash_workspace_bytes(self.n), self.device, workspace)
+            with torch.cuda.device(self.device):
+                check(L.tr_sparseconv_build_hash(_ptr(coords), self.n, self._ws.ptr, self._ws.nbytes,
+                                                 _stream(self.device), ctypes.byref(h)))
+        else:
+            need = L.tr_sparseconv_hash_grid_workspace_bytes(self.n, int(grid_log2), int(batch))
+            if need == 0:
+                raise ValueError(f"grid_log2 = {grid_log2} must be in [2, 16] and batch = {batch} in [1, 65536]")
+            self._ws = _workspace(need, self.device, workspace)
+            with torch.cuda.device(self.device):
+                check(L.tr_sparseconv_build_hash_grid(_ptr(coords), self.n, int(grid_log2), int(batch), self._ws.ptr,
+                                                      self._ws.nbytes, _stream(self.device), ctypes.byref(h)))
         self._h = h
         self._destroy = L.tr_sparseconv_hash_destroy
         if check_status:
@@ -161,8 +172,11 @@ class KernelMap:
 
 
 def build_hash(coords: torch.Tensor, check_status: bool = True,
-               workspace: Workspace | None = None) -> HashTable:
-    return HashTable(coords, check_status=check_status, workspace=workspace)
+               workspace: Workspace | None = None, grid_log2: int | None = None, batch: int = 1) -> HashTable:
+    """grid_log2 (with batch): the grid the coordinates lie in, when the caller
+    knows it (the resolution of a level); the hash is the same, built from an
+    occupancy bitmap when that fits (tr_sparseconv_build_hash_grid)."""
+    return HashTable(coords, check_status=check_status, workspace=workspace, grid_log2=grid_log2, batch=batch)
 
 
 def build_kernel_map(h: HashTable, nbr: torch.Tensor | None = None,

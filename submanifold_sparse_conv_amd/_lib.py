@@ -44,6 +44,8 @@ SIGNATURES = [
     ("tr_sparseconv_last_error", ctypes.c_char_p, []),
     ("tr_sparseconv_hash_workspace_bytes", _SZ, [_I64]),
     ("tr_sparseconv_build_hash", _I, [_P, _I64, _P, _SZ, _P, _PP]),
+    ("tr_sparseconv_hash_grid_workspace_bytes", _SZ, [_I64, _I, _I]),
+    ("tr_sparseconv_build_hash_grid", _I, [_P, _I64, _I, _I, _P, _SZ, _P, _PP]),
     ("tr_sparseconv_status", _I, [_P, _P]),
     ("tr_sparseconv_hash_size", _I64, [_P]),
     ("tr_sparseconv_hash_lookup", _I, [_P, _P, _I64, _P, _P]),

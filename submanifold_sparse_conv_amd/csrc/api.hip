@@ -106,20 +106,20 @@ size_t tr_sparseconv_hash_workspace_bytes(int64_t n) {
   return hash_layout(n).total;
 }
 
-int tr_sparseconv_build_hash(const int32_t* coords, int64_t n, void* workspace, size_t ws_bytes,
-                             void* stream, tr_sc_hash** out) {
-  if (out == nullptr) return fail(TR_SC_ERR_INVALID_ARG, "build_hash: out is NULL");
+static int build_hash_radix(const char* who, const int32_t* coords, int64_t n, uint32_t lim, uint32_t blim,
+                            void* workspace, size_t ws_bytes, void* stream, tr_sc_hash** out) {
+  if (out == nullptr) return fail(TR_SC_ERR_INVALID_ARG, "%s: out is NULL", who);
   *out = nullptr;
-  if (n < 0 || n > kMaxN) return fail(TR_SC_ERR_INVALID_ARG, "build_hash: n = %lld out of [0, 2^30]", (long long)n);
-  if (n > 0 && coords == nullptr) return fail(TR_SC_ERR_INVALID_ARG, "build_hash: coords is NULL");
-  if (workspace == nullptr) return fail(TR_SC_ERR_INVALID_ARG, "build_hash: workspace is NULL");
+  if (n < 0 || n > kMaxN) return fail(TR_SC_ERR_INVALID_ARG, "%s: n = %lld out of [0, 2^30]", who, (long long)n);
+  if (n > 0 && coords == nullptr) return fail(TR_SC_ERR_INVALID_ARG, "%s: coords is NULL", who);
+  if (workspace == nullptr) return fail(TR_SC_ERR_INVALID_ARG, "%s: workspace is NULL", who);
   if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
-    return fail(TR_SC_ERR_INVALID_ARG, "build_hash: workspace not 256-byte aligned");
+    return fail(TR_SC_ERR_INVALID_ARG, "%s: workspace not 256-byte aligned", who);
   if (reinterpret_cast<uintptr_t>(coords) % 16 != 0)
-    return fail(TR_SC_ERR_INVALID_ARG, "build_hash: coords not 16-byte aligned");
+    return fail(TR_SC_ERR_INVALID_ARG, "%s: coords not 16-byte aligned", who);
   const HashLayout l = hash_layout(n);
   if (ws_bytes < l.total)
-    return fail(TR_SC_ERR_WORKSPACE, "build_hash: workspace %zu bytes < %zu needed", ws_bytes, l.total);
+    return fail(TR_SC_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu needed", who, ws_bytes, l.total);
   hipStream_t st = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
   HashHeader* hdr = reinterpret_cast<HashHeader*>(ws + l.hdr);
@@ -133,15 +133,15 @@ int tr_sparseconv_build_hash(const int32_t* coords, int64_t n, void* workspace, 
   // No host wait: the digits of the sort are chosen on the device from the key
   // bits that vary; range and duplicate errors are left in the header for
   // tr_sparseconv_status.
-  hipError_t e = launch_pack(coords, n, keys[0], rows[0], keys[1], rows[1], parts, hdr, st);
-  if (e != hipSuccess) return hip_fail(e, "build_hash: pack");
+  hipError_t e = launch_pack(coords, n, lim, blim, keys[0], rows[0], keys[1], rows[1], parts, hdr, st);
+  if (e != hipSuccess) return hip_fail(e, who);
   const int cur = 1;
   if (n > 0) {
     e = launch_sort(keys[0], rows[0], keys[1], rows[1], n, hdr, parts, counts, totals, st);
-    if (e != hipSuccess) return hip_fail(e, "build_hash: sort");
+    if (e != hipSuccess) return hip_fail(e, who);
   }
   e = launch_blocks(keys[cur], n, slots, l.cap, reinterpret_cast<uint32_t*>(parts), hdr, st);
-  if (e != hipSuccess) return hip_fail(e, "build_hash: block table");
+  if (e != hipSuccess) return hip_fail(e, who);
 
   tr_sc_hash* h = new tr_sc_hash;
   h->magic = kHashMagic;
@@ -149,6 +149,106 @@ int tr_sparseconv_build_hash(const int32_t* coords, int64_t n, void* workspace, 
   h->hdr = hdr;
   h->table = TableRef{slots, hdr, rows[cur]};
   h->skeys = keys[cur];
+  *out = h;
+  return TR_SC_OK;
+}
+
+int tr_sparseconv_build_hash(const int32_t* coords, int64_t n, void* workspace, size_t ws_bytes,
+                             void* stream, tr_sc_hash** out) {
+  return build_hash_radix("build_hash", coords, n, 0x10000u, 0x10000u, workspace, ws_bytes, stream, out);
+}
+
+// The occupancy-bitmap build applies when the grid's bitmap is at most 32 MB
+// (4M words of 64 cells).
+constexpr int64_t kDenseMaxWords = int64_t(1) << 22;
+static int64_t grid_words(int g, int batch) {  // 64-cell words of a batch x (2^g)^3 grid, g >= 2
+  return int64_t(batch) << (3 * g - 6);
+}
+static bool grid_dense(int64_t n, int g, int batch) {
+  return n > 0 && (3 * g - 6 <= 22) && grid_words(g, batch) <= kDenseMaxWords;
+}
+
+// Grid workspace (bitmap build): header | keys[n] | rows[n] | bitmap | word
+// prefixes | chunk totals | chunk block counts | block slots.
+struct GridLayout {
+  size_t hdr, keys, rows, bitmap, wpre, ctot, cblk, slots, total;
+  int lgc, nchunks;
+  uint32_t cap;
+};
+static GridLayout grid_layout(int64_t n, int g, int batch) {
+  GridLayout l{};
+  const int64_t words = grid_words(g, batch);
+  l.lgc = dense_chunk_log2(words);
+  l.nchunks = int((words + (int64_t(1) << l.lgc) - 1) >> l.lgc);
+  const size_t w = size_t(l.nchunks) << l.lgc;
+  size_t o = 0;
+  l.hdr = o;
+  o += align_up(sizeof(HashHeader), 256);
+  l.keys = o;
+  o += align_up(size_t(n) * 8, 256);
+  l.rows = o;
+  o += align_up(size_t(n) * 4, 256);
+  l.bitmap = o;
+  o += align_up(w * 8, 256);
+  l.wpre = o;
+  o += align_up(w * 4, 256);
+  l.ctot = o;
+  o += align_up(size_t(l.nchunks) * 4, 256);
+  l.cblk = o;
+  o += align_up(size_t(l.nchunks) * 4, 256);
+  l.cap = table_capacity(n < words ? n : words);
+  l.slots = o;
+  o += size_t(l.cap) * sizeof(BlockSlot);
+  l.total = o;
+  return l;
+}
+
+static bool grid_args_ok(int grid_log2, int batch) {
+  return grid_log2 >= 2 && grid_log2 <= 16 && batch >= 1 && batch <= 65536;
+}
+
+size_t tr_sparseconv_hash_grid_workspace_bytes(int64_t n, int grid_log2, int batch) {
+  if (n < 0 || n > kMaxN || !grid_args_ok(grid_log2, batch)) return 0;
+  return grid_dense(n, grid_log2, batch) ? grid_layout(n, grid_log2, batch).total : hash_layout(n).total;
+}
+
+int tr_sparseconv_build_hash_grid(const int32_t* coords, int64_t n, int grid_log2, int batch, void* workspace,
+                                  size_t ws_bytes, void* stream, tr_sc_hash** out) {
+  if (out == nullptr) return fail(TR_SC_ERR_INVALID_ARG, "build_hash_grid: out is NULL");
+  *out = nullptr;
+  if (!grid_args_ok(grid_log2, batch))
+    return fail(TR_SC_ERR_INVALID_ARG, "build_hash_grid: grid_log2 = %d outside [2, 16] or batch = %d outside [1, 65536]",
+                grid_log2, batch);
+  if (n < 0 || n > kMaxN)
+    return fail(TR_SC_ERR_INVALID_ARG, "build_hash_grid: n = %lld out of [0, 2^30]", (long long)n);
+  if (!grid_dense(n, grid_log2, batch))
+    return build_hash_radix("build_hash_grid", coords, n, 1u << grid_log2, uint32_t(batch), workspace, ws_bytes,
+                            stream, out);
+  if (coords == nullptr) return fail(TR_SC_ERR_INVALID_ARG, "build_hash_grid: coords is NULL");
+  if (workspace == nullptr) return fail(TR_SC_ERR_INVALID_ARG, "build_hash_grid: workspace is NULL");
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+    return fail(TR_SC_ERR_INVALID_ARG, "build_hash_grid: workspace not 256-byte aligned");
+  if (reinterpret_cast<uintptr_t>(coords) % 16 != 0)
+    return fail(TR_SC_ERR_INVALID_ARG, "build_hash_grid: coords not 16-byte aligned");
+  const GridLayout l = grid_layout(n, grid_log2, batch);
+  if (ws_bytes < l.total)
+    return fail(TR_SC_ERR_WORKSPACE, "build_hash_grid: workspace %zu bytes < %zu needed", ws_bytes, l.total);
+  char* ws = static_cast<char*>(workspace);
+  HashHeader* hdr = reinterpret_cast<HashHeader*>(ws + l.hdr);
+  uint64_t* keys = reinterpret_cast<uint64_t*>(ws + l.keys);
+  int32_t* rows = reinterpret_cast<int32_t*>(ws + l.rows);
+  BlockSlot* slots = reinterpret_cast<BlockSlot*>(ws + l.slots);
+  const hipError_t e = launch_dense_hash(
+      coords, n, grid_log2, batch, reinterpret_cast<unsigned long long*>(ws + l.bitmap), l.lgc, l.nchunks,
+      reinterpret_cast<uint32_t*>(ws + l.wpre), reinterpret_cast<uint32_t*>(ws + l.ctot),
+      reinterpret_cast<uint32_t*>(ws + l.cblk), keys, rows, slots, l.cap, hdr, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "build_hash_grid");
+  tr_sc_hash* h = new tr_sc_hash;
+  h->magic = kHashMagic;
+  h->n = n;
+  h->hdr = hdr;
+  h->table = TableRef{slots, hdr, rows};
+  h->skeys = keys;
   *out = h;
   return TR_SC_OK;
 }

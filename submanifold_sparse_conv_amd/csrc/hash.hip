@@ -30,9 +30,10 @@ __device__ inline unsigned long long wave_and(unsigned long long v) {
 // keys[i] = keys2[i] = key of coords[i]; rows[i] = rows2[i] = i (the first
 // radix pass that has bits reads whichever of the two buffers its parity
 // gives). Each block leaves the OR and AND of its keys and an out-of-range
-// flag in part[3 * block + {0, 1, 2}].
+// flag (a spatial component >= lim or an object index >= blim) in
+// part[3 * block + {0, 1, 2}].
 __global__ __launch_bounds__(kThreads) void pack_keys(const int4* __restrict__ coords, int64_t n,
-                                                      uint64_t* __restrict__ keys,
+                                                      uint32_t lim, uint32_t blim, uint64_t* __restrict__ keys,
                                                       int32_t* __restrict__ rows,
                                                       uint64_t* __restrict__ keys2,
                                                       int32_t* __restrict__ rows2,
@@ -44,7 +45,7 @@ __global__ __launch_bounds__(kThreads) void pack_keys(const int4* __restrict__ c
   for (int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x; i < n;
        i += int64_t(gridDim.x) * kThreads) {
     const int4 c = coords[i];
-    const bool b = (uint32_t(c.x) | uint32_t(c.y) | uint32_t(c.z) | uint32_t(c.w)) > 0xFFFFu;
+    const bool b = uint32_t(c.x) >= blim || uint32_t(c.y) >= lim || uint32_t(c.z) >= lim || uint32_t(c.w) >= lim;
     bad |= b;
     const uint64_t key = b ? 0ull : make_key(uint32_t(c.x), uint32_t(c.y), uint32_t(c.z), uint32_t(c.w));
     keys[i] = key;
@@ -622,6 +623,204 @@ __global__ __launch_bounds__(kThreads) void table_lookup(TableRef t, const int4*
 }
 
 
+// ---------------------------------------------------------------------------
+// Morton order from an occupancy bitmap, for voxels in a known grid (x, y, z <
+// 2^g, object b < B). Cell c = (b << 3g) | the low 3g bits of the Morton key
+// orders the cells as the keys do, so the sorted position of a voxel is the
+// number of occupied cells before its own: a counting sort over the bitmap,
+// with no radix passes. An aligned 64-cell word of the bitmap is one 4x4x4
+// block (its six low Morton bits are the in-block cell), so the words are also
+// the block table's occupancy bitmaps and the nonzero words its blocks.
+// ---------------------------------------------------------------------------
+// The bitmap is scanned in at most kThreads chunks of 2^lgc words (lgc >= 10:
+// at least four words per thread), so that every workgroup of the two kernels
+// after the scan can take the exclusive scan of the chunk totals itself, one
+// value per thread.
+constexpr int kDenseMinLgChunk = 10;
+
+// Clears the bitmap and initialises the header (flags 0, empty-table capacity).
+__global__ __launch_bounds__(kThreads) void dense_clear(uint4* __restrict__ bitmap16, int64_t n16, HashHeader* hdr) {
+  for (int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x; i < n16; i += int64_t(gridDim.x) * kThreads)
+    bitmap16[i] = make_uint4(0u, 0u, 0u, 0u);
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    hdr->flags = 0u;
+    hdr->nblocks = 0u;
+    hdr->cap_mask = 15u;
+    hdr->shift = 60u;
+  }
+}
+
+// Sets each voxel's cell bit (a coordinate outside the grid sets the range flag
+// and no bit). Lanes of a wave whose cells share a bitmap word -- runs of
+// consecutive lanes, common when the rows come in raster or Morton order -- are
+// merged first, and the first lane of each run sets the run's bits with one
+// atomic that returns nothing. Duplicates are found from the count of set bits
+// (dense_scatter): each voxel in the grid sets one bit, so the bitmap holds
+// fewer bits than voxels exactly when two voxels share a cell.
+__global__ __launch_bounds__(kThreads) void dense_mark(const int4* __restrict__ coords, int64_t n, int g,
+                                                       uint32_t batch, unsigned long long* __restrict__ bitmap,
+                                                       HashHeader* hdr) {
+  const uint32_t lim = 1u << g;
+  const uint64_t low = (uint64_t(1) << (3 * g)) - 1u;
+  const int lane = threadIdx.x & 63;
+  bool bad = false;
+  for (int64_t i0 = int64_t(blockIdx.x) * kThreads; i0 < n; i0 += int64_t(gridDim.x) * kThreads) {
+    const int64_t i = i0 + threadIdx.x;
+    int64_t word = -1 - lane;  // distinct from every other lane's when the lane sets nothing
+    unsigned long long bit = 0ull;
+    if (i < n) {
+      const int4 c = coords[i];
+      if (uint32_t(c.x) >= batch || uint32_t(c.y) >= lim || uint32_t(c.z) >= lim || uint32_t(c.w) >= lim) {
+        bad = true;
+      } else {
+        const uint64_t key = make_key(uint32_t(c.x), uint32_t(c.y), uint32_t(c.z), uint32_t(c.w));
+        const uint64_t cell = (uint64_t(uint32_t(c.x)) << (3 * g)) | (key & low);
+        word = int64_t(cell >> 6);
+        bit = 1ull << (cell & 63u);
+      }
+    }
+    for (int o = 1; o < 64; o <<= 1) {  // bits of lanes [lane, lane + 2o) with the same word
+      const unsigned long long ob = __shfl_down(bit, o, 64);
+      const int64_t ow = __shfl_down(word, o, 64);
+      if (lane + o < 64 && ow == word) bit |= ob;
+    }
+    const int64_t prev = __shfl_up(word, 1, 64);
+    if (word >= 0 && (lane == 0 || prev != word))
+      __hip_atomic_fetch_or(&bitmap[word], bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  if (__ballot(bad) != 0 && (threadIdx.x & 63) == 0) atomicOr(&hdr->flags, kFlagCoordRange);
+}
+
+// Per chunk of 2^lgc words: each word's occupied cells before it within the
+// chunk (wpre), the chunk's occupied cells (ctot) and nonzero words (cblk).
+// Thread t takes 2^lgc / kThreads consecutive words.
+__global__ __launch_bounds__(kThreads) void dense_scan(const unsigned long long* __restrict__ bitmap, int lgc,
+                                                       uint32_t* __restrict__ wpre, uint32_t* __restrict__ ctot,
+                                                       uint32_t* __restrict__ cblk) {
+  __shared__ uint32_t s_tmp[kThreads / 64];
+  const int per = (1 << lgc) / kThreads;  // a multiple of 4
+  const int64_t w0 = (int64_t(blockIdx.x) << lgc) + int64_t(threadIdx.x) * per;
+  uint32_t sum = 0, nz = 0;
+  for (int q = 0; q < per; q += 2) {
+    const ulonglong2 a = *reinterpret_cast<const ulonglong2*>(bitmap + w0 + q);
+    sum += __popcll(a.x) + __popcll(a.y);
+    nz += uint32_t(a.x != 0ull) + uint32_t(a.y != 0ull);
+  }
+  uint32_t tot, nzt;
+  uint32_t ex = block_exclusive_scan(sum, s_tmp, &tot);
+  block_exclusive_scan(nz, s_tmp, &nzt);
+  for (int q = 0; q < per; q += 4) {
+    const ulonglong2 a = *reinterpret_cast<const ulonglong2*>(bitmap + w0 + q);
+    const ulonglong2 b = *reinterpret_cast<const ulonglong2*>(bitmap + w0 + q + 2);
+    const uint32_t p0 = __popcll(a.x), p1 = __popcll(a.y), p2 = __popcll(b.x), p3 = __popcll(b.y);
+    *reinterpret_cast<uint4*>(wpre + w0 + q) = make_uint4(ex, ex + p0, ex + p0 + p1, ex + p0 + p1 + p2);
+    ex += p0 + p1 + p2 + p3;
+  }
+  if (threadIdx.x == 0) {
+    ctot[blockIdx.x] = tot;
+    cblk[blockIdx.x] = nzt;
+  }
+}
+
+// Exclusive scan of the chunk totals into s_pre (nchunks <= kThreads) and the
+// number of nonzero words; every workgroup of the next two kernels does it.
+__device__ uint32_t dense_chunk_prefix(const uint32_t* __restrict__ ctot, const uint32_t* __restrict__ cblk,
+                                       int nchunks, uint32_t* s_pre, uint32_t* s_tmp, uint32_t* bits_set = nullptr) {
+  const int c = threadIdx.x;
+  const uint32_t v = c < nchunks ? ctot[c] : 0u, nz = c < nchunks ? cblk[c] : 0u;
+  uint32_t tot, nzt;
+  s_pre[c] = block_exclusive_scan(v, s_tmp, &tot);
+  block_exclusive_scan(nz, s_tmp, &nzt);
+  __syncthreads();
+  if (bits_set != nullptr) *bits_set = tot;
+  return nzt;
+}
+
+// Sorted keys and rows: voxel i goes to the occupied cells before its own.
+// The same workgroups also size the block table from the nonzero words
+// (capacity: power of two >= 2x the blocks, at least 16, at most max_cap) and
+// clear it; the first one records the capacity.
+__global__ __launch_bounds__(kThreads) void dense_scatter(const int4* __restrict__ coords, int64_t n, int g,
+                                                          uint32_t batch, const unsigned long long* __restrict__ bitmap,
+                                                          int lgc, const uint32_t* __restrict__ wpre,
+                                                          const uint32_t* __restrict__ ctot,
+                                                          const uint32_t* __restrict__ cblk, int nchunks,
+                                                          uint64_t* __restrict__ skeys, int32_t* __restrict__ srows,
+                                                          BlockSlot* __restrict__ slots, uint32_t max_cap,
+                                                          HashHeader* hdr) {
+  __shared__ uint32_t s_pre[kThreads];
+  __shared__ uint32_t s_tmp[kThreads / 64];
+  uint32_t nset;
+  const uint32_t nb = dense_chunk_prefix(ctot, cblk, nchunks, s_pre, s_tmp, &nset);
+  uint32_t cap = 16, lg = 4;
+  while (cap < 2u * nb && cap < max_cap) {
+    cap <<= 1;
+    ++lg;
+  }
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    hdr->nblocks = nb;
+    hdr->cap_mask = cap - 1;
+    hdr->shift = 64 - lg;
+    // fewer bits than voxels: two voxels share a cell (or some voxel lies
+    // outside the grid, which the range flag reports first)
+    if (int64_t(nset) != n) atomicOr(&hdr->flags, kFlagDuplicate);
+  }
+  for (uint32_t i = blockIdx.x * kThreads + threadIdx.x; i < cap; i += gridDim.x * kThreads) {
+    uint4* q = reinterpret_cast<uint4*>(slots + i);
+    q[0] = make_uint4(0xFFFFFFFFu, 0xFFFFFFFFu, 0u, 0u);
+    q[1] = make_uint4(0u, 0u, 0u, 0u);
+  }
+  const uint32_t lim = 1u << g;
+  const uint64_t low = (uint64_t(1) << (3 * g)) - 1u;
+  for (int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x; i < n; i += int64_t(gridDim.x) * kThreads) {
+    const int4 c = coords[i];
+    if (uint32_t(c.x) >= batch || uint32_t(c.y) >= lim || uint32_t(c.z) >= lim || uint32_t(c.w) >= lim)
+      continue;  // outside the grid: flagged by dense_mark
+    const uint64_t key = make_key(uint32_t(c.x), uint32_t(c.y), uint32_t(c.z), uint32_t(c.w));
+    const uint64_t cell = (uint64_t(uint32_t(c.x)) << (3 * g)) | (key & low);
+    const int64_t w = int64_t(cell >> 6);
+    const uint32_t below = __popcll(bitmap[w] & ((1ull << (cell & 63u)) - 1ull));
+    const uint32_t pos = s_pre[w >> lgc] + wpre[w] + below;
+    skeys[pos] = key;
+    srows[pos] = int32_t(i);
+  }
+}
+
+// One thread per bitmap word: a nonzero word is a block; insert {block key,
+// bitmap, first sorted position}. Block key = key >> 6 = (b << 42) | (the
+// word's Morton bits).
+__global__ __launch_bounds__(kThreads) void dense_insert(const unsigned long long* __restrict__ bitmap, int lgc,
+                                                         const uint32_t* __restrict__ wpre,
+                                                         const uint32_t* __restrict__ ctot,
+                                                         const uint32_t* __restrict__ cblk, int nchunks, int g,
+                                                         BlockSlot* __restrict__ slots, HashHeader* hdr) {
+  __shared__ uint32_t s_pre[kThreads];
+  __shared__ uint32_t s_tmp[kThreads / 64];
+  dense_chunk_prefix(ctot, cblk, nchunks, s_pre, s_tmp);
+  const uint32_t mask = hdr->cap_mask, shift = hdr->shift;
+  const int wb = 3 * g - 6;  // Morton bits of a block index
+  const int64_t nwords = int64_t(nchunks) << lgc;
+  for (int64_t w = int64_t(blockIdx.x) * kThreads + threadIdx.x; w < nwords; w += int64_t(gridDim.x) * kThreads) {
+    const unsigned long long bits = bitmap[w];
+    if (bits == 0ull) continue;
+    const uint64_t bkey = (uint64_t(w >> wb) << 42) | uint64_t(w & ((int64_t(1) << wb) - 1));
+    const uint32_t start = s_pre[w >> lgc] + wpre[w];
+    uint32_t s = home_slot(bkey, shift) & mask;
+    bool placed = false;
+    for (uint32_t probe = 0; probe <= mask; ++probe) {
+      unsigned long long* kp = reinterpret_cast<unsigned long long*>(&slots[s].bkey);
+      if (atomicCAS(kp, kEmptyKey, bkey) == kEmptyKey) {
+        slots[s].bits = bits;
+        slots[s].start = start;
+        placed = true;
+        break;
+      }
+      s = (s + 1) & mask;
+    }
+    if (!placed) atomicOr(&hdr->flags, kFlagCapacity);
+  }
+}
+
 inline unsigned grid_for(int64_t n, int per_block) { return unsigned((n + per_block - 1) / per_block); }
 
 }  // namespace
@@ -642,11 +841,11 @@ int64_t pack_partials(int64_t n) {
   return b < 1 ? 1 : (b < kPackBlocks ? b : kPackBlocks);
 }
 
-hipError_t launch_pack(const int32_t* coords, int64_t n, uint64_t* keys, int32_t* rows, uint64_t* keys2,
-                       int32_t* rows2, unsigned long long* part, HashHeader* hdr, hipStream_t st) {
+hipError_t launch_pack(const int32_t* coords, int64_t n, uint32_t lim, uint32_t blim, uint64_t* keys, int32_t* rows,
+                       uint64_t* keys2, int32_t* rows2, unsigned long long* part, HashHeader* hdr, hipStream_t st) {
   if (n > 0)  // the first histogram pass of the sort builds the header
-    pack_keys<<<int(pack_partials(n)), kThreads, 0, st>>>(reinterpret_cast<const int4*>(coords), n, keys, rows,
-                                                          keys2, rows2, part);
+    pack_keys<<<int(pack_partials(n)), kThreads, 0, st>>>(reinterpret_cast<const int4*>(coords), n, lim, blim, keys,
+                                                          rows, keys2, rows2, part);
   else
     reduce_bits<<<1, kThreads, 0, st>>>(part, 0, hdr);
   return hipGetLastError();
@@ -692,6 +891,35 @@ hipError_t launch_blocks(const uint64_t* keys, int64_t n, BlockSlot* slots, uint
   const uint32_t cb = (max_cap + kThreads - 1) / kThreads;
   block_clear<<<cb < 2048u ? cb : 2048u, kThreads, 0, st>>>(slots, max_cap, part, nb, hdr);
   if (n > 0) block_insert<<<grid_for(n, kThreads), kThreads, 0, st>>>(keys, n, slots, hdr);
+  return hipGetLastError();
+}
+
+int dense_max_chunks() { return kThreads; }
+int dense_chunk_log2(int64_t words) {
+  int lgc = kDenseMinLgChunk;
+  while ((words + (int64_t(1) << lgc) - 1) >> lgc > kThreads) ++lgc;
+  return lgc;
+}
+
+hipError_t launch_dense_hash(const int32_t* coords, int64_t n, int g, int batch, unsigned long long* bitmap,
+                             int lgc, int nchunks, uint32_t* wpre, uint32_t* ctot, uint32_t* cblk, uint64_t* skeys,
+                             int32_t* srows, BlockSlot* slots, uint32_t max_cap, HashHeader* hdr, hipStream_t st) {
+  const int64_t words = int64_t(nchunks) << lgc;
+  const int64_t n16 = words / 2;
+  const int64_t cb = (n16 + kThreads - 1) / kThreads;
+  dense_clear<<<unsigned(cb < 4096 ? cb : 4096), kThreads, 0, st>>>(reinterpret_cast<uint4*>(bitmap), n16, hdr);
+  const int64_t vb = (n + kThreads - 1) / kThreads;
+  const unsigned vgrid = unsigned(vb < 4096 ? (vb > 0 ? vb : 1) : 4096);
+  const auto* c4 = reinterpret_cast<const int4*>(coords);
+  dense_mark<<<vgrid, kThreads, 0, st>>>(c4, n, g, uint32_t(batch), bitmap, hdr);
+  dense_scan<<<unsigned(nchunks), kThreads, 0, st>>>(bitmap, lgc, wpre, ctot, cblk);
+  const int64_t sb = (int64_t(max_cap) + kThreads - 1) / kThreads;
+  const unsigned sgrid = unsigned(vb > sb ? (vb < 2048 ? vb : 2048) : (sb < 2048 ? sb : 2048));
+  dense_scatter<<<sgrid, kThreads, 0, st>>>(c4, n, g, uint32_t(batch), bitmap, lgc, wpre, ctot, cblk, nchunks, skeys,
+                                            srows, slots, max_cap, hdr);
+  const int64_t wgrid = (words + kThreads - 1) / kThreads;
+  dense_insert<<<unsigned(wgrid < 4096 ? wgrid : 4096), kThreads, 0, st>>>(bitmap, lgc, wpre, ctot, cblk, nchunks,
+                                                                          g, slots, hdr);
   return hipGetLastError();
 }
 

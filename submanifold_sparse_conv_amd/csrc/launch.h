@@ -15,8 +15,10 @@ constexpr int kSortBuckets = 1 << kMaxDigitBits;
 // Packs keys / rows (into both sort buffers) and the partials (OR, AND, range
 // flag) from which the sort's first histogram pass builds the header (flags,
 // digits of the sort); for n = 0 it writes the header itself.
-hipError_t launch_pack(const int32_t* coords, int64_t n, uint64_t* keys, int32_t* rows, uint64_t* keys2,
-                       int32_t* rows2, unsigned long long* part, HashHeader* hdr, hipStream_t st);
+// Spatial components must be < lim and object indices < blim (65536 each
+// without a grid).
+hipError_t launch_pack(const int32_t* coords, int64_t n, uint32_t lim, uint32_t blim, uint64_t* keys, int32_t* rows,
+                       uint64_t* keys2, int32_t* rows2, unsigned long long* part, HashHeader* hdr, hipStream_t st);
 // kSortPasses LSD radix passes (digits from the header; the leading ones may be
 // empty) keys1 -> keys0 -> keys1 -> keys0 -> keys1, then the single-workgroup
 // pass over any further bits: the sorted keys and rows end in keys1 / rows1.
@@ -27,6 +29,16 @@ hipError_t launch_sort(uint64_t* keys0, int32_t* rows0, uint64_t* keys1, int32_t
 hipError_t launch_blocks(const uint64_t* keys, int64_t n, BlockSlot* slots, uint32_t max_cap,
                          uint32_t* part, HashHeader* hdr, hipStream_t st);
 hipError_t launch_lookup(const TableRef& t, const int32_t* q, int64_t nq, int32_t* out, hipStream_t st);
+// Morton sort and block table of voxels in a known grid (x, y, z < 2^g, object
+// < batch) from an occupancy bitmap of nchunks chunks of 2^lgc 64-bit words
+// (cells (b << 3g) | low 3g Morton bits; lgc = dense_chunk_log2(words), which
+// keeps nchunks <= dense_max_chunks()); wpre: one word per bitmap word; ctot,
+// cblk: one word per chunk.
+int dense_max_chunks();
+int dense_chunk_log2(int64_t words);
+hipError_t launch_dense_hash(const int32_t* coords, int64_t n, int g, int batch, unsigned long long* bitmap,
+                             int lgc, int nchunks, uint32_t* wpre, uint32_t* ctot, uint32_t* cblk, uint64_t* skeys,
+                             int32_t* srows, BlockSlot* slots, uint32_t max_cap, HashHeader* hdr, hipStream_t st);
 
 // Kernel map (nbr, caller order; mask, Morton order) and the gather-GEMM row
 // order: grows / gmask = Morton order regrouped inside windows of kGroupWindow
