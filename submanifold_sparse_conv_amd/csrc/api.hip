@@ -85,6 +85,8 @@ struct tr_sc_hash {
   HashHeader* hdr;
   TableRef table;         // block slots, header (capacity, shift), sorted rows
   const uint64_t* skeys;  // sorted keys
+  bool has_dense;         // built in a known grid from an occupancy bitmap
+  DenseRef dense;
 };
 
 struct tr_sc_kmap {
@@ -149,6 +151,8 @@ static int build_hash_radix(const char* who, const int32_t* coords, int64_t n, u
   h->hdr = hdr;
   h->table = TableRef{slots, hdr, rows[cur]};
   h->skeys = keys[cur];
+  h->has_dense = false;
+  h->dense = DenseRef{};
   *out = h;
   return TR_SC_OK;
 }
@@ -169,9 +173,10 @@ static bool grid_dense(int64_t n, int g, int batch) {
 }
 
 // Grid workspace (bitmap build): header | keys[n] | rows[n] | bitmap | word
-// prefixes | chunk totals | chunk block counts | block slots.
+// prefixes | chunk totals | chunk block counts | chunk first positions | block
+// slots.
 struct GridLayout {
-  size_t hdr, keys, rows, bitmap, wpre, ctot, cblk, slots, total;
+  size_t hdr, keys, rows, bitmap, wpre, ctot, cblk, cpre, slots, total;
   int lgc, nchunks;
   uint32_t cap;
 };
@@ -195,6 +200,8 @@ static GridLayout grid_layout(int64_t n, int g, int batch) {
   l.ctot = o;
   o += align_up(size_t(l.nchunks) * 4, 256);
   l.cblk = o;
+  o += align_up(size_t(l.nchunks) * 4, 256);
+  l.cpre = o;
   o += align_up(size_t(l.nchunks) * 4, 256);
   l.cap = table_capacity(n < words ? n : words);
   l.slots = o;
@@ -241,7 +248,8 @@ int tr_sparseconv_build_hash_grid(const int32_t* coords, int64_t n, int grid_log
   const hipError_t e = launch_dense_hash(
       coords, n, grid_log2, batch, reinterpret_cast<unsigned long long*>(ws + l.bitmap), l.lgc, l.nchunks,
       reinterpret_cast<uint32_t*>(ws + l.wpre), reinterpret_cast<uint32_t*>(ws + l.ctot),
-      reinterpret_cast<uint32_t*>(ws + l.cblk), keys, rows, slots, l.cap, hdr, static_cast<hipStream_t>(stream));
+      reinterpret_cast<uint32_t*>(ws + l.cblk), reinterpret_cast<uint32_t*>(ws + l.cpre), keys, rows, slots, l.cap,
+      hdr, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "build_hash_grid");
   tr_sc_hash* h = new tr_sc_hash;
   h->magic = kHashMagic;
@@ -249,6 +257,10 @@ int tr_sparseconv_build_hash_grid(const int32_t* coords, int64_t n, int grid_log
   h->hdr = hdr;
   h->table = TableRef{slots, hdr, rows};
   h->skeys = keys;
+  h->has_dense = true;
+  h->dense = DenseRef{reinterpret_cast<const unsigned long long*>(ws + l.bitmap),
+                      reinterpret_cast<const uint32_t*>(ws + l.wpre), reinterpret_cast<const uint32_t*>(ws + l.cpre),
+                      l.lgc, l.nchunks, grid_log2};
   *out = h;
   return TR_SC_OK;
 }
@@ -322,7 +334,7 @@ int tr_sparseconv_build_kernel_map(const tr_sc_hash* h, int32_t* nbr, void* work
   uint32_t* mask = static_cast<uint32_t*>(workspace);
   int32_t* grows = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + part);
   uint32_t* gmask = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + 2 * part);
-  hipError_t e = launch_kmap(h->skeys, h->n, h->table, nbr, mask, grows, gmask,
+  hipError_t e = launch_kmap(h->skeys, h->n, h->table, h->has_dense ? &h->dense : nullptr, nbr, mask, grows, gmask,
                              static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "build_kernel_map");
   tr_sc_kmap* m = new tr_sc_kmap;

@@ -100,6 +100,17 @@ struct TableRef {
   const int32_t* srows;   // sorted position -> caller row
 };
 
+// The occupancy bitmap of a hash built in a known grid (x, y, z < 2^g): word w
+// of block key k is ((k >> 42) << (3g - 6)) | (k & (2^(3g - 6) - 1)); its bits
+// are the block's occupancy bitmap, and the block's first sorted position is
+// cpre[w >> lgc] + wpre[w] (nchunks <= 256 chunks of 2^lgc words).
+struct DenseRef {
+  const unsigned long long* bitmap;
+  const uint32_t* wpre;
+  const uint32_t* cpre;
+  int lgc, nchunks, g;
+};
+
 __host__ __device__ inline uint32_t home_slot(uint64_t bkey, uint32_t shift) {
   return uint32_t((bkey * 0x9E3779B97F4A7C15ull) >> shift);
 }

@@ -745,9 +745,9 @@ __global__ __launch_bounds__(kThreads) void dense_scatter(const int4* __restrict
                                                           int lgc, const uint32_t* __restrict__ wpre,
                                                           const uint32_t* __restrict__ ctot,
                                                           const uint32_t* __restrict__ cblk, int nchunks,
-                                                          uint64_t* __restrict__ skeys, int32_t* __restrict__ srows,
-                                                          BlockSlot* __restrict__ slots, uint32_t max_cap,
-                                                          HashHeader* hdr) {
+                                                          uint32_t* __restrict__ cpre, uint64_t* __restrict__ skeys,
+                                                          int32_t* __restrict__ srows, BlockSlot* __restrict__ slots,
+                                                          uint32_t max_cap, HashHeader* hdr) {
   __shared__ uint32_t s_pre[kThreads];
   __shared__ uint32_t s_tmp[kThreads / 64];
   uint32_t nset;
@@ -765,6 +765,7 @@ __global__ __launch_bounds__(kThreads) void dense_scatter(const int4* __restrict
     // outside the grid, which the range flag reports first)
     if (int64_t(nset) != n) atomicOr(&hdr->flags, kFlagDuplicate);
   }
+  if (blockIdx.x == 0 && int(threadIdx.x) < nchunks) cpre[threadIdx.x] = s_pre[threadIdx.x];
   for (uint32_t i = blockIdx.x * kThreads + threadIdx.x; i < cap; i += gridDim.x * kThreads) {
     uint4* q = reinterpret_cast<uint4*>(slots + i);
     q[0] = make_uint4(0xFFFFFFFFu, 0xFFFFFFFFu, 0u, 0u);
@@ -902,8 +903,9 @@ int dense_chunk_log2(int64_t words) {
 }
 
 hipError_t launch_dense_hash(const int32_t* coords, int64_t n, int g, int batch, unsigned long long* bitmap,
-                             int lgc, int nchunks, uint32_t* wpre, uint32_t* ctot, uint32_t* cblk, uint64_t* skeys,
-                             int32_t* srows, BlockSlot* slots, uint32_t max_cap, HashHeader* hdr, hipStream_t st) {
+                             int lgc, int nchunks, uint32_t* wpre, uint32_t* ctot, uint32_t* cblk, uint32_t* cpre,
+                             uint64_t* skeys, int32_t* srows, BlockSlot* slots, uint32_t max_cap, HashHeader* hdr,
+                             hipStream_t st) {
   const int64_t words = int64_t(nchunks) << lgc;
   const int64_t n16 = words / 2;
   const int64_t cb = (n16 + kThreads - 1) / kThreads;
@@ -915,8 +917,8 @@ hipError_t launch_dense_hash(const int32_t* coords, int64_t n, int g, int batch,
   dense_scan<<<unsigned(nchunks), kThreads, 0, st>>>(bitmap, lgc, wpre, ctot, cblk);
   const int64_t sb = (int64_t(max_cap) + kThreads - 1) / kThreads;
   const unsigned sgrid = unsigned(vb > sb ? (vb < 2048 ? vb : 2048) : (sb < 2048 ? sb : 2048));
-  dense_scatter<<<sgrid, kThreads, 0, st>>>(c4, n, g, uint32_t(batch), bitmap, lgc, wpre, ctot, cblk, nchunks, skeys,
-                                            srows, slots, max_cap, hdr);
+  dense_scatter<<<sgrid, kThreads, 0, st>>>(c4, n, g, uint32_t(batch), bitmap, lgc, wpre, ctot, cblk, nchunks, cpre,
+                                            skeys, srows, slots, max_cap, hdr);
   const int64_t wgrid = (words + kThreads - 1) / kThreads;
   dense_insert<<<unsigned(wgrid < 4096 ? wgrid : 4096), kThreads, 0, st>>>(bitmap, lgc, wpre, ctot, cblk, nchunks,
                                                                           g, slots, hdr);

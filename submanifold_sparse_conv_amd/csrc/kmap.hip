@@ -53,12 +53,24 @@ __device__ inline uint32_t cell_z(int z) { return uint32_t(z & 1) | (uint32_t(z 
 // voxel (record j of lane l at j * 64 + l), which turns the per-tap choice of
 // block into one indexed LDS read; the same bytes then stage the wave's 64 x
 // 27 output rows and their caller rows for the write-back.
+//
+// DENSE: the hash was built in a known grid, and the block records come from
+// its occupancy bitmap instead of the table: the word of a neighbour block is
+// its Morton block index (nearby words for nearby blocks, no probe), its bits
+// the block's bitmap, its prefix the block's first sorted position. A block
+// outside the grid is absent.
+template <bool DENSE>
 __global__ __launch_bounds__(kThreads) void kmap_kernel(const uint64_t* __restrict__ skeys, int64_t n,
-                                                        TableRef t, int32_t* __restrict__ nbr,
+                                                        TableRef t, DenseRef d, int32_t* __restrict__ nbr,
                                                         uint32_t* __restrict__ mask_out) {
   constexpr int kWaves = kThreads / 64;
   static_assert(64 * 27 * 4 + 64 * 4 <= 8 * 64 * 16, "staged rows fit in the record region");
   __shared__ uint4 lds[kWaves][8 * 64];
+  __shared__ uint32_t s_cpre[kThreads];  // DENSE: first sorted position of each bitmap chunk
+  if constexpr (DENSE) {
+    if (int(threadIdx.x) < d.nchunks) s_cpre[threadIdx.x] = d.cpre[threadIdx.x];
+    __syncthreads();
+  }
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   uint4* rec = lds[wave];
   int32_t* res = reinterpret_cast<int32_t*>(lds[wave]);  // [64][27]: odd stride, conflict-free
@@ -109,30 +121,52 @@ __global__ __launch_bounds__(kThreads) void kmap_kernel(const uint64_t* __restri
       bk[j] = b;
       need[j] = nd;
     }
-    const uint32_t hs0 = home_slot(bkey, tshift) & tmask;
-    uint4 v0[8];
-    uint32_t st0[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const uint32_t h = need[j] ? home_slot(bk[j], tshift) & tmask : hs0;
-      v0[j] = *reinterpret_cast<const uint4*>(t.slots + h);
-      st0[j] = t.slots[h].start;
-    }
     uint64_t bbits[8];
     uint32_t bstart[8];
-    uint32_t longer = 0;  // blocks whose home slot holds another key
+    if constexpr (DENSE) {
+      const int wb = 3 * d.g - 6;  // Morton bits of a block index in the grid
+      const uint64_t wlow = (uint64_t(1) << wb) - 1u;
+      auto word_of = [&](uint64_t k) { return int64_t(((k >> 42) << wb) | (k & wlow)); };
+      const int64_t w_own = word_of(bkey);
+      unsigned long long bw[8];
+      uint32_t pw[8];
+      bool in[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const uint64_t k = uint64_t(v0[j].x) | (uint64_t(v0[j].y) << 32);
-      const bool hit = need[j] && k == bk[j];
-      bbits[j] = hit ? (uint64_t(v0[j].z) | (uint64_t(v0[j].w) << 32)) : 0ull;
-      bstart[j] = hit ? st0[j] : 0u;
-      longer |= uint32_t(need[j] && !hit && k != kEmptyKey) << j;
-    }
-    if (longer) {
+      for (int j = 0; j < 8; ++j) {  // all loads in flight together; a block not needed reads the own word
+        in[j] = need[j] && ((bk[j] & kBlockMorton) >> wb) == 0u;
+        const int64_t w = in[j] ? word_of(bk[j]) : w_own;
+        bw[j] = d.bitmap[w];
+        pw[j] = d.wpre[w] + s_cpre[w >> d.lgc];
+      }
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
-        if ((longer >> j) & 1u) block_find(t.slots, tmask, tshift, bk[j], bbits[j], bstart[j]);
+      for (int j = 0; j < 8; ++j) {
+        bbits[j] = in[j] ? bw[j] : 0ull;
+        bstart[j] = in[j] ? pw[j] : 0u;
+      }
+    } else {
+      const uint32_t hs0 = home_slot(bkey, tshift) & tmask;
+      uint4 v0[8];
+      uint32_t st0[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t h = need[j] ? home_slot(bk[j], tshift) & tmask : hs0;
+        v0[j] = *reinterpret_cast<const uint4*>(t.slots + h);
+        st0[j] = t.slots[h].start;
+      }
+      uint32_t longer = 0;  // blocks whose home slot holds another key
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint64_t k = uint64_t(v0[j].x) | (uint64_t(v0[j].y) << 32);
+        const bool hit = need[j] && k == bk[j];
+        bbits[j] = hit ? (uint64_t(v0[j].z) | (uint64_t(v0[j].w) << 32)) : 0ull;
+        bstart[j] = hit ? st0[j] : 0u;
+        longer |= uint32_t(need[j] && !hit && k != kEmptyKey) << j;
+      }
+      if (longer) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if ((longer >> j) & 1u) block_find(t.slots, tmask, tshift, bk[j], bbits[j], bstart[j]);
+      }
     }
 #pragma unroll
     for (int j = 0; j < 8; ++j)
@@ -296,10 +330,14 @@ __global__ __launch_bounds__(kGroupThreads) void group_rows(const int32_t* __res
 
 }  // namespace
 
-hipError_t launch_kmap(const uint64_t* skeys, int64_t n, const TableRef& t, int32_t* nbr, uint32_t* mask,
-                       int32_t* grows, uint32_t* gmask, hipStream_t st) {
+hipError_t launch_kmap(const uint64_t* skeys, int64_t n, const TableRef& t, const DenseRef* dense, int32_t* nbr,
+                       uint32_t* mask, int32_t* grows, uint32_t* gmask, hipStream_t st) {
   if (n > 0) {
-    kmap_kernel<<<unsigned((n + kThreads - 1) / kThreads), kThreads, 0, st>>>(skeys, n, t, nbr, mask);
+    const unsigned grid = unsigned((n + kThreads - 1) / kThreads);
+    if (dense != nullptr)
+      kmap_kernel<true><<<grid, kThreads, 0, st>>>(skeys, n, t, *dense, nbr, mask);
+    else
+      kmap_kernel<false><<<grid, kThreads, 0, st>>>(skeys, n, t, DenseRef{}, nbr, mask);
     group_rows<<<unsigned((n + kGroupWindow - 1) / kGroupWindow), kGroupThreads, 0, st>>>(t.srows, mask, n,
                                                                                          grows, gmask);
   }

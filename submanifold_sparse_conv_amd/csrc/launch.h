@@ -33,19 +33,23 @@ hipError_t launch_lookup(const TableRef& t, const int32_t* q, int64_t nq, int32_
 // < batch) from an occupancy bitmap of nchunks chunks of 2^lgc 64-bit words
 // (cells (b << 3g) | low 3g Morton bits; lgc = dense_chunk_log2(words), which
 // keeps nchunks <= dense_max_chunks()); wpre: one word per bitmap word; ctot,
-// cblk: one word per chunk.
+// cblk, cpre (the chunks' first positions, written for the kernel map): one
+// word per chunk.
 int dense_max_chunks();
 int dense_chunk_log2(int64_t words);
 hipError_t launch_dense_hash(const int32_t* coords, int64_t n, int g, int batch, unsigned long long* bitmap,
-                             int lgc, int nchunks, uint32_t* wpre, uint32_t* ctot, uint32_t* cblk, uint64_t* skeys,
-                             int32_t* srows, BlockSlot* slots, uint32_t max_cap, HashHeader* hdr, hipStream_t st);
+                             int lgc, int nchunks, uint32_t* wpre, uint32_t* ctot, uint32_t* cblk, uint32_t* cpre,
+                             uint64_t* skeys, int32_t* srows, BlockSlot* slots, uint32_t max_cap, HashHeader* hdr,
+                             hipStream_t st);
 
 // Kernel map (nbr, caller order; mask, Morton order) and the gather-GEMM row
 // order: grows / gmask = Morton order regrouped inside windows of kGroupWindow
 // voxels by the octant pattern of the neighbour mask.
 constexpr int kGroupWindow = 4096;
-hipError_t launch_kmap(const uint64_t* skeys, int64_t n, const TableRef& t, int32_t* nbr, uint32_t* mask,
-                       int32_t* grows, uint32_t* gmask, hipStream_t st);
+// dense: the hash's occupancy bitmap when it was built in a known grid (the
+// block records are read from it instead of the table), else null.
+hipError_t launch_kmap(const uint64_t* skeys, int64_t n, const TableRef& t, const DenseRef* dense, int32_t* nbr,
+                       uint32_t* mask, int32_t* grows, uint32_t* gmask, hipStream_t st);
 
 // Forward kernels. `srows` is the row order of the tiles (position -> caller
 // row), `mask` the 27-bit neighbour mask of the voxel at each position.
