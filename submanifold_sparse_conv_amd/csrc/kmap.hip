@@ -249,16 +249,16 @@ __global__ __launch_bounds__(kGroupThreads) void group_rows(const int32_t* __res
                                                             int32_t* __restrict__ grows,
                                                             uint32_t* __restrict__ gmask) {
   constexpr int WAVES = kGroupThreads / 64;
-  __shared__ uint32_t hist[256];
-  __shared__ uint32_t base_off[256];
-  __shared__ uint32_t wtot[256 / 64];
-  __shared__ uint32_t wcount[WAVES][256];
+  constexpr int PER = kGroupWindow / kGroupThreads;
+  static_assert(PER * kGroupThreads == kGroupWindow, "window = whole passes of the workgroup");
+  // cnt[it][wave][d]: keys with pattern d among the lanes of (item it, wave);
+  // turned in place into their first output position.
+  __shared__ uint32_t cnt[PER][WAVES][256];
+  __shared__ uint32_t s_tmp[4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t w0 = int64_t(blockIdx.x) * kGroupWindow;
   const int64_t w1 = w0 + kGroupWindow < n ? w0 + kGroupWindow : n;
   // The window's masks and rows, loaded once (all loads in flight together).
-  constexpr int PER = kGroupWindow / kGroupThreads;
-  static_assert(PER * kGroupThreads == kGroupWindow, "window = whole passes of the workgroup");
   uint32_t mv[PER];
   int32_t rv[PER];
 #pragma unroll
@@ -267,39 +267,16 @@ __global__ __launch_bounds__(kGroupThreads) void group_rows(const int32_t* __res
     mv[it] = t < w1 ? mask[t] : 0u;
     rv[it] = t < w1 ? srows[t] : 0;
   }
-  if (tid < 256) {
-    hist[tid] = 0;
-    for (int w = 0; w < WAVES; ++w) wcount[w][tid] = 0;
-  }
+  for (int q = tid; q < PER * WAVES * 256; q += kGroupThreads) (&cnt[0][0][0])[q] = 0u;
   __syncthreads();
-#pragma unroll
-  for (int it = 0; it < PER; ++it)
-    if (w0 + it * kGroupThreads + tid < w1) atomicAdd(&hist[octant_key(mv[it])], 1u);
-  __syncthreads();
-  if (tid < 256) {  // exclusive scan of the histogram: four waves, then their totals
-    const uint32_t v = hist[tid];
-    uint32_t x = v;
-    for (int o = 1; o < 64; o <<= 1) {
-      const uint32_t y = __shfl_up(x, o, 64);
-      if (lane >= o) x += y;
-    }
-    if (lane == 63) wtot[wave] = x;
-    base_off[tid] = x - v;
-  }
-  __syncthreads();
-  if (tid < 256) {
-    uint32_t before = 0;
-    for (int w = 0; w < wave; ++w) before += wtot[w];
-    base_off[tid] += before;
-  }
-  __syncthreads();
+  // Rank every item among the equal patterns of its (item, wave) with ballots;
+  // the first lane of each pattern stores the count.
   const unsigned long long lt = (1ull << lane) - 1ull;
+  uint32_t dg[PER], rank[PER];
 #pragma unroll
   for (int it = 0; it < PER; ++it) {
-    const int64_t t = w0 + it * kGroupThreads + tid;
-    const bool valid = t < w1;
-    const uint32_t m = mv[it], d = octant_key(m);
-    const int32_t row = rv[it];
+    const bool valid = w0 + it * kGroupThreads + tid < w1;
+    const uint32_t d = octant_key(mv[it]);
     unsigned long long peers = __ballot(valid);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -307,24 +284,46 @@ __global__ __launch_bounds__(kGroupThreads) void group_rows(const int32_t* __res
       const unsigned long long bal = __ballot(bit);
       peers &= bit ? bal : ~bal;
     }
-    if (valid && (peers & lt) == 0) wcount[wave][d] = __popcll(peers);
-    __syncthreads();
-    if (valid) {
-      uint32_t pos = base_off[d] + __popcll(peers & lt);
-      for (int w = 0; w < wave; ++w) pos += wcount[w][d];
-      grows[w0 + pos] = row;
-      gmask[w0 + pos] = m;
+    dg[it] = d;
+    rank[it] = valid ? __popcll(peers & lt) : ~0u;
+    if (valid && (peers & lt) == 0) cnt[it][wave][d] = __popcll(peers);
+  }
+  __syncthreads();
+  // Thread d < 256 owns pattern d: its total, the exclusive scan of the totals
+  // over the patterns (four waves), then its positions in (item, wave) order.
+  uint32_t tot = 0, excl = 0;
+  if (tid < 256) {
+#pragma unroll
+    for (int it = 0; it < PER; ++it)
+      for (int w = 0; w < WAVES; ++w) tot += cnt[it][w][tid];
+    uint32_t x = tot;
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t y = __shfl_up(x, o, 64);
+      if (lane >= o) x += y;
     }
-    __syncthreads();
-    if (tid < 256) {  // advance the digit offsets; clear the counts for the next pass
-      uint32_t add = 0;
+    excl = x - tot;
+    if (lane == 63) s_tmp[wave] = x;
+  }
+  __syncthreads();
+  if (tid < 256) {
+    uint32_t run = excl;
+    for (int w = 0; w < wave; ++w) run += s_tmp[w];
+#pragma unroll
+    for (int it = 0; it < PER; ++it)
       for (int w = 0; w < WAVES; ++w) {
-        add += wcount[w][tid];
-        wcount[w][tid] = 0;
+        const uint32_t v = cnt[it][w][tid];
+        cnt[it][w][tid] = run;
+        run += v;
       }
-      base_off[tid] += add;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int it = 0; it < PER; ++it) {
+    if (rank[it] != ~0u) {
+      const uint32_t pos = cnt[it][wave][dg[it]] + rank[it];
+      grows[w0 + pos] = rv[it];
+      gmask[w0 + pos] = mv[it];
     }
-    __syncthreads();
   }
 }
 
