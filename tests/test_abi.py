@@ -59,6 +59,23 @@ def test_workspace_sizes(L):
     assert L.tr_sparseconv_forward_workspace_bytes(0, 32, 1) == 0
 
 
+def test_grid_workspace_sizes(L):
+    G = L.tr_sparseconv_hash_grid_workspace_bytes
+    for g, batch in ((1, 1), (17, 1), (8, 0), (8, 65537)):
+        assert G(1000, g, batch) == 0                     # grid outside [2, 16] x [1, 65536]
+    assert G(-1, 8, 1) == 0 and G((1 << 30) + 1, 8, 1) == 0
+    # bitmap build: the bitmap (2^(3g) bits per object) plus per-voxel and per-word arrays;
+    # 256^3 x 1: 2 MB of bitmap and 1 MB of word prefixes at least
+    n = 393720
+    dense = G(n, 8, 1)
+    assert dense >= n * 12 + (1 << 21) + (1 << 20)
+    assert G(n, 8, 2) > dense                            # twice the bitmap
+    # beyond 32 MB of bitmap the build is the radix one, with its workspace
+    assert G(n, 10, 1) == L.tr_sparseconv_hash_workspace_bytes(n)
+    assert G(n, 16, 65536) == L.tr_sparseconv_hash_workspace_bytes(n)
+    assert G(0, 8, 1) == L.tr_sparseconv_hash_workspace_bytes(0)  # empty: the radix path
+
+
 def test_host_argument_errors(L):
     from submanifold_sparse_conv_amd import _lib
     P = ctypes.c_void_p
@@ -73,6 +90,16 @@ def test_host_argument_errors(L):
                                       ctypes.byref(out)) == _lib.ERR_INVALID_ARG  # misaligned
     assert L.tr_sparseconv_build_hash(fake, 10, fake, 64, None, ctypes.byref(out)) == _lib.ERR_WORKSPACE
     assert b"workspace" in L.tr_sparseconv_last_error()
+    bg = L.tr_sparseconv_build_hash_grid
+    assert bg(fake, 10, 8, 1, fake, 1 << 20, None, None) == _lib.ERR_INVALID_ARG
+    assert bg(fake, 10, 1, 1, fake, 1 << 20, None, ctypes.byref(out)) == _lib.ERR_INVALID_ARG
+    assert bg(fake, 10, 8, 0, fake, 1 << 20, None, ctypes.byref(out)) == _lib.ERR_INVALID_ARG
+    assert bg(fake, -1, 8, 1, fake, 1 << 20, None, ctypes.byref(out)) == _lib.ERR_INVALID_ARG
+    assert bg(None, 10, 8, 1, fake, 1 << 20, None, ctypes.byref(out)) == _lib.ERR_INVALID_ARG
+    assert bg(fake, 10, 8, 1, P(0x10010), 1 << 30, None, ctypes.byref(out)) == _lib.ERR_INVALID_ARG
+    assert bg(fake, 10, 8, 1, fake, 64, None, ctypes.byref(out)) == _lib.ERR_WORKSPACE
+    assert bg(fake, 10, 12, 1, fake, 64, None, ctypes.byref(out)) == _lib.ERR_WORKSPACE  # radix fallback
+    assert out.value is None
     assert L.tr_sparseconv_status(None, None) == _lib.ERR_INVALID_ARG
     assert L.tr_sparseconv_hash_size(None) == -1
     assert L.tr_sparseconv_build_kernel_map(None, fake, fake, 1 << 20, None,
