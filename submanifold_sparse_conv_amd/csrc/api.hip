@@ -93,8 +93,9 @@ struct tr_sc_kmap {
   uint32_t magic;
   int64_t n;
   const int32_t* nbr;
-  const int32_t* grows;   // tile row order (position -> caller row)
-  const uint32_t* gmask;  // neighbour mask of each position
+  const int32_t* grows;        // tile row order (position -> caller row)
+  const uint32_t* gmask;       // neighbour mask of each position
+  const unsigned char* plan;   // halo plan records of the gather-GEMM
 };
 
 extern "C" {
@@ -312,10 +313,11 @@ void tr_sparseconv_hash_destroy(tr_sc_hash* h) {
   }
 }
 
-// Kernel-map workspace: mask[n] (Morton order) | grows[n] | gmask[n] (tile order).
+// Kernel-map workspace: mask[n] (Morton order) | grows[n] | gmask[n] (tile
+// order) | halo plan (one record per tile of kHaloTM voxels).
 size_t tr_sparseconv_kmap_workspace_bytes(int64_t n) {
   if (n < 0 || n > kMaxN) return 0;
-  return 3 * align_up(size_t(n) * 4, 256) + 256;
+  return 3 * align_up(size_t(n) * 4, 256) + size_t(halo_tiles(n)) * kPlanBytes + 256;
 }
 
 int tr_sparseconv_build_kernel_map(const tr_sc_hash* h, int32_t* nbr, void* workspace, size_t ws_bytes,
@@ -334,8 +336,9 @@ int tr_sparseconv_build_kernel_map(const tr_sc_hash* h, int32_t* nbr, void* work
   uint32_t* mask = static_cast<uint32_t*>(workspace);
   int32_t* grows = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + part);
   uint32_t* gmask = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + 2 * part);
+  unsigned char* plan = static_cast<unsigned char*>(workspace) + 3 * part;
   hipError_t e = launch_kmap(h->skeys, h->n, h->table, h->has_dense ? &h->dense : nullptr, nbr, mask, grows, gmask,
-                             static_cast<hipStream_t>(stream));
+                             plan, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "build_kernel_map");
   tr_sc_kmap* m = new tr_sc_kmap;
   m->magic = kKmapMagic;
@@ -343,6 +346,7 @@ int tr_sparseconv_build_kernel_map(const tr_sc_hash* h, int32_t* nbr, void* work
   m->nbr = nbr;
   m->grows = grows;
   m->gmask = gmask;
+  m->plan = plan;
   *out = m;
   return TR_SC_OK;
 }
@@ -358,7 +362,7 @@ size_t tr_sparseconv_packed_weights_bytes(int c_in, int c_out, int dtype) {
   if (c_in <= 0 || c_out <= 0) return 0;
   const size_t elems = size_t(27) * size_t(c_in) * size_t(c_out);
   if (dtype == TR_SC_BF16 || dtype == TR_SC_F16)
-    return size_t(packed_weight_elems(c_in, c_out)) * 2 + 256;  // + zero block
+    return size_t(packed_half_bytes(c_in, c_out));  // + zero block (+ fragment-order copy)
   if (dtype == TR_SC_F32) return align_up(elems * 4, 256);
   return 0;
 }
@@ -390,7 +394,7 @@ int run_forward(const char* who, const tr_sc_kmap* m, const void* x, int x_dtype
   if (x == y) return fail(TR_SC_ERR_INVALID_ARG, "%s: x and y are the same buffer", who);
   if (int64_t(m->n) * c_out >= (int64_t(1) << 40) || int64_t(m->n) * c_in >= (int64_t(1) << 40))
     return fail(TR_SC_ERR_UNSUPPORTED, "%s: tensor too large", who);
-  ConvArgs a{m->nbr, m->grows, m->gmask, m->n, x, wp, y, c_in, c_out, x_dtype, w_dtype, y_dtype, epi};
+  ConvArgs a{m->nbr, m->grows, m->gmask, m->plan, m->n, x, wp, y, c_in, c_out, x_dtype, w_dtype, y_dtype, epi};
   hipError_t e;
   if (w_dtype == TR_SC_F32) {
     e = launch_forward_simple_f32(a, st);

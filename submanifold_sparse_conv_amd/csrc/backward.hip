@@ -338,6 +338,10 @@ hipError_t launch_pack_dgrad(const void* w, void* wp, int c_in, int c_out, int d
     // c_in * c_out is a multiple of 64 (both multiples of 8): whole 16-byte chunks per tap
     pack_dgrad_half<<<grid, kThreads, 0, st>>>(static_cast<const uint4*>(w), static_cast<uint4*>(wp),
                                                int64_t(c_in) * c_out / 8, packed_weight_elems(c_out, c_in) / 8);
+    // the data gradient is a c_out -> c_in convolution
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess || !halo_shape(c_out, c_in)) return e;
+    return launch_pack_frag(wp, c_out, c_in, st);
   }
   return hipGetLastError();
 }

@@ -168,6 +168,15 @@ __device__ inline int xcd_remap(int bid, int grid) {
   return xcd * per + (xcd < rem ? xcd : rem) + local;
 }
 
+// Octant pattern of a neighbour mask: bit (dx>0)*4 + (dy>0)*2 + (dz>0) is set
+// when the corner neighbour at (dx, dy, dz), |dx| = |dy| = |dz| = 1, exists.
+// It says on which sides of a thin surface the voxel lies.
+__device__ inline uint32_t octant_key(uint32_t m) {
+  return ((m >> 0) & 1u) | (((m >> 2) & 1u) << 1) | (((m >> 6) & 1u) << 2) | (((m >> 8) & 1u) << 3) |
+         (((m >> 18) & 1u) << 4) | (((m >> 20) & 1u) << 5) | (((m >> 24) & 1u) << 6) |
+         (((m >> 26) & 1u) << 7);
+}
+
 // Direct global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4):
 // lane l of the wave writes lds_base + 16 * l. `lds_base` must be wave-uniform.
 __device__ inline void copy16_to_lds(const void* g, void* lds_base) {

@@ -32,6 +32,8 @@
 // Weights are first re-laid out to [27][C_out][C_in] (input channels
 // contiguous), the operand order of the matrix instruction, followed by a
 // 256-byte block of zeros (the copy source of absent neighbours).
+#include <mutex>
+
 #include "common.h"
 #include "launch.h"
 
@@ -41,6 +43,7 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kThreads = 256;
 
@@ -54,6 +57,9 @@ struct Half<false> {
   static __device__ __forceinline__ f32x4 mma(vec a, vec b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
   }
+  static __device__ __forceinline__ f32x16 mma32(vec a, vec b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
   static __device__ __forceinline__ float widen(uint16_t h) { return bf16_to_f32(h); }
   static __device__ __forceinline__ uint16_t narrow(float v) { return f32_to_bf16_rne(v); }
 };
@@ -63,6 +69,9 @@ struct Half<true> {
   typedef _Float16 elt;
   static __device__ __forceinline__ f32x4 mma(vec a, vec b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x16 mma32(vec a, vec b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
   }
   static __device__ __forceinline__ float widen(uint16_t h) {
     return float(__builtin_bit_cast(_Float16, h));
@@ -96,6 +105,7 @@ __device__ __forceinline__ void split_terms(const uint4 (&raw)[2], typename H::v
 
 struct RowsArgs {
   const int32_t* nbr;
+  const unsigned char* plan;  // halo plan records (fwd_halo)
   const int32_t* srows;
   const uint32_t* vmask;
   int64_t n;
@@ -540,6 +550,403 @@ __global__ __launch_bounds__(kThreads, 3) void fwd_lds(const RowsArgs p) {
   store_tile<FM, FN, H>(p, acc, crow, n0, reinterpret_cast<float*>(bbuf0) + wave * 8 * TN);
 }
 
+// Epilogue of a wave's block of RB x CB 32x32 fp32 accumulators: acc[b][cb]
+// holds rows 32 b + 8 (e / 4) + 4 (lane / 32) + e % 4 (element e) of the
+// wave's rows and column n0 + 32 cb + lane % 32. In passes of 16 rows (rows
+// 32 b + 16 h ..), v = act(acc + bias) goes to this wave's LDS region `sO` (16
+// rows of 32 CB floats, row stride 32 CB + 8 floats so that the two half-waves
+// write different banks); then each lane takes 16-byte output pieces of whole
+// rows, adds the residual, rounds once and stores at the caller row. crow[q]:
+// caller row of the wave's row 64 q + lane (-1: not stored).
+template <class H, int RB, int CB>
+__device__ __forceinline__ void store_tile32(const RowsArgs& p, const f32x16 (&acc)[RB][CB],
+                                             const int32_t (&crow)[(RB + 1) / 2], int n0, float* sO) {
+  constexpr int TN = 32 * CB, SR = TN + 8;
+  const int c_out = p.c_out;
+  const int lane = threadIdx.x & 63;
+  const int l32 = lane & 31, hw = lane >> 5;
+  float bv[CB];
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) {
+    const int c = n0 + cb * 32 + l32;
+    bv[cb] = (p.bias != nullptr && c < c_out) ? p.bias[c] : 0.f;
+  }
+  const int act = p.act;
+#pragma unroll
+  for (int b = 0; b < RB; ++b) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      // elements e = 8h .. 8h+7: rows 16h + 8 (e' / 4) + 4 hw + e' % 4 of the block (e' = e - 8h)
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int r = 8 * (e >> 2) + 4 * hw + (e & 3);
+          sO[r * SR + cb * 32 + l32] = activate(acc[b][cb][8 * h + e] + bv[cb], act);
+        }
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's staging writes are done
+      const int row0 = 32 * b + 16 * h;    // the pass's first row in the wave
+      if (!p.y_f32) {
+#pragma unroll
+        for (int q = lane; q < 16 * (TN / 8); q += 64) {
+          const int r = q / (TN / 8), cc = q % (TN / 8);
+          const int32_t row = __shfl(crow[(row0 + r) >> 6], (row0 + r) & 63, 64);
+          const int co = n0 + cc * 8;
+          if (row >= 0 && co < c_out) {
+            const float4 lo = *reinterpret_cast<const float4*>(sO + r * SR + cc * 8);
+            const float4 hi = *reinterpret_cast<const float4*>(sO + r * SR + cc * 8 + 4);
+            float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+            const int64_t off = int64_t(row) * c_out + co;
+            if (p.residual != nullptr) {
+              const uint4 rr = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.residual) + off);
+              const uint16_t* rh = reinterpret_cast<const uint16_t*>(&rr);
+#pragma unroll
+              for (int e = 0; e < 8; ++e) v[e] += H::widen(rh[e]);
+            }
+            uint4 o;
+            uint16_t* oh = reinterpret_cast<uint16_t*>(&o);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) oh[e] = H::narrow(v[e]);
+            store_stream(reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.y) + off), o);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int q = lane; q < 16 * (TN / 4); q += 64) {
+          const int r = q / (TN / 4), cc = q % (TN / 4);
+          const int32_t row = __shfl(crow[(row0 + r) >> 6], (row0 + r) & 63, 64);
+          const int co = n0 + cc * 4;
+          if (row >= 0 && co < c_out) {
+            float4 v = *reinterpret_cast<const float4*>(sO + r * SR + cc * 4);
+            const int64_t off = int64_t(row) * c_out + co;
+            if (p.residual != nullptr) {
+              const float4 rr = *reinterpret_cast<const float4*>(static_cast<const float*>(p.residual) + off);
+              v.x += rr.x, v.y += rr.y, v.z += rr.z, v.w += rr.w;
+            }
+            store_stream(reinterpret_cast<uint4*>(static_cast<float*>(p.y) + off),
+                         uint4{__float_as_uint(v.x), __float_as_uint(v.y), __float_as_uint(v.z), __float_as_uint(v.w)});
+          }
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // reads done before the next pass overwrites
+    }
+  }
+}
+
+// The same output-stationary product with the gathered rows read from a halo:
+// over tiles of kHaloTM Morton-consecutive voxels, the tile's distinct
+// neighbour rows are copied into LDS once per 32-channel chunk and every tap
+// reads its A fragments from there, instead of gathering each (voxel, tap) row
+// from global memory. Over a thin surface the halo holds ~1.75 rows per voxel
+// against ~17.7 gathered ones. The plan (tile order, halo rows, the LDS
+// offset of every (row, tap)'s row, which 32-row blocks have which taps) comes
+// from the kernel map (halo_plan).
+//
+// Matrix instruction v_mfma_f32_32x32x16 (bf16 / fp16): on gfx950 it sustains
+// ~97 % of the matrix peak from two waves per SIMD, where 16x16x32 stays near
+// 62 % whatever the occupancy (measured). The four waves split the 256 x 128
+// tile two by two: wave w owns rows 128 (w / 2) .. + 128 (four 32-row blocks)
+// and columns n0 + 64 (w % 2) .. + 64 (two 32-column blocks), eight 32x32 fp32
+// accumulators.
+//
+// Stages run chunk-major: for each 32-channel chunk, the tile's taps in order;
+// a stage is two 16-channel steps of up to 8 multiplies each. Each wave loads
+// its own B fragments straight into registers from the fragment-ordered copy
+// of the weights (one contiguous kilobyte per fragment), two stages ahead, so
+// the weights need no LDS and the stages need no barrier: the waves only meet
+// when a chunk's halo is replaced. The MFMA issue slot of a SIMD is shared with
+// all other vector instructions, so a stage keeps those few: A fragment
+// addresses are one XOR of offsets stored in the plan, tap and block masks
+// live in scalar registers. A 32-row block skips the multiplies of a tap none
+// of its rows has. Each output row sums, chunk by chunk, its taps in order
+// (two 16-channel products per stage): the same bits whatever the slots, run
+// to run.
+//
+// Halo rows are 64 bytes (four 16-byte pieces); piece q of row r sits at
+// position q ^ ((r >> 2) & 3), so 16 rows read at one piece fall on 16
+// different bank groups whenever their numbers differ mod 16. A tile whose halo
+// does not fit (nh < 0: sparse sets, up to 27 distinct neighbours per voxel)
+// gathers its A fragments from global memory in the same order, so its
+// results are the same bits. Shapes: halo_shape (c_in % 32 == 0, c_out % 128
+// == 0).
+//
+// Work items: blockIdx -> (row tile, column tile); when the last round of
+// workgroups would hold few items (split > 0), each of the last `split` items
+// becomes four workgroups, each multiplying for one wave's block (the other
+// three waves only help with the halo copies), so the last round takes about
+// a quarter of a tile.
+constexpr int kHaloKC = 32;
+static_assert(kHaloRowBytes == kHaloKC * 2, "halo rows hold one chunk of half-precision channels");
+
+struct HaloLaunch {
+  int full;   // work items run whole
+  int split;  // items after them, each run as four parts
+};
+
+template <bool F16>
+__global__ __launch_bounds__(kThreads, 2) void fwd_halo(const RowsArgs p, const HaloLaunch hl) {
+  typedef Half<F16> H;
+  typedef typename H::vec hvec;
+  constexpr int TM = kHaloTM, TN = 128, RB = 4, CB = 2;
+  constexpr int KC = kHaloKC, ROWB = kHaloRowBytes;
+  constexpr int HBYTES = kHaloCap * ROWB;
+  constexpr int SLOTQ = (kPlanSlotBytes + 1023) / 1024, ROWQ = (kHaloCap * 4 + 1023) / 1024;
+  static_assert(HBYTES >= 4 * 16 * (32 * CB + 8) * 4, "the output staging lives in the halo area");
+  __shared__ __attribute__((aligned(1024))) unsigned char s_halo[HBYTES];
+  __shared__ __attribute__((aligned(1024))) unsigned char s_slotb[SLOTQ * 1024];  // uint16 [tap][sidx]
+  __shared__ __attribute__((aligned(1024))) unsigned char s_rowb[ROWQ * 1024];    // int32 [slot]
+
+  const int c_in = p.c_in, c_out = p.c_out;
+  const int bid = xcd_remap(blockIdx.x, gridDim.x);
+  int item = bid, part = -1;
+  if (bid >= hl.full) {
+    item = hl.full + (bid - hl.full) / 4;
+    part = (bid - hl.full) % 4;
+  }
+  const int rt = item / p.n_tiles_n;
+  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hw = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int rh = wave >> 1, chf = wave & 1;
+  const int n0 = (item % p.n_tiles_n) * TN + 64 * chf;  // this wave's first column
+  const bool mine = part < 0 || part == wave;          // this wave multiplies and stores
+  const unsigned char* const rec = p.plan + int64_t(rt) * kPlanBytes;
+  const HaloHeader* const hdr = reinterpret_cast<const HaloHeader*>(rec + kPlanHdr);
+  const int nh = hdr->nh;
+  const uint32_t tmask = hdr->tmask;
+  // This wave's block masks (its four 32-row blocks), 4 bits per tap.
+  uint64_t bml = 0, bmh = 0;
+  if (mine) {
+#pragma unroll
+    for (int k = 0; k < 27; ++k) {
+      const uint64_t f = (hdr->fm[k] >> (4 * rh)) & 15u;
+      if (k < 16) bml |= f << (4 * k);
+      else bmh |= f << (4 * (k - 16));
+    }
+  }
+  auto block_mask = [&](int k) { return uint32_t((k < 16 ? bml >> (4 * k) : bmh >> (4 * (k - 16))) & 15u); };
+  const int nchunks = c_in / KC;
+  const int ntaps = __popc(tmask);
+  const int nst = ntaps * nchunks;
+
+  // crow[q]: caller row of this wave's row 64 q + lane (-1: not stored).
+  int32_t crow[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q)
+    crow[q] = mine ? reinterpret_cast<const int32_t*>(rec + kPlanCrow)[128 * rh + 64 * q + lane] : -1;
+  f32x16 acc[RB][CB];
+#pragma unroll
+  for (int b = 0; b < RB; ++b)
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[b][cb][e] = 0.f;
+
+  // B fragments of stage (c, k): steps s = 0, 1 x this wave's column blocks,
+  // 16 bytes per lane from one contiguous kilobyte each.
+  const uint4* const wf = reinterpret_cast<const uint4*>(p.wp + frag_weight_offset(c_in, c_out));
+  const int ncb = c_out / 32, cb0 = n0 / 32;
+  auto load_b = [&](int c, int k, uint4 (&b)[2][CB]) {
+    const uint4* f = wf + (int64_t((k * nchunks + c) * 2) * ncb + cb0) * 64 + lane;
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) b[s][cb] = f[(s * ncb + cb) * 64];
+  };
+  auto mma_step = [&](uint32_t bm, const hvec (&a)[RB], const uint4 (&b)[CB]) {
+#pragma unroll
+    for (int blk = 0; blk < RB; ++blk) {
+      if ((bm >> blk) & 1u) {
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+          acc[blk][cb] = H::mma32(a[blk], *reinterpret_cast<const hvec*>(&b[cb]), acc[blk][cb]);
+      }
+    }
+  };
+  // Stage sequence: chunk-major, the tile's taps in order within a chunk.
+  // (c, k, rem): the stage's chunk and tap, and the taps after k in the chunk.
+  auto next_stage = [&](int& c, int& k, uint32_t& rem) {
+    if (rem == 0u) {
+      ++c;
+      rem = tmask;
+    }
+    k = __builtin_ctz(rem);
+    rem &= rem - 1u;
+  };
+
+  if (nh >= 0) {
+    for (int q = wave; q < SLOTQ + ROWQ; q += 4) {
+      const bool sl = q < SLOTQ;
+      const unsigned char* g =
+          sl ? rec + kPlanSlots + q * 1024 + lane * 16 : rec + kPlanRows + (q - SLOTQ) * 1024 + lane * 16;
+      copy16_to_lds(g, sl ? s_slotb + q * 1024 : s_rowb + (q - SLOTQ) * 1024);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    bare_barrier();
+    const int32_t* const s_rows = reinterpret_cast<const int32_t*>(s_rowb);
+    // Halo rows of chunk c: slot q*16 + lane/4, piece lane&3 (slot 0 and the
+    // slots past the halo read the zero block).
+    auto fill_halo = [&](int c) {
+      const int nq = (nh + 1 + 15) >> 4;
+      for (int q = wave; q < nq; q += 4) {
+        const int slot = q * 16 + (lane >> 2);
+        const int ch = c * KC + (((lane & 3) ^ ((slot >> 2) & 3)) << 3);
+        const bool ok = slot >= 1 && slot <= nh;
+        const void* g = ok ? static_cast<const void*>(static_cast<const uint16_t*>(p.x) +
+                                                      int64_t(s_rows[slot]) * c_in + ch)
+                           : static_cast<const void*>(p.zeros);
+        copy16_to_lds(g, s_halo + q * 1024);
+      }
+    };
+    // LDS offsets of this lane's four rows (128 rh + 32 blk + lane % 32) at tap k
+    const unsigned char* const slot_lane = s_slotb + (128 * rh + l32 * 4) * 2;
+    auto read_slots = [&](int k) { return *reinterpret_cast<const uint2*>(slot_lane + k * TM * 2); };
+    const uint32_t pa = uint32_t(hw) << 4;  // piece 2 s + hw: offset ^ (pa + 32 s)
+    auto load_a = [&](uint2 so, int s, hvec (&a)[RB]) {
+      const uint32_t o[RB] = {so.x & 0xFFFFu, so.x >> 16, so.y & 0xFFFFu, so.y >> 16};
+#pragma unroll
+      for (int blk = 0; blk < RB; ++blk)
+        a[blk] = *reinterpret_cast<const hvec*>(s_halo + (o[blk] ^ (pa + 32u * s)));
+    };
+    // Stage state: (c, k, rem) of the current stage; (cf, kf, remf) of the
+    // stage whose B fragments are loaded next (two ahead). B and A fragments in
+    // two register sets each, used by alternate stages: a stage multiplies on
+    // its set while the next stage's A fragments (read one stage ahead) and
+    // the B fragments of the stage after (two ahead) land in the other set.
+    int c = 0, k = 0;
+    uint32_t rem = tmask;
+    next_stage(c, k, rem);
+    int cf = c, kf = k;
+    uint32_t remf = rem;
+    uint4 b0[2][CB], b1[2][CB];
+    hvec a0[2][RB], a1[2][RB];
+    int cn = c, kn = k;  // the stage after the current one
+    uint32_t remn = rem;
+    if (nst > 1) next_stage(cn, kn, remn);
+    uint2 so = read_slots(kn);  // slots of the stage after the current one
+    if (nst > 0) {
+      load_b(cf, kf, b0);
+      if (nst > 1) {
+        next_stage(cf, kf, remf);
+        load_b(cf, kf, b1);
+      }
+      fill_halo(0);
+      __builtin_amdgcn_s_waitcnt(0);
+      bare_barrier();  // chunk 0's halo has landed
+      const uint2 s0 = read_slots(k);
+      load_a(s0, 0, a0[0]);
+      load_a(s0, 1, a0[1]);
+    }
+    // One stage on sets (bc, ac); the other sets receive the stages ahead.
+    auto stage = [&](int st, uint4 (&bc)[2][CB], hvec (&ac)[2][RB], hvec (&an)[2][RB]) {
+      const uint32_t bm = block_mask(k);
+      const bool more = st + 1 < nst;
+      const bool opens = more && cn != c;  // the next stage opens a new chunk
+      if (more && !opens) {
+        load_a(so, 0, an[0]);
+        load_a(so, 1, an[1]);
+      }
+      mma_step(bm, ac[0], bc[0]);
+      mma_step(bm, ac[1], bc[1]);
+      if (st + 2 < nst) {
+        next_stage(cf, kf, remf);
+        load_b(cf, kf, bc);
+      }
+      if (opens) {
+        // replace the halo once every wave's reads of this chunk are done,
+        // then read the next stage's A fragments from it
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        bare_barrier();
+        fill_halo(cn);
+        __builtin_amdgcn_s_waitcnt(0);
+        bare_barrier();
+        load_a(so, 0, an[0]);
+        load_a(so, 1, an[1]);
+      }
+      c = cn, k = kn, rem = remn;
+      if (st + 2 < nst) next_stage(cn, kn, remn);
+      so = read_slots(kn);
+    };
+    for (int st = 0; st < nst; st += 2) {
+      stage(st, b0, a0, a1);
+      if (st + 1 < nst) stage(st + 1, b1, a1, a0);
+    }
+  } else {
+    // Too many distinct neighbours: A fragments straight from global memory.
+    // Row 128 rh + 32 blk + lane % 32: caller row and mask.
+    const int32_t* const pc = reinterpret_cast<const int32_t*>(rec + kPlanCrow) + 128 * rh;
+    const uint32_t* const pm = reinterpret_cast<const uint32_t*>(rec + kPlanMask) + 128 * rh;
+    int32_t rr[RB];
+    uint32_t rm[RB];
+#pragma unroll
+    for (int blk = 0; blk < RB; ++blk) {
+      rr[blk] = pc[32 * blk + l32];
+      rm[blk] = pm[32 * blk + l32];
+    }
+    int c = 0, k = 0;
+    uint32_t rem = tmask;
+    for (int st = 0; st < nst; ++st) {
+      next_stage(c, k, rem);
+      const uint32_t bm = block_mask(k);
+      if (bm == 0u) continue;
+      uint4 b[2][CB];
+      load_b(c, k, b);
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        hvec a[RB];
+#pragma unroll
+        for (int blk = 0; blk < RB; ++blk) {
+          const int32_t j = ((rm[blk] >> k) & 1u) ? p.nbr[int64_t(rr[blk]) * 27 + k] : -1;
+          const int ch = c * KC + (2 * s + hw) * 8;
+          const void* g = j >= 0 ? static_cast<const void*>(static_cast<const uint16_t*>(p.x) + int64_t(j) * c_in + ch)
+                                 : static_cast<const void*>(p.zeros);
+          const uint4 raw = *reinterpret_cast<const uint4*>(g);
+          a[blk] = *reinterpret_cast<const hvec*>(&raw);
+        }
+        mma_step(bm, a, b[s]);
+      }
+    }
+  }
+
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  store_tile32<H, RB, CB>(p, acc, crow, n0, reinterpret_cast<float*>(s_halo) + wave * 16 * (32 * CB + 8));
+}
+
+// Workgroups that fit on the device at once (two per CU for fwd_halo), per device.
+int halo_slots() {
+  constexpr int kMaxDev = 64;
+  static std::once_flag once[kMaxDev];
+  static int slots[kMaxDev];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return 0;
+  std::call_once(once[dev], [dev] {
+    int cus = 0;
+    slots[dev] = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess ? 2 * cus : 0;
+  });
+  return slots[dev];
+}
+
+template <bool F16>
+hipError_t launch_halo(const ConvArgs& a, const uint16_t* wp, const uint16_t* zeros, hipStream_t st) {
+  constexpr int TM = kHaloTM, TN = 128;
+  const int64_t mt = (a.n + TM - 1) / TM;
+  const int nt = (a.c_out + TN - 1) / TN;
+  const int64_t items = mt * nt;
+  if (items * 4 > 0x7FFFFFFF) return hipErrorInvalidValue;
+  // Split the last round into 64-row parts when it would hold at most a
+  // quarter of the device's workgroup slots.
+  HaloLaunch hl{int(items), 0};
+  const int64_t slots = halo_slots();
+  if (slots > 0 && items > slots) {
+    const int64_t last = items - (items - 1) / slots * slots;
+    if (last * 4 <= slots) hl = HaloLaunch{int(items - last), int(last)};
+  }
+  RowsArgs p{a.nbr, a.plan, a.srows, a.mask, a.n, a.x, wp, zeros, a.y, a.epi.bias, a.epi.residual,
+             a.epi.act, a.y_dtype == TR_SC_F32 ? 1 : 0, a.c_in, a.c_out, nt};
+  fwd_halo<F16><<<unsigned(hl.full + 4 * hl.split), kThreads, 0, st>>>(p, hl);
+  return hipGetLastError();
+}
+
 template <int FM, int FN, bool F16>
 hipError_t launch_lds(const ConvArgs& a, const uint16_t* wp, const uint16_t* zeros, hipStream_t st) {
   constexpr int TM = 64 * FM, TN = 16 * FN;
@@ -547,7 +954,7 @@ hipError_t launch_lds(const ConvArgs& a, const uint16_t* wp, const uint16_t* zer
   const int nt = (a.c_out + TN - 1) / TN;
   const int64_t grid = mt * nt;
   if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
-  RowsArgs p{a.nbr, a.srows, a.mask, a.n, a.x, wp, zeros, a.y, a.epi.bias, a.epi.residual,
+  RowsArgs p{a.nbr, a.plan, a.srows, a.mask, a.n, a.x, wp, zeros, a.y, a.epi.bias, a.epi.residual,
              a.epi.act, a.y_dtype == TR_SC_F32 ? 1 : 0, a.c_in, a.c_out, nt};
   fwd_lds<FM, FN, F16><<<unsigned(grid), kThreads, 0, st>>>(p);
   return hipGetLastError();
@@ -560,7 +967,7 @@ hipError_t launch_rows(const ConvArgs& a, const uint16_t* wp, const uint16_t* ze
   const int nt = (a.c_out + TN - 1) / TN;
   const int64_t grid = mt * nt;
   if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
-  RowsArgs p{a.nbr, a.srows, a.mask, a.n, a.x, wp, zeros, a.y, a.epi.bias, a.epi.residual,
+  RowsArgs p{a.nbr, a.plan, a.srows, a.mask, a.n, a.x, wp, zeros, a.y, a.epi.bias, a.epi.residual,
              a.epi.act, a.y_dtype == TR_SC_F32 ? 1 : 0, a.c_in, a.c_out, nt};
   fwd_rows<FM, FN, F16, XT><<<unsigned(grid), kThreads, 0, st>>>(p);
   return hipGetLastError();
@@ -582,6 +989,7 @@ hipError_t dispatch(const ConvArgs& a, const uint16_t* p, const uint16_t* zeros,
   // Wide layers: 64-row waves halve the LDS reads of weight fragments per
   // multiply (the weight slice is read once per wave). Narrow layers: 32-row
   // waves give twice the workgroups and a third wave per SIMD.
+  if (halo_shape(a.c_in, a.c_out)) return launch_halo<F16>(a, p, zeros, st);
   if (a.c_out >= 128 && a.c_in >= 256) return launch_rows<4, 8, F16, 1>(a, p, zeros, st);
   if (a.c_out >= 128) return launch_rows<2, 8, F16, 1>(a, p, zeros, st);
   // 64-wide layers over a large voxel set (a decoder level): rows through LDS

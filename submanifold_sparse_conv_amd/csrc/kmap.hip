@@ -228,15 +228,6 @@ __global__ __launch_bounds__(kThreads) void kmap_kernel(const uint64_t* __restri
   }
 }
 
-// Octant pattern of a neighbour mask: bit (dx>0)*4 + (dy>0)*2 + (dz>0) is set
-// when the corner neighbour at (dx, dy, dz), |dx| = |dy| = |dz| = 1, exists.
-// It says on which sides of a thin surface the voxel lies.
-__device__ inline uint32_t octant_key(uint32_t m) {
-  return ((m >> 0) & 1u) | (((m >> 2) & 1u) << 1) | (((m >> 6) & 1u) << 2) | (((m >> 8) & 1u) << 3) |
-         (((m >> 18) & 1u) << 4) | (((m >> 20) & 1u) << 5) | (((m >> 24) & 1u) << 6) |
-         (((m >> 26) & 1u) << 7);
-}
-
 constexpr int kGroupThreads = 1024;
 
 // Row order of the gather-GEMM: inside each window of kGroupWindow Morton-
@@ -330,7 +321,7 @@ __global__ __launch_bounds__(kGroupThreads) void group_rows(const int32_t* __res
 }  // namespace
 
 hipError_t launch_kmap(const uint64_t* skeys, int64_t n, const TableRef& t, const DenseRef* dense, int32_t* nbr,
-                       uint32_t* mask, int32_t* grows, uint32_t* gmask, hipStream_t st) {
+                       uint32_t* mask, int32_t* grows, uint32_t* gmask, unsigned char* plan, hipStream_t st) {
   if (n > 0) {
     const unsigned grid = unsigned((n + kThreads - 1) / kThreads);
     if (dense != nullptr)
@@ -339,6 +330,9 @@ hipError_t launch_kmap(const uint64_t* skeys, int64_t n, const TableRef& t, cons
       kmap_kernel<false><<<grid, kThreads, 0, st>>>(skeys, n, t, DenseRef{}, nbr, mask);
     group_rows<<<unsigned((n + kGroupWindow - 1) / kGroupWindow), kGroupThreads, 0, st>>>(t.srows, mask, n,
                                                                                          grows, gmask);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_halo_plan(t.srows, mask, nbr, n, plan, st);
   }
   return hipGetLastError();
 }

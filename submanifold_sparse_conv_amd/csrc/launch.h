@@ -46,10 +46,45 @@ hipError_t launch_dense_hash(const int32_t* coords, int64_t n, int g, int batch,
 // order: grows / gmask = Morton order regrouped inside windows of kGroupWindow
 // voxels by the octant pattern of the neighbour mask.
 constexpr int kGroupWindow = 4096;
+
+// Halo plan of the gather-GEMM over tiles of kHaloTM Morton-consecutive voxels:
+// per tile, the rows in tile order (octant-regrouped inside the tile), the
+// tile's distinct neighbour rows ("halo", numbered from slot 1; slot 0 stands
+// for an absent neighbour) and the slot of every (row, tap). One record of
+// kPlanBytes per tile, sections 1 KB-aligned:
+//   [kPlanHdr]   HaloHeader
+//   [kPlanRows]  int32 caller row of halo slot s (s = 1 .. nh), kHaloCap entries
+//   [kPlanCrow]  int32 caller row at tile position r (-1 past the end)
+//   [kPlanMask]  uint32 27-bit neighbour mask at tile position r
+//   [kPlanSlots] uint16 LDS byte offset, in the gather-GEMM's halo of
+//                kHaloRowBytes-byte rows, of the row of (tap k, position r) --
+//                slot s * kHaloRowBytes + (((s >> 2) & 3) << 4) -- at
+//                k * kHaloTM + sidx(r), sidx(r) = 128 (r / 128) + 4 (r % 32) +
+//                (r / 32) % 4: a lane's four 32-row blocks at one tap are adjacent
+constexpr int kHaloTM = 256;
+constexpr int kHaloCap = 736;     // halo slots of one tile, slot 0 included
+constexpr int kHaloHash = 2048;   // dedup table entries (power of two)
+constexpr int kHaloProbes = 64;   // a longer probe run marks the tile as not fitting
+constexpr int kHaloRowBytes = 64; // halo rows in LDS: 32 half-precision channels
+static_assert(kHaloCap * kHaloRowBytes + 48 < 65536, "halo offsets fit in 16 bits");
+constexpr int kPlanHdr = 0, kPlanRows = 1024, kPlanCrow = 4096, kPlanMask = 5120, kPlanSlots = 6144;
+constexpr int kPlanSlotBytes = 27 * kHaloTM * 2;  // 13,824
+constexpr int kPlanBytes = kPlanSlots + 14336;    // slots padded to whole kilobytes
+static_assert(kPlanRows + kHaloCap * 4 <= kPlanCrow && kPlanSlotBytes <= 14336, "plan record layout");
+struct HaloHeader {
+  int32_t nh;         // halo rows (slots 1 .. nh); -1: the halo does not fit, gather from global memory
+  uint32_t tmask;     // taps some row of the tile has
+  uint16_t fm[27];    // bit b: 32-row block b (rows 32b .. 32b + 31) has tap k
+};
+inline int64_t halo_tiles(int64_t n) { return (n + kHaloTM - 1) / kHaloTM; }
+
 // dense: the hash's occupancy bitmap when it was built in a known grid (the
-// block records are read from it instead of the table), else null.
+// block records are read from it instead of the table), else null. plan:
+// halo_tiles(n) records of kPlanBytes.
 hipError_t launch_kmap(const uint64_t* skeys, int64_t n, const TableRef& t, const DenseRef* dense, int32_t* nbr,
-                       uint32_t* mask, int32_t* grows, uint32_t* gmask, hipStream_t st);
+                       uint32_t* mask, int32_t* grows, uint32_t* gmask, unsigned char* plan, hipStream_t st);
+hipError_t launch_halo_plan(const int32_t* srows, const uint32_t* mask, const int32_t* nbr, int64_t n,
+                            unsigned char* plan, hipStream_t st);
 
 // Forward kernels. `srows` is the row order of the tiles (position -> caller
 // row), `mask` the 27-bit neighbour mask of the voxel at each position.
@@ -62,6 +97,7 @@ struct ConvArgs {
   const int32_t* nbr;   // [n, 27] caller order
   const int32_t* srows; // [n]
   const uint32_t* mask; // [n] Morton order
+  const unsigned char* plan;  // halo plan records (halo_tiles(n) x kPlanBytes)
   int64_t n;
   const void* x;
   const void* w;
@@ -73,10 +109,28 @@ struct ConvArgs {
 hipError_t launch_forward_simple_f32(const ConvArgs& a, hipStream_t st);
 // wp[k][co][ci] = w[k][ci][co] (bf16 or fp16), the matrix-core operand layout,
 // followed by 256 zero bytes (packed_weight_elems elements, then the zeros).
-inline int64_t packed_weight_elems(int c_in, int c_out) {
+__host__ __device__ inline int64_t packed_weight_elems(int c_in, int c_out) {
   return (int64_t(27) * c_in * c_out + 127) / 128 * 128;  // keeps the zero block 256-byte aligned
 }
 hipError_t launch_pack_weights(const void* w, void* wp, int c_in, int c_out, hipStream_t st);
+// Shapes the halo gather-GEMM takes (half-precision features). Their packed
+// weights carry, after the zero block, a second copy in MFMA fragment order:
+// fragment (tap k, 32-channel chunk c, 16-channel step s, 32-column block b)
+// is 64 lanes x 8 halves at ((k * (c_in / 32) + c) * 2 + s) * (c_out / 32) + b,
+// lane l holding column 32 b + l % 32, input channels 32 c + 16 s + 8 (l / 32) ..
+// + 8 -- one contiguous kilobyte per fragment.
+inline bool halo_shape(int c_in, int c_out) {
+  return c_in % 32 == 0 && c_out % 128 == 0 && c_in <= 256 && c_out <= 256;
+}
+__host__ __device__ inline int64_t frag_weight_offset(int c_in, int c_out) {  // in halves
+  return packed_weight_elems(c_in, c_out) + 128;  // after the 256-byte zero block
+}
+inline int64_t packed_half_bytes(int c_in, int c_out) {
+  const int64_t base = packed_weight_elems(c_in, c_out) * 2 + 256;
+  return halo_shape(c_in, c_out) ? base + int64_t(27) * c_in * c_out * 2 : base;
+}
+// Fragment-order copy of a [27][c_out][c_in] packing (wp) at wp + frag_weight_offset.
+hipError_t launch_pack_frag(void* wp, int c_in, int c_out, hipStream_t st);
 hipError_t launch_forward_mfma(const ConvArgs& a, const void* wp, hipStream_t st);
 
 // Backward. Data-gradient weights: the forward packing of the c_out -> c_in

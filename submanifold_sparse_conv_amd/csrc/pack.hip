@@ -77,7 +77,37 @@ __global__ __launch_bounds__(kThreads) void pack_weights_v8(const uint16_t* __re
   }
 }
 
+// Fragment-order copy: thread = one lane of one fragment, 16 bytes in and out
+// (fragment layout in launch.h, next to halo_shape).
+__global__ __launch_bounds__(kThreads) void pack_frag(const uint4* __restrict__ wp, uint4* __restrict__ wf, int c_in,
+                                                      int c_out, int64_t total) {
+  const int nc = c_in / 32, ncb = c_out / 32;
+  for (int64_t e = int64_t(blockIdx.x) * kThreads + threadIdx.x; e < total; e += int64_t(gridDim.x) * kThreads) {
+    const int lane = int(e & 63);
+    int64_t f = e >> 6;
+    const int cb = int(f % ncb);
+    f /= ncb;
+    const int s = int(f & 1);
+    f >>= 1;
+    const int c = int(f % nc);
+    const int k = int(f / nc);
+    const int col = cb * 32 + (lane & 31);
+    const int ci = c * 32 + s * 16 + (lane >> 5) * 8;
+    wf[e] = wp[((int64_t(k) * c_out + col) * c_in + ci) / 8];
+  }
+}
+
 }  // namespace
+
+hipError_t launch_pack_frag(void* wp, int c_in, int c_out, hipStream_t st) {
+  const int64_t total = int64_t(27) * c_in * c_out / 8;  // 16-byte pieces
+  const int64_t blocks = (total + kThreads - 1) / kThreads;
+  uint16_t* base = static_cast<uint16_t*>(wp);
+  pack_frag<<<unsigned(blocks < 4096 ? blocks : 4096), kThreads, 0, st>>>(
+      reinterpret_cast<const uint4*>(base), reinterpret_cast<uint4*>(base + frag_weight_offset(c_in, c_out)), c_in,
+      c_out, total);
+  return hipGetLastError();
+}
 
 hipError_t launch_pack_weights(const void* w, void* wp, int c_in, int c_out, hipStream_t st) {
   dim3 grid(unsigned((c_out + 63) / 64), unsigned((c_in + 63) / 64), 27);
@@ -90,7 +120,9 @@ hipError_t launch_pack_weights(const void* w, void* wp, int c_in, int c_out, hip
     pack_weights_v8<<<grid, kThreads, 0, st>>>(src, dst, c_in, c_out, zeros);
   else
     pack_weights<<<grid, kThreads, 0, st>>>(src, dst, c_in, c_out, zeros);
-  return hipGetLastError();
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !halo_shape(c_in, c_out)) return e;
+  return launch_pack_frag(wp, c_in, c_out, st);
 }
 
 }  // namespace trsc
