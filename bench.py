@@ -30,7 +30,7 @@ PEAK_FP32_VECTOR_TFLOPS = 157.3  # MI355X fp32 vector (256 CUs, 2.4 GHz)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fwd_mfma.json")
 # the gather-GEMM kernel and the headers it includes: counters taken on other sources are stale
 GEMM_SOURCES = [os.path.join(ROOT, "submanifold_sparse_conv_amd", "csrc", f)
-                for f in ("gemm_mfma.hip", "common.h", "launch.h")]
+                for f in ("gemm_mfma.hip", "common.h", "launch.h", "halo_plan.hip")]
 
 WORKLOAD_NAMES = {
     "T": "16^3 sphere shell (radius 6, thickness 1), C 8->8 fp32",
@@ -570,7 +570,7 @@ def main():
     main_cfg = config_record(args.config, wl, M, (t_hash, t_map, t_pack, t_gemm), t_gemm_ss,
                              hash_without_grid(sc, torch, coords))
     if wl.dtype == "bf16":
-        roof = {"kernel": "fwd_rows (gather-GEMM)", "bound": "mfma", "achieved": gemm_tflops,
+        roof = {"kernel": "fwd_halo (gather-GEMM over LDS-staged halo rows)", "bound": "mfma", "achieved": gemm_tflops,
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": gemm_tflops / PEAK_BF16_TFLOPS,
                 "traffic": traffic}
     else:  # fp32 features and weights: the plain FMA kernel

@@ -96,6 +96,7 @@ struct tr_sc_kmap {
   const int32_t* grows;        // tile row order (position -> caller row)
   const uint32_t* gmask;       // neighbour mask of each position
   const unsigned char* plan;   // halo plan records of the gather-GEMM
+  const int32_t* order;        // its tiles in launch order
 };
 
 extern "C" {
@@ -314,10 +315,12 @@ void tr_sparseconv_hash_destroy(tr_sc_hash* h) {
 }
 
 // Kernel-map workspace: mask[n] (Morton order) | grows[n] | gmask[n] (tile
-// order) | halo plan (one record per tile of kHaloTM voxels).
+// order) | halo plan (one record per tile of kHaloTM voxels) | the tiles'
+// launch order.
 size_t tr_sparseconv_kmap_workspace_bytes(int64_t n) {
   if (n < 0 || n > kMaxN) return 0;
-  return 3 * align_up(size_t(n) * 4, 256) + size_t(halo_tiles(n)) * kPlanBytes + 256;
+  return 3 * align_up(size_t(n) * 4, 256) + size_t(halo_tiles(n)) * kPlanBytes +
+         align_up(size_t(halo_tiles(n)) * 4, 256) + 256;
 }
 
 int tr_sparseconv_build_kernel_map(const tr_sc_hash* h, int32_t* nbr, void* workspace, size_t ws_bytes,
@@ -337,8 +340,9 @@ int tr_sparseconv_build_kernel_map(const tr_sc_hash* h, int32_t* nbr, void* work
   int32_t* grows = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + part);
   uint32_t* gmask = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + 2 * part);
   unsigned char* plan = static_cast<unsigned char*>(workspace) + 3 * part;
+  int32_t* order = reinterpret_cast<int32_t*>(plan + size_t(halo_tiles(h->n)) * kPlanBytes);
   hipError_t e = launch_kmap(h->skeys, h->n, h->table, h->has_dense ? &h->dense : nullptr, nbr, mask, grows, gmask,
-                             plan, static_cast<hipStream_t>(stream));
+                             plan, order, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "build_kernel_map");
   tr_sc_kmap* m = new tr_sc_kmap;
   m->magic = kKmapMagic;
@@ -347,6 +351,7 @@ int tr_sparseconv_build_kernel_map(const tr_sc_hash* h, int32_t* nbr, void* work
   m->grows = grows;
   m->gmask = gmask;
   m->plan = plan;
+  m->order = order;
   *out = m;
   return TR_SC_OK;
 }
@@ -394,7 +399,7 @@ int run_forward(const char* who, const tr_sc_kmap* m, const void* x, int x_dtype
   if (x == y) return fail(TR_SC_ERR_INVALID_ARG, "%s: x and y are the same buffer", who);
   if (int64_t(m->n) * c_out >= (int64_t(1) << 40) || int64_t(m->n) * c_in >= (int64_t(1) << 40))
     return fail(TR_SC_ERR_UNSUPPORTED, "%s: tensor too large", who);
-  ConvArgs a{m->nbr, m->grows, m->gmask, m->plan, m->n, x, wp, y, c_in, c_out, x_dtype, w_dtype, y_dtype, epi};
+  ConvArgs a{m->nbr, m->grows, m->gmask, m->plan, m->order, m->n, x, wp, y, c_in, c_out, x_dtype, w_dtype, y_dtype, epi};
   hipError_t e;
   if (w_dtype == TR_SC_F32) {
     e = launch_forward_simple_f32(a, st);

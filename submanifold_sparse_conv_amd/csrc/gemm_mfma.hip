@@ -33,6 +33,7 @@
 // contiguous), the operand order of the matrix instruction, followed by a
 // 256-byte block of zeros (the copy source of absent neighbours).
 #include <mutex>
+#include <utility>
 
 #include "common.h"
 #include "launch.h"
@@ -46,6 +47,17 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kThreads = 256;
+
+// f(std::integral_constant<int, 0>{}) .. f(std::integral_constant<int, N-1>{}),
+// unrolled at compile time.
+template <class F, int... J>
+__device__ __forceinline__ void static_for_seq(F&& f, std::integer_sequence<int, J...>) {
+  (f(std::integral_constant<int, J>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_seq(f, std::make_integer_sequence<int, N>{});
+}
 
 // The two half types of the matrix cores: their MFMA and conversions.
 template <bool F16>
@@ -106,6 +118,7 @@ __device__ __forceinline__ void split_terms(const uint4 (&raw)[2], typename H::v
 struct RowsArgs {
   const int32_t* nbr;
   const unsigned char* plan;  // halo plan records (fwd_halo)
+  const int32_t* order;       // halo tiles in launch order (fwd_halo)
   const int32_t* srows;
   const uint32_t* vmask;
   int64_t n;
@@ -672,16 +685,17 @@ __device__ __forceinline__ void store_tile32(const RowsArgs& p, const f32x16 (&a
 //
 // Work items: blockIdx -> (row tile, column tile); when the last round of
 // workgroups would hold few items (split > 0), each of the last `split` items
-// becomes four workgroups, each multiplying for one wave's block (the other
-// three waves only help with the halo copies), so the last round takes about
-// a quarter of a tile.
+// becomes sixteen workgroups, each multiplying and storing one 32-row block of
+// one wave (the other waves only help with the halo copies), so that the last
+// round is short.
 constexpr int kHaloKC = 32;
 static_assert(kHaloRowBytes == kHaloKC * 2, "halo rows hold one chunk of half-precision channels");
 
 struct HaloLaunch {
   int full;   // work items run whole
-  int split;  // items after them, each run as four parts
+  int split;  // items after them, each run as kHaloParts parts
 };
+constexpr int kHaloParts = 16;  // one part per (wave, 32-row block)
 
 template <bool F16>
 __global__ __launch_bounds__(kThreads, 2) void fwd_halo(const RowsArgs p, const HaloLaunch hl) {
@@ -697,42 +711,45 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_halo(const RowsArgs p, const 
   __shared__ __attribute__((aligned(1024))) unsigned char s_rowb[ROWQ * 1024];    // int32 [slot]
 
   const int c_in = p.c_in, c_out = p.c_out;
-  const int bid = xcd_remap(blockIdx.x, gridDim.x);
+  // Workgroups take the tiles in the plan's order (longest first): the
+  // hardware starts them in index order as slots free up, so the shortest
+  // tiles and the split parts fill the end.
+  const int bid = blockIdx.x;
   int item = bid, part = -1;
   if (bid >= hl.full) {
-    item = hl.full + (bid - hl.full) / 4;
-    part = (bid - hl.full) % 4;
+    item = hl.full + (bid - hl.full) / kHaloParts;
+    part = (bid - hl.full) % kHaloParts;
   }
-  const int rt = item / p.n_tiles_n;
+  const int rt = p.order[item / p.n_tiles_n];
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hw = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int rh = wave >> 1, chf = wave & 1;
   const int n0 = (item % p.n_tiles_n) * TN + 64 * chf;  // this wave's first column
-  const bool mine = part < 0 || part == wave;          // this wave multiplies and stores
+  const bool mine = part < 0 || part / 4 == wave;      // this wave multiplies and stores
+  // a part: one 32-row block of one wave (its other blocks neither multiply nor store)
+  const uint32_t pblk = part < 0 ? 15u : 1u << (part & 3);
   const unsigned char* const rec = p.plan + int64_t(rt) * kPlanBytes;
   const HaloHeader* const hdr = reinterpret_cast<const HaloHeader*>(rec + kPlanHdr);
   const int nh = hdr->nh;
-  const uint32_t tmask = hdr->tmask;
   // This wave's block masks (its four 32-row blocks), 4 bits per tap.
   uint64_t bml = 0, bmh = 0;
   if (mine) {
 #pragma unroll
     for (int k = 0; k < 27; ++k) {
-      const uint64_t f = (hdr->fm[k] >> (4 * rh)) & 15u;
+      const uint64_t f = (hdr->fm[k] >> (4 * rh)) & pblk;
       if (k < 16) bml |= f << (4 * k);
       else bmh |= f << (4 * (k - 16));
     }
   }
-  auto block_mask = [&](int k) { return uint32_t((k < 16 ? bml >> (4 * k) : bmh >> (4 * (k - 16))) & 15u); };
-  const int nchunks = c_in / KC;
-  const int ntaps = __popc(tmask);
-  const int nst = ntaps * nchunks;
+  const int nchunks = c_in / KC;  // even (halo_shape)
 
   // crow[q]: caller row of this wave's row 64 q + lane (-1: not stored).
   int32_t crow[2];
 #pragma unroll
   for (int q = 0; q < 2; ++q)
-    crow[q] = mine ? reinterpret_cast<const int32_t*>(rec + kPlanCrow)[128 * rh + 64 * q + lane] : -1;
+    crow[q] = mine && ((pblk >> (2 * q + hw)) & 1u)
+                  ? reinterpret_cast<const int32_t*>(rec + kPlanCrow)[128 * rh + 64 * q + lane]
+                  : -1;
   f32x16 acc[RB][CB];
 #pragma unroll
   for (int b = 0; b < RB; ++b)
@@ -741,37 +758,35 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_halo(const RowsArgs p, const 
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[b][cb][e] = 0.f;
 
-  // B fragments of stage (c, k): steps s = 0, 1 x this wave's column blocks,
-  // 16 bytes per lane from one contiguous kilobyte each.
-  const uint4* const wf = reinterpret_cast<const uint4*>(p.wp + frag_weight_offset(c_in, c_out));
+  // B fragments of stage g (chunk g / 27, tap g % 27): steps s = 0, 1 x this
+  // wave's column blocks, 16 bytes per lane from one contiguous kilobyte each;
+  // the stages' fragments are at a constant stride.
   const int ncb = c_out / 32, cb0 = n0 / 32;
-  auto load_b = [&](int c, int k, uint4 (&b)[2][CB]) {
-    const uint4* f = wf + (int64_t((k * nchunks + c) * 2) * ncb + cb0) * 64 + lane;
+  const uint4* const wf = reinterpret_cast<const uint4*>(p.wp + frag_weight_offset(c_in, c_out)) + cb0 * 64 + lane;
+  const int64_t bstride = int64_t(2) * ncb * 64;  // uint4 per stage
+  auto load_b = [&](int g, uint4 (&b)[2][CB]) {
+    const uint4* f = wf + g * bstride;
 #pragma unroll
     for (int s = 0; s < 2; ++s)
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb) b[s][cb] = f[(s * ncb + cb) * 64];
   };
-  auto mma_step = [&](uint32_t bm, const hvec (&a)[RB], const uint4 (&b)[CB]) {
+  // The multiplies of one stage for the blocks in bm, step by step: an
+  // accumulator's two products of a stage are a whole step apart, so the
+  // second does not wait for the first's result.
+  auto mma_stage = [&](uint32_t bm, const hvec (&a)[2][RB], const uint4 (&b)[2][CB]) {
 #pragma unroll
-    for (int blk = 0; blk < RB; ++blk) {
-      if ((bm >> blk) & 1u) {
+    for (int s = 0; s < 2; ++s)
 #pragma unroll
-        for (int cb = 0; cb < CB; ++cb)
-          acc[blk][cb] = H::mma32(a[blk], *reinterpret_cast<const hvec*>(&b[cb]), acc[blk][cb]);
+      for (int blk = 0; blk < RB; ++blk) {
+        if ((bm >> blk) & 1u) {
+#pragma unroll
+          for (int cb = 0; cb < CB; ++cb)
+            acc[blk][cb] = H::mma32(a[s][blk], *reinterpret_cast<const hvec*>(&b[s][cb]), acc[blk][cb]);
+        }
       }
-    }
   };
-  // Stage sequence: chunk-major, the tile's taps in order within a chunk.
-  // (c, k, rem): the stage's chunk and tap, and the taps after k in the chunk.
-  auto next_stage = [&](int& c, int& k, uint32_t& rem) {
-    if (rem == 0u) {
-      ++c;
-      rem = tmask;
-    }
-    k = __builtin_ctz(rem);
-    rem &= rem - 1u;
-  };
+  const int nst = nchunks * 27;  // stages: every chunk runs all 27 taps (a tap no row has multiplies nothing)
 
   if (nh >= 0) {
     for (int q = wave; q < SLOTQ + ROWQ; q += 4) {
@@ -801,74 +816,58 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_halo(const RowsArgs p, const 
     const unsigned char* const slot_lane = s_slotb + (128 * rh + l32 * 4) * 2;
     auto read_slots = [&](int k) { return *reinterpret_cast<const uint2*>(slot_lane + k * TM * 2); };
     const uint32_t pa = uint32_t(hw) << 4;  // piece 2 s + hw: offset ^ (pa + 32 s)
-    auto load_a = [&](uint2 so, int s, hvec (&a)[RB]) {
+    auto load_a = [&](uint2 so, hvec (&a)[2][RB]) {
       const uint32_t o[RB] = {so.x & 0xFFFFu, so.x >> 16, so.y & 0xFFFFu, so.y >> 16};
 #pragma unroll
-      for (int blk = 0; blk < RB; ++blk)
-        a[blk] = *reinterpret_cast<const hvec*>(s_halo + (o[blk] ^ (pa + 32u * s)));
+      for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int blk = 0; blk < RB; ++blk)
+          a[s][blk] = *reinterpret_cast<const hvec*>(s_halo + (o[blk] ^ (pa + 32u * s)));
     };
-    // Stage state: (c, k, rem) of the current stage; (cf, kf, remf) of the
-    // stage whose B fragments are loaded next (two ahead). B and A fragments in
-    // two register sets each, used by alternate stages: a stage multiplies on
-    // its set while the next stage's A fragments (read one stage ahead) and
-    // the B fragments of the stage after (two ahead) land in the other set.
-    int c = 0, k = 0;
-    uint32_t rem = tmask;
-    next_stage(c, k, rem);
-    int cf = c, kf = k;
-    uint32_t remf = rem;
+    // Registers: A and B fragments in two sets used by alternate stages. A
+    // stage multiplies on its set while the next stage's A fragments (read one
+    // stage ahead, within a chunk) and the B fragments of the stage after next
+    // land in the other set; `so` holds the slots of the next stage's tap.
     uint4 b0[2][CB], b1[2][CB];
     hvec a0[2][RB], a1[2][RB];
-    int cn = c, kn = k;  // the stage after the current one
-    uint32_t remn = rem;
-    if (nst > 1) next_stage(cn, kn, remn);
-    uint2 so = read_slots(kn);  // slots of the stage after the current one
-    if (nst > 0) {
-      load_b(cf, kf, b0);
-      if (nst > 1) {
-        next_stage(cf, kf, remf);
-        load_b(cf, kf, b1);
-      }
-      fill_halo(0);
-      __builtin_amdgcn_s_waitcnt(0);
-      bare_barrier();  // chunk 0's halo has landed
-      const uint2 s0 = read_slots(k);
-      load_a(s0, 0, a0[0]);
-      load_a(s0, 1, a0[1]);
-    }
-    // One stage on sets (bc, ac); the other sets receive the stages ahead.
+    load_b(0, b0);
+    load_b(1, b1);
+    fill_halo(0);
+    __builtin_amdgcn_s_waitcnt(0);
+    bare_barrier();  // chunk 0's halo has landed
+    load_a(read_slots(0), a0);
+    uint2 so = read_slots(1);
+    // Stage st = 27 c + k. Two stages per iteration (nst is even), so that
+    // each stage's register sets are fixed; the stage's loads are issued
+    // unconditionally (clamped past the end, read again after a halo refill)
+    // so that the waits the compiler places before the multiplies stay exact.
+    int c = 0, k = 0;
     auto stage = [&](int st, uint4 (&bc)[2][CB], hvec (&ac)[2][RB], hvec (&an)[2][RB]) {
-      const uint32_t bm = block_mask(k);
-      const bool more = st + 1 < nst;
-      const bool opens = more && cn != c;  // the next stage opens a new chunk
-      if (more && !opens) {
-        load_a(so, 0, an[0]);
-        load_a(so, 1, an[1]);
+      const uint32_t bm = uint32_t((k < 16 ? bml >> (4 * k) : bmh >> (4 * (k - 16))) & 15u);
+      load_a(so, an);                               // the next stage (same chunk unless k == 26)
+      so = read_slots(k < 25 ? k + 2 : k - 25);     // the stage after next
+      mma_stage(bm, ac, bc);
+      load_b(st + 2 < nst ? st + 2 : st, bc);       // the stage after next
+      if (k == 26) {
+        if (c + 1 < nchunks) {
+          // the next stage opens chunk c + 1: replace the halo once every
+          // wave's reads of this chunk are done, then read its first A fragments
+          __builtin_amdgcn_s_waitcnt(0xC07F);
+          bare_barrier();
+          fill_halo(c + 1);
+          __builtin_amdgcn_s_waitcnt(0);
+          bare_barrier();
+          load_a(read_slots(0), an);
+        }
+        ++c;
+        k = 0;
+      } else {
+        ++k;
       }
-      mma_step(bm, ac[0], bc[0]);
-      mma_step(bm, ac[1], bc[1]);
-      if (st + 2 < nst) {
-        next_stage(cf, kf, remf);
-        load_b(cf, kf, bc);
-      }
-      if (opens) {
-        // replace the halo once every wave's reads of this chunk are done,
-        // then read the next stage's A fragments from it
-        __builtin_amdgcn_s_waitcnt(0xC07F);
-        bare_barrier();
-        fill_halo(cn);
-        __builtin_amdgcn_s_waitcnt(0);
-        bare_barrier();
-        load_a(so, 0, an[0]);
-        load_a(so, 1, an[1]);
-      }
-      c = cn, k = kn, rem = remn;
-      if (st + 2 < nst) next_stage(cn, kn, remn);
-      so = read_slots(kn);
     };
     for (int st = 0; st < nst; st += 2) {
       stage(st, b0, a0, a1);
-      if (st + 1 < nst) stage(st + 1, b1, a1, a0);
+      stage(st + 1, b1, a1, a0);
     }
   } else {
     // Too many distinct neighbours: A fragments straight from global memory.
@@ -882,28 +881,26 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_halo(const RowsArgs p, const 
       rr[blk] = pc[32 * blk + l32];
       rm[blk] = pm[32 * blk + l32];
     }
-    int c = 0, k = 0;
-    uint32_t rem = tmask;
-    for (int st = 0; st < nst; ++st) {
-      next_stage(c, k, rem);
-      const uint32_t bm = block_mask(k);
+    for (int g = 0; g < nst; ++g) {
+      const int c = g / 27, k = g - 27 * (g / 27);
+      const uint32_t bm = uint32_t((k < 16 ? bml >> (4 * k) : bmh >> (4 * (k - 16))) & 15u);
       if (bm == 0u) continue;
       uint4 b[2][CB];
-      load_b(c, k, b);
+      load_b(g, b);
+      hvec a[2][RB];
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
-        hvec a[RB];
 #pragma unroll
         for (int blk = 0; blk < RB; ++blk) {
           const int32_t j = ((rm[blk] >> k) & 1u) ? p.nbr[int64_t(rr[blk]) * 27 + k] : -1;
           const int ch = c * KC + (2 * s + hw) * 8;
-          const void* g = j >= 0 ? static_cast<const void*>(static_cast<const uint16_t*>(p.x) + int64_t(j) * c_in + ch)
-                                 : static_cast<const void*>(p.zeros);
-          const uint4 raw = *reinterpret_cast<const uint4*>(g);
-          a[blk] = *reinterpret_cast<const hvec*>(&raw);
+          const void* gp = j >= 0 ? static_cast<const void*>(static_cast<const uint16_t*>(p.x) + int64_t(j) * c_in + ch)
+                                  : static_cast<const void*>(p.zeros);
+          const uint4 raw = *reinterpret_cast<const uint4*>(gp);
+          a[s][blk] = *reinterpret_cast<const hvec*>(&raw);
         }
-        mma_step(bm, a, b[s]);
       }
+      mma_stage(bm, a, b);
     }
   }
 
@@ -932,18 +929,18 @@ hipError_t launch_halo(const ConvArgs& a, const uint16_t* wp, const uint16_t* ze
   const int64_t mt = (a.n + TM - 1) / TM;
   const int nt = (a.c_out + TN - 1) / TN;
   const int64_t items = mt * nt;
-  if (items * 4 > 0x7FFFFFFF) return hipErrorInvalidValue;
-  // Split the last round into 64-row parts when it would hold at most a
-  // quarter of the device's workgroup slots.
+  if (items * kHaloParts > 0x7FFFFFFF) return hipErrorInvalidValue;
+  // Split the last round into parts when it would hold at most a sixteenth
+  // of the device's workgroup slots.
   HaloLaunch hl{int(items), 0};
   const int64_t slots = halo_slots();
   if (slots > 0 && items > slots) {
     const int64_t last = items - (items - 1) / slots * slots;
-    if (last * 4 <= slots) hl = HaloLaunch{int(items - last), int(last)};
+    if (last * kHaloParts <= slots) hl = HaloLaunch{int(items - last), int(last)};
   }
-  RowsArgs p{a.nbr, a.plan, a.srows, a.mask, a.n, a.x, wp, zeros, a.y, a.epi.bias, a.epi.residual,
+  RowsArgs p{a.nbr, a.plan, a.order, a.srows, a.mask, a.n, a.x, wp, zeros, a.y, a.epi.bias, a.epi.residual,
              a.epi.act, a.y_dtype == TR_SC_F32 ? 1 : 0, a.c_in, a.c_out, nt};
-  fwd_halo<F16><<<unsigned(hl.full + 4 * hl.split), kThreads, 0, st>>>(p, hl);
+  fwd_halo<F16><<<unsigned(hl.full + kHaloParts * hl.split), kThreads, 0, st>>>(p, hl);
   return hipGetLastError();
 }
 
@@ -954,7 +951,7 @@ hipError_t launch_lds(const ConvArgs& a, const uint16_t* wp, const uint16_t* zer
   const int nt = (a.c_out + TN - 1) / TN;
   const int64_t grid = mt * nt;
   if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
-  RowsArgs p{a.nbr, a.plan, a.srows, a.mask, a.n, a.x, wp, zeros, a.y, a.epi.bias, a.epi.residual,
+  RowsArgs p{a.nbr, a.plan, a.order, a.srows, a.mask, a.n, a.x, wp, zeros, a.y, a.epi.bias, a.epi.residual,
              a.epi.act, a.y_dtype == TR_SC_F32 ? 1 : 0, a.c_in, a.c_out, nt};
   fwd_lds<FM, FN, F16><<<unsigned(grid), kThreads, 0, st>>>(p);
   return hipGetLastError();
@@ -967,7 +964,7 @@ hipError_t launch_rows(const ConvArgs& a, const uint16_t* wp, const uint16_t* ze
   const int nt = (a.c_out + TN - 1) / TN;
   const int64_t grid = mt * nt;
   if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
-  RowsArgs p{a.nbr, a.plan, a.srows, a.mask, a.n, a.x, wp, zeros, a.y, a.epi.bias, a.epi.residual,
+  RowsArgs p{a.nbr, a.plan, a.order, a.srows, a.mask, a.n, a.x, wp, zeros, a.y, a.epi.bias, a.epi.residual,
              a.epi.act, a.y_dtype == TR_SC_F32 ? 1 : 0, a.c_in, a.c_out, nt};
   fwd_rows<FM, FN, F16, XT><<<unsigned(grid), kThreads, 0, st>>>(p);
   return hipGetLastError();

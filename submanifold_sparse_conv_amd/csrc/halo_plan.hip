@@ -106,31 +106,41 @@ __global__ __launch_bounds__(kPlanThreads) void halo_plan(const int32_t* __restr
   reinterpret_cast<uint32_t*>(rec + kPlanMask)[r] = m;
   s_pmask[r] = m;
 
-  // (2) The item's neighbours (all 27 loads in flight), inserted into the table.
+  // (2) The item's neighbours (all 27 loads in flight), inserted into the
+  // table: every first probe issued together, then the collisions retried
+  // (a run longer than kHaloProbes marks the tile as not fitting).
   {
     int32_t jv[27];
+    int hv[27];
 #pragma unroll
     for (int k = 0; k < 27; ++k) jv[k] = ((m >> k) & 1u) ? nbr[int64_t(cr) * 27 + k] : -1;
-    bool over = false;
+#pragma unroll
+    for (int k = 0; k < 27; ++k) hv[k] = jv[k] >= 0 ? int((uint32_t(jv[k]) * 2654435761u) >> (32 - kHaloHashBits)) : -1;
+    uint32_t left = 0;  // taps still to place
 #pragma unroll
     for (int k = 0; k < 27; ++k) {
-      const int32_t j = jv[k];
-      int h = -1;
-      if (j >= 0 && !over) {
-        h = int((uint32_t(j) * 2654435761u) >> 21) & (kHaloHash - 1);
-        for (int probe = 0;; ++probe) {
-          if (probe == kHaloProbes) {
-            over = true;
-            h = -1;
-            break;
-          }
-          const int32_t old = atomicCAS(&tab[h], -1, j);
-          if (old == -1 || old == j) break;
-          h = (h + 1) & (kHaloHash - 1);
+      if (hv[k] >= 0) {
+        const int32_t old = atomicCAS(&tab[hv[k]], -1, jv[k]);
+        if (old != -1 && old != jv[k]) left |= 1u << k;
+      }
+    }
+    bool over = false;
+    for (int probe = 1; left != 0u; ++probe) {
+      if (probe == kHaloProbes) {
+        over = true;
+        break;
+      }
+#pragma unroll
+      for (int k = 0; k < 27; ++k) {
+        if ((left >> k) & 1u) {
+          hv[k] = (hv[k] + 1) & (kHaloHash - 1);
+          const int32_t old = atomicCAS(&tab[hv[k]], -1, jv[k]);
+          if (old == -1 || old == jv[k]) left &= ~(1u << k);
         }
       }
-      s_slot[k * kHaloTM + sx] = int16_t(h);
     }
+#pragma unroll
+    for (int k = 0; k < 27; ++k) s_slot[k * kHaloTM + sx] = int16_t(over ? -1 : hv[k]);
     if (over) s_over = 1u;
   }
   __syncthreads();
@@ -215,9 +225,90 @@ __global__ __launch_bounds__(kPlanThreads) void halo_plan(const int32_t* __restr
   }
   if (tid < 27)
     hdr->fm[tid] = uint16_t(s_fm[tid][0] | (s_fm[tid][1] << 2) | (s_fm[tid][2] << 4) | (s_fm[tid][3] << 6));
+  if (tid < 64) {
+    // the work estimate: (block, tap) pairs that multiply (a tile gathering
+    // from global memory counts three times)
+    int pairs = 0;
+    if (lane < 27) pairs = __popc(uint32_t(s_fm[lane][0] | (s_fm[lane][1] << 2) | (s_fm[lane][2] << 4) | (s_fm[lane][3] << 6)));
+    for (int o = 32; o > 0; o >>= 1) pairs += __shfl_xor(pairs, o, 64);
+    if (lane == 0) hdr->cost = uint16_t(fits ? pairs : 3 * pairs);
+  }
+}
+
+// The launch order of the tiles: a stable counting sort by decreasing cost in
+// one workgroup. Bucket b holds cost kHaloMaxCost - b. Tiles are placed a pass
+// of kOrderThreads at a time; a tile's rank among the pass's tiles of its
+// bucket is its rank inside its wave (a ballot per distinct bucket of the
+// wave) plus the counts of that bucket in the earlier waves.
+constexpr int kOrderThreads = 1024;
+constexpr int kOrderWaves = kOrderThreads / 64;
+constexpr int kOrderBuckets = 1024;
+static_assert(kHaloMaxCost < kOrderBuckets && kOrderBuckets == kOrderThreads, "cost buckets");
+__global__ __launch_bounds__(kOrderThreads) void halo_order(const unsigned char* __restrict__ plan, int64_t tiles,
+                                                            int32_t* __restrict__ order) {
+  __shared__ uint32_t cnt[kOrderBuckets];
+  __shared__ uint16_t wc[kOrderWaves][kOrderBuckets];
+  __shared__ uint32_t wsum[kOrderWaves];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const unsigned long long lt = (1ull << lane) - 1ull;
+  cnt[tid] = 0u;
+  for (int w = 0; w < kOrderWaves; ++w) wc[w][tid] = 0;
+  __syncthreads();
+  auto bucket_of = [&](int64_t t) {
+    return kHaloMaxCost - int(reinterpret_cast<const HaloHeader*>(plan + t * int64_t(kPlanBytes) + kPlanHdr)->cost);
+  };
+  for (int64_t t = tid; t < tiles; t += kOrderThreads) atomicAdd(&cnt[bucket_of(t)], 1u);
+  __syncthreads();
+  {  // exclusive scan of the bucket counts
+    const uint32_t own = cnt[tid];
+    uint32_t x = own;
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t y = __shfl_up(x, o, 64);
+      if (lane >= o) x += y;
+    }
+    if (lane == 63) wsum[wave] = x;
+    __syncthreads();
+    uint32_t before = 0;
+    for (int w = 0; w < wave; ++w) before += wsum[w];
+    cnt[tid] = before + x - own;
+  }
+  __syncthreads();
+  for (int64_t t0 = 0; t0 < tiles; t0 += kOrderThreads) {
+    const int64_t t = t0 + tid;
+    const int b = t < tiles ? bucket_of(t) : -1;
+    uint32_t rank = 0;
+    unsigned long long todo = __ballot(b >= 0);
+    while (todo) {  // one round per distinct bucket of the wave (wave-uniform)
+      const int leader = __ffsll(todo) - 1;
+      const int bl = __shfl(b, leader, 64);
+      const unsigned long long same = __ballot(b == bl);
+      if (b == bl) rank = uint32_t(__popcll(same & lt));
+      if (lane == leader) wc[wave][bl] = uint16_t(__popcll(same));
+      todo &= ~same;
+    }
+    __syncthreads();
+    if (b >= 0) {
+      for (int w = 0; w < wave; ++w) rank += wc[w][b];
+      order[cnt[b] + rank] = int32_t(t);
+    }
+    __syncthreads();
+    uint32_t add = 0;
+    for (int w = 0; w < kOrderWaves; ++w) {
+      add += wc[w][tid];
+      wc[w][tid] = 0;
+    }
+    cnt[tid] += add;
+    __syncthreads();
+  }
 }
 
 }  // namespace
+
+hipError_t launch_halo_order(const unsigned char* plan, int64_t tiles, int32_t* order, hipStream_t st) {
+  if (tiles <= 0) return hipSuccess;
+  halo_order<<<1, kOrderThreads, 0, st>>>(plan, tiles, order);
+  return hipGetLastError();
+}
 
 hipError_t launch_halo_plan(const int32_t* srows, const uint32_t* mask, const int32_t* nbr, int64_t n,
                             unsigned char* plan, hipStream_t st) {

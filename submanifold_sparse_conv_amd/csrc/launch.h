@@ -63,7 +63,8 @@ constexpr int kGroupWindow = 4096;
 //                (r / 32) % 4: a lane's four 32-row blocks at one tap are adjacent
 constexpr int kHaloTM = 256;
 constexpr int kHaloCap = 736;     // halo slots of one tile, slot 0 included
-constexpr int kHaloHash = 2048;   // dedup table entries (power of two)
+constexpr int kHaloHashBits = 12;
+constexpr int kHaloHash = 1 << kHaloHashBits;  // dedup table entries
 constexpr int kHaloProbes = 64;   // a longer probe run marks the tile as not fitting
 constexpr int kHaloRowBytes = 64; // halo rows in LDS: 32 half-precision channels
 static_assert(kHaloCap * kHaloRowBytes + 48 < 65536, "halo offsets fit in 16 bits");
@@ -75,14 +76,21 @@ struct HaloHeader {
   int32_t nh;         // halo rows (slots 1 .. nh); -1: the halo does not fit, gather from global memory
   uint32_t tmask;     // taps some row of the tile has
   uint16_t fm[27];    // bit b: 32-row block b (rows 32b .. 32b + 31) has tap k
+  uint16_t cost;      // work estimate: (block, tap) pairs that multiply, x 3 when nh < 0
 };
 inline int64_t halo_tiles(int64_t n) { return (n + kHaloTM - 1) / kHaloTM; }
+constexpr int kHaloMaxCost = 3 * 27 * (kHaloTM / 32);
+// The tiles in the gather-GEMM's launch order: decreasing cost (ties in tile
+// order), so that the hardware's in-order dispatch of workgroups to free slots
+// runs the longest tiles first and the shortest fill the end.
+hipError_t launch_halo_order(const unsigned char* plan, int64_t tiles, int32_t* order, hipStream_t st);
 
 // dense: the hash's occupancy bitmap when it was built in a known grid (the
 // block records are read from it instead of the table), else null. plan:
 // halo_tiles(n) records of kPlanBytes.
 hipError_t launch_kmap(const uint64_t* skeys, int64_t n, const TableRef& t, const DenseRef* dense, int32_t* nbr,
-                       uint32_t* mask, int32_t* grows, uint32_t* gmask, unsigned char* plan, hipStream_t st);
+                       uint32_t* mask, int32_t* grows, uint32_t* gmask, unsigned char* plan, int32_t* order,
+                       hipStream_t st);
 hipError_t launch_halo_plan(const int32_t* srows, const uint32_t* mask, const int32_t* nbr, int64_t n,
                             unsigned char* plan, hipStream_t st);
 
@@ -98,6 +106,7 @@ struct ConvArgs {
   const int32_t* srows; // [n]
   const uint32_t* mask; // [n] Morton order
   const unsigned char* plan;  // halo plan records (halo_tiles(n) x kPlanBytes)
+  const int32_t* order;       // halo tiles in launch order
   int64_t n;
   const void* x;
   const void* w;
@@ -115,12 +124,13 @@ __host__ __device__ inline int64_t packed_weight_elems(int c_in, int c_out) {
 hipError_t launch_pack_weights(const void* w, void* wp, int c_in, int c_out, hipStream_t st);
 // Shapes the halo gather-GEMM takes (half-precision features). Their packed
 // weights carry, after the zero block, a second copy in MFMA fragment order:
-// fragment (tap k, 32-channel chunk c, 16-channel step s, 32-column block b)
-// is 64 lanes x 8 halves at ((k * (c_in / 32) + c) * 2 + s) * (c_out / 32) + b,
-// lane l holding column 32 b + l % 32, input channels 32 c + 16 s + 8 (l / 32) ..
-// + 8 -- one contiguous kilobyte per fragment.
+// fragment (32-channel chunk c, tap k, 16-channel step s, 32-column block b)
+// is 64 lanes x 8 halves at ((c * 27 + k) * 2 + s) * (c_out / 32) + b, lane l
+// holding column 32 b + l % 32, input channels 32 c + 16 s + 8 (l / 32) .. + 8
+// -- one contiguous kilobyte per fragment, the stages of the gather-GEMM
+// (chunk-major, taps in order) at a constant stride.
 inline bool halo_shape(int c_in, int c_out) {
-  return c_in % 32 == 0 && c_out % 128 == 0 && c_in <= 256 && c_out <= 256;
+  return c_in % 64 == 0 && c_out % 128 == 0 && c_in <= 256 && c_out <= 256;
 }
 __host__ __device__ inline int64_t frag_weight_offset(int c_in, int c_out) {  // in halves
   return packed_weight_elems(c_in, c_out) + 128;  // after the 256-byte zero block

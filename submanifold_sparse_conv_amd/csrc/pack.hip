@@ -81,7 +81,7 @@ __global__ __launch_bounds__(kThreads) void pack_weights_v8(const uint16_t* __re
 // (fragment layout in launch.h, next to halo_shape).
 __global__ __launch_bounds__(kThreads) void pack_frag(const uint4* __restrict__ wp, uint4* __restrict__ wf, int c_in,
                                                       int c_out, int64_t total) {
-  const int nc = c_in / 32, ncb = c_out / 32;
+  const int ncb = c_out / 32;
   for (int64_t e = int64_t(blockIdx.x) * kThreads + threadIdx.x; e < total; e += int64_t(gridDim.x) * kThreads) {
     const int lane = int(e & 63);
     int64_t f = e >> 6;
@@ -89,8 +89,8 @@ __global__ __launch_bounds__(kThreads) void pack_frag(const uint4* __restrict__ 
     f /= ncb;
     const int s = int(f & 1);
     f >>= 1;
-    const int c = int(f % nc);
-    const int k = int(f / nc);
+    const int k = int(f % 27);
+    const int c = int(f / 27);
     const int col = cb * 32 + (lane & 31);
     const int ci = c * 32 + s * 16 + (lane >> 5) * 8;
     wf[e] = wp[((int64_t(k) * c_out + col) * c_in + ci) / 8];
