@@ -683,11 +683,10 @@ __device__ __forceinline__ void store_tile32(const RowsArgs& p, const f32x16 (&a
 // results are the same bits. Shapes: halo_shape (c_in % 32 == 0, c_out % 128
 // == 0).
 //
-// Work items: blockIdx -> (row tile, column tile); when the last round of
-// workgroups would hold few items (split > 0), each of the last `split` items
-// becomes sixteen workgroups, each multiplying and storing one 32-row block of
-// one wave (the other waves only help with the halo copies), so that the last
-// round is short.
+// Work items: blockIdx -> (row tile, column tile) in the plan's launch order;
+// when the last round of workgroups would hold few items (split > 0), each of
+// the last `split` items becomes kHaloParts workgroups (halo_part), so that
+// the last round is short.
 constexpr int kHaloKC = 32;
 static_assert(kHaloRowBytes == kHaloKC * 2, "halo rows hold one chunk of half-precision channels");
 
@@ -695,7 +694,128 @@ struct HaloLaunch {
   int full;   // work items run whole
   int split;  // items after them, each run as kHaloParts parts
 };
-constexpr int kHaloParts = 16;  // one part per (wave, 32-row block)
+constexpr int kHaloParts = kHaloTM / 32;  // one part per 32-row block
+// halo_part's LDS, in floats: partial sums of waves 1-3 | output staging | neighbour table
+constexpr int kPartNbrAt = 3 * 4 * 16 * 64 + 16 * (32 * 4 + 8);
+
+// One 32-row block of an item (rows 32 blk .. + 31 of the tile, columns
+// n0 .. n0 + 127), for the last, short round: the four waves split the input
+// channels (wave w takes the 32-channel chunks w, w + 4, ...), gather their A
+// fragments straight from global memory with the loads three taps ahead, and
+// their partial sums meet in LDS, added in chunk order, before wave 0's
+// epilogue. A part's chain of dependent steps is a quarter of a whole item's
+// (or less), so the round ends soon after it starts. The sums of a split item
+// are added in another order than a whole item's: results equal to rounding,
+// and the same bits run to run (the split depends only on the sizes and the
+// device).
+template <class H>
+__device__ __forceinline__ void halo_part(const RowsArgs& p, const unsigned char* rec, int blk, int n0, float* s_red) {
+  typedef typename H::vec hvec;
+  constexpr int CB = 4, D = 3;  // 27 taps = 9 x D: a tap's load set is k % D in every chunk
+  const int c_in = p.c_in, c_out = p.c_out;
+  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hw = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const HaloHeader* const hdr = reinterpret_cast<const HaloHeader*>(rec + kPlanHdr);
+  const int r = 32 * blk + l32;
+  const int32_t crow = reinterpret_cast<const int32_t*>(rec + kPlanCrow)[r];
+  uint32_t tm = 0;  // taps the block has
+#pragma unroll
+  for (int k = 0; k < 27; ++k) tm |= uint32_t((hdr->fm[k] >> blk) & 1u) << k;
+  const int nchunks = c_in / kHaloKC;
+  // caller rows of the block's rows' neighbours (-1: absent), [tap][row], in
+  // LDS past the partial sums and the output staging
+  int32_t* const s_nb = reinterpret_cast<int32_t*>(s_red) + kPartNbrAt;
+  for (int e = tid; e < 27 * 32; e += kThreads) {
+    const int k = e >> 5, rr = 32 * blk + (e & 31);
+    const int32_t cr = reinterpret_cast<const int32_t*>(rec + kPlanCrow)[rr];
+    const uint32_t m = cr >= 0 ? reinterpret_cast<const uint32_t*>(rec + kPlanMask)[rr] : 0u;
+    s_nb[e] = ((m >> k) & 1u) ? p.nbr[int64_t(cr) * 27 + k] : -1;
+  }
+  __syncthreads();
+
+  const int ncb = c_out / 32, cb0 = n0 / 32;
+  const uint4* const wf = reinterpret_cast<const uint4*>(p.wp + frag_weight_offset(c_in, c_out)) + cb0 * 64 + lane;
+  const uint16_t* const xs = static_cast<const uint16_t*>(p.x);
+  f32x16 acc[CB];
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[cb][e] = 0.f;
+  uint4 bq[D][2][CB], aq[D][2];
+  // the loads of tap k of chunk c (a chunk past the wave's last reads chunk
+  // `wave` again; nothing multiplies it)
+  auto issue = [&](int c, int k, uint4 (&b)[2][CB], uint4 (&a)[2]) {
+    const int cc = c < nchunks ? c : wave;
+    const uint4* f = wf + int64_t((cc * 27 + k) * 2) * ncb * 64;
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) b[s][cb] = f[(s * ncb + cb) * 64];
+    const int32_t j = s_nb[k * 32 + l32];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const void* g = j >= 0 ? static_cast<const void*>(xs + int64_t(j) * c_in + cc * kHaloKC + (2 * s + hw) * 8)
+                             : static_cast<const void*>(p.zeros);
+      a[s] = *reinterpret_cast<const uint4*>(g);
+    }
+  };
+  if (wave < nchunks) {
+#pragma unroll
+    for (int k = 0; k < D; ++k) issue(wave, k, bq[k], aq[k]);
+    auto step = [&](int c, int k, uint4 (&b)[2][CB], uint4 (&a)[2]) {
+      if ((tm >> k) & 1u) {
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+          for (int cb = 0; cb < CB; ++cb)
+            acc[cb] = H::mma32(*reinterpret_cast<const hvec*>(&a[s]), *reinterpret_cast<const hvec*>(&b[s][cb]),
+                               acc[cb]);
+      }
+      if (k + D < 27)
+        issue(c, k + D, b, a);
+      else
+        issue(c + 4, k + D - 27, b, a);
+    };
+    for (int c = wave; c < nchunks; c += 4) {
+#pragma unroll 1
+      for (int k = 0; k < 27; k += D) {
+        step(c, k, bq[0], aq[0]);
+        step(c, k + 1, bq[1], aq[1]);
+        step(c, k + 2, bq[2], aq[2]);
+      }
+    }
+  }
+  // partial sums of waves 1.. into LDS (their accumulator layout), wave 0
+  // adds them in chunk order and stores
+  __builtin_amdgcn_s_waitcnt(0);
+  if (wave > 0 && wave < nchunks) {
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+      for (int e = 0; e < 16; e += 4)
+        *reinterpret_cast<float4*>(s_red + (((wave - 1) * CB + cb) * 16 + e) * 64 + lane * 4) =
+            make_float4(acc[cb][e], acc[cb][e + 1], acc[cb][e + 2], acc[cb][e + 3]);
+  }
+  __syncthreads();
+  if (wave == 0) {
+    for (int w = 1; w < (nchunks < 4 ? nchunks : 4); ++w)
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+        for (int e = 0; e < 16; e += 4) {
+          const float4 v = *reinterpret_cast<const float4*>(s_red + (((w - 1) * CB + cb) * 16 + e) * 64 + lane * 4);
+          acc[cb][e] += v.x;
+          acc[cb][e + 1] += v.y;
+          acc[cb][e + 2] += v.z;
+          acc[cb][e + 3] += v.w;
+        }
+    f32x16 out[1][CB];
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) out[0][cb] = acc[cb];
+    const int32_t cr[1] = {lane < 32 ? crow : -1};
+    store_tile32<H, 1, CB>(p, out, cr, n0, s_red + 3 * CB * 16 * 64);
+  }
+}
 
 template <bool F16>
 __global__ __launch_bounds__(kThreads, 2) void fwd_halo(const RowsArgs p, const HaloLaunch hl) {
@@ -706,9 +826,12 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_halo(const RowsArgs p, const 
   constexpr int HBYTES = kHaloCap * ROWB;
   constexpr int SLOTQ = (kPlanSlotBytes + 1023) / 1024, ROWQ = (kHaloCap * 4 + 1023) / 1024;
   static_assert(HBYTES >= 4 * 16 * (32 * CB + 8) * 4, "the output staging lives in the halo area");
-  __shared__ __attribute__((aligned(1024))) unsigned char s_halo[HBYTES];
-  __shared__ __attribute__((aligned(1024))) unsigned char s_slotb[SLOTQ * 1024];  // uint16 [tap][sidx]
-  __shared__ __attribute__((aligned(1024))) unsigned char s_rowb[ROWQ * 1024];    // int32 [slot]
+  // LDS: halo | slot table | halo rows' caller rows (a part uses it whole)
+  __shared__ __attribute__((aligned(1024))) unsigned char s_lds[HBYTES + (SLOTQ + ROWQ) * 1024];
+  static_assert((kPartNbrAt + 27 * 32) * 4 <= HBYTES + (SLOTQ + ROWQ) * 1024, "halo_part's LDS");
+  unsigned char* const s_halo = s_lds;
+  unsigned char* const s_slotb = s_lds + HBYTES;                  // uint16 [tap][sidx]
+  unsigned char* const s_rowb = s_lds + HBYTES + SLOTQ * 1024;    // int32 [slot]
 
   const int c_in = p.c_in, c_out = p.c_out;
   // Workgroups take the tiles in the plan's order (longest first): the
@@ -721,22 +844,23 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_halo(const RowsArgs p, const 
     part = (bid - hl.full) % kHaloParts;
   }
   const int rt = p.order[item / p.n_tiles_n];
+  const unsigned char* const rec = p.plan + int64_t(rt) * kPlanBytes;
+  if (part >= 0) {
+    halo_part<H>(p, rec, part, (item % p.n_tiles_n) * TN, reinterpret_cast<float*>(s_lds));
+    return;
+  }
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hw = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int rh = wave >> 1, chf = wave & 1;
   const int n0 = (item % p.n_tiles_n) * TN + 64 * chf;  // this wave's first column
-  const bool mine = part < 0 || part / 4 == wave;      // this wave multiplies and stores
-  // a part: one 32-row block of one wave (its other blocks neither multiply nor store)
-  const uint32_t pblk = part < 0 ? 15u : 1u << (part & 3);
-  const unsigned char* const rec = p.plan + int64_t(rt) * kPlanBytes;
   const HaloHeader* const hdr = reinterpret_cast<const HaloHeader*>(rec + kPlanHdr);
   const int nh = hdr->nh;
   // This wave's block masks (its four 32-row blocks), 4 bits per tap.
   uint64_t bml = 0, bmh = 0;
-  if (mine) {
+  {
 #pragma unroll
     for (int k = 0; k < 27; ++k) {
-      const uint64_t f = (hdr->fm[k] >> (4 * rh)) & pblk;
+      const uint64_t f = (hdr->fm[k] >> (4 * rh)) & 15u;
       if (k < 16) bml |= f << (4 * k);
       else bmh |= f << (4 * (k - 16));
     }
@@ -747,9 +871,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_halo(const RowsArgs p, const 
   int32_t crow[2];
 #pragma unroll
   for (int q = 0; q < 2; ++q)
-    crow[q] = mine && ((pblk >> (2 * q + hw)) & 1u)
-                  ? reinterpret_cast<const int32_t*>(rec + kPlanCrow)[128 * rh + 64 * q + lane]
-                  : -1;
+    crow[q] = reinterpret_cast<const int32_t*>(rec + kPlanCrow)[128 * rh + 64 * q + lane];
   f32x16 acc[RB][CB];
 #pragma unroll
   for (int b = 0; b < RB; ++b)
@@ -930,8 +1052,8 @@ hipError_t launch_halo(const ConvArgs& a, const uint16_t* wp, const uint16_t* ze
   const int nt = (a.c_out + TN - 1) / TN;
   const int64_t items = mt * nt;
   if (items * kHaloParts > 0x7FFFFFFF) return hipErrorInvalidValue;
-  // Split the last round into parts when it would hold at most a sixteenth
-  // of the device's workgroup slots.
+  // Split the last round into parts when its parts fit the device's
+  // workgroup slots at once.
   HaloLaunch hl{int(items), 0};
   const int64_t slots = halo_slots();
   if (slots > 0 && items > slots) {
