@@ -316,11 +316,11 @@ void tr_sparseconv_hash_destroy(tr_sc_hash* h) {
 
 // Kernel-map workspace: mask[n] (Morton order) | grows[n] | gmask[n] (tile
 // order) | halo plan (one record per tile of kHaloTM voxels) | the tiles'
-// launch order.
+// launch order | their costs.
 size_t tr_sparseconv_kmap_workspace_bytes(int64_t n) {
   if (n < 0 || n > kMaxN) return 0;
   return 3 * align_up(size_t(n) * 4, 256) + size_t(halo_tiles(n)) * kPlanBytes +
-         align_up(size_t(halo_tiles(n)) * 4, 256) + 256;
+         align_up(size_t(halo_tiles(n)) * 4, 256) + align_up(size_t(halo_tiles(n)) * 2, 256) + 256;
 }
 
 int tr_sparseconv_build_kernel_map(const tr_sc_hash* h, int32_t* nbr, void* workspace, size_t ws_bytes,
@@ -341,8 +341,10 @@ int tr_sparseconv_build_kernel_map(const tr_sc_hash* h, int32_t* nbr, void* work
   uint32_t* gmask = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + 2 * part);
   unsigned char* plan = static_cast<unsigned char*>(workspace) + 3 * part;
   int32_t* order = reinterpret_cast<int32_t*>(plan + size_t(halo_tiles(h->n)) * kPlanBytes);
+  uint16_t* costs = reinterpret_cast<uint16_t*>(reinterpret_cast<unsigned char*>(order) +
+                                                align_up(size_t(halo_tiles(h->n)) * 4, 256));
   hipError_t e = launch_kmap(h->skeys, h->n, h->table, h->has_dense ? &h->dense : nullptr, nbr, mask, grows, gmask,
-                             plan, order, static_cast<hipStream_t>(stream));
+                             plan, costs, order, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "build_kernel_map");
   tr_sc_kmap* m = new tr_sc_kmap;
   m->magic = kKmapMagic;

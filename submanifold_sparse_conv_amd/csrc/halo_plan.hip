@@ -38,11 +38,21 @@ __device__ inline int slot_index(int r) { return (r >> 7) * 128 + (r & 31) * 4 +
 __global__ __launch_bounds__(kPlanThreads) void halo_plan(const int32_t* __restrict__ srows,
                                                           const uint32_t* __restrict__ mask,
                                                           const int32_t* __restrict__ nbr, int64_t n,
-                                                          unsigned char* __restrict__ plan) {
-  __shared__ int32_t tab[kHaloHash];
+                                                          unsigned char* __restrict__ plan,
+                                                          uint16_t* __restrict__ costs) {
+  // LDS: the dedup table and the slot table, which first hold the items'
+  // neighbour lists ([item][tap], loaded row by row so that a wave's loads
+  // cover a few cache lines each)
+  constexpr int kTabBytes = kHaloHash * 4, kSlotBytes = 27 * kHaloTM * 2;
+  static_assert(kTabBytes + kSlotBytes >= kHaloTM * 27 * 4, "neighbour lists fit the tables' space");
+  __shared__ __attribute__((aligned(16))) unsigned char s_big[kTabBytes + kSlotBytes];
+  int32_t* const tab = reinterpret_cast<int32_t*>(s_big);
+  int16_t* const s_slot = reinterpret_cast<int16_t*>(s_big + kTabBytes);
+  int32_t* const s_nl = reinterpret_cast<int32_t*>(s_big);
   __shared__ uint32_t cnt[4][256];  // items per (wave, octant pattern), then first positions
-  __shared__ __attribute__((aligned(16))) int16_t s_slot[27 * kHaloTM];
   __shared__ uint32_t s_pmask[kHaloTM];
+  __shared__ uint32_t s_im[kHaloTM];
+  __shared__ int32_t s_icr[kHaloTM];
   __shared__ uint8_t s_fm[27][4];
   __shared__ uint32_t s_wsum[4], s_tmask, s_over;
 
@@ -55,9 +65,24 @@ __global__ __launch_bounds__(kPlanThreads) void halo_plan(const int32_t* __restr
   const int32_t cr = valid ? srows[pos] : -1;
 
   for (int q = tid; q < 4 * 256; q += kPlanThreads) (&cnt[0][0])[q] = 0u;
-  for (int e = tid; e < kHaloHash; e += kPlanThreads) tab[e] = -1;
+  s_im[tid] = m;
+  s_icr[tid] = cr;
   if (tid == 0) s_tmask = 0u, s_over = 0u;
   __syncthreads();
+  // the neighbour lists, [item][tap] (-1: absent): element e = tid + 256 q,
+  // all 27 loads of a thread in flight together
+  {
+    int32_t v[27];
+#pragma unroll
+    for (int q = 0; q < 27; ++q) {
+      const int e = tid + kPlanThreads * q, i = e / 27, k = e - 27 * i;
+      const uint32_t mi = s_im[i];
+      const int32_t ci = s_icr[i];
+      v[q] = ((mi >> k) & 1u) ? nbr[int64_t(ci) * 27 + k] : -1;
+    }
+#pragma unroll
+    for (int q = 0; q < 27; ++q) s_nl[tid + kPlanThreads * q] = v[q];
+  }
 
   // (1) Tile position r: stable counting sort of the valid items by octant
   // pattern (rank among equal patterns of the wave by ballots, then a scan over
@@ -113,7 +138,10 @@ __global__ __launch_bounds__(kPlanThreads) void halo_plan(const int32_t* __restr
     int32_t jv[27];
     int hv[27];
 #pragma unroll
-    for (int k = 0; k < 27; ++k) jv[k] = ((m >> k) & 1u) ? nbr[int64_t(cr) * 27 + k] : -1;
+    for (int k = 0; k < 27; ++k) jv[k] = s_nl[tid * 27 + k];
+    __syncthreads();  // the lists are in registers: the table takes their space
+    for (int e = tid; e < kHaloHash; e += kPlanThreads) tab[e] = -1;
+    __syncthreads();
 #pragma unroll
     for (int k = 0; k < 27; ++k) hv[k] = jv[k] >= 0 ? int((uint32_t(jv[k]) * 2654435761u) >> (32 - kHaloHashBits)) : -1;
     uint32_t left = 0;  // taps still to place
@@ -231,33 +259,27 @@ __global__ __launch_bounds__(kPlanThreads) void halo_plan(const int32_t* __restr
     int pairs = 0;
     if (lane < 27) pairs = __popc(uint32_t(s_fm[lane][0] | (s_fm[lane][1] << 2) | (s_fm[lane][2] << 4) | (s_fm[lane][3] << 6)));
     for (int o = 32; o > 0; o >>= 1) pairs += __shfl_xor(pairs, o, 64);
-    if (lane == 0) hdr->cost = uint16_t(fits ? pairs : 3 * pairs);
+    if (lane == 0) costs[tile] = uint16_t(fits ? pairs : 3 * pairs);
   }
 }
 
-// The launch order of the tiles: a stable counting sort by decreasing cost in
-// one workgroup. Bucket b holds cost kHaloMaxCost - b. Tiles are placed a pass
-// of kOrderThreads at a time; a tile's rank among the pass's tiles of its
-// bucket is its rank inside its wave (a ballot per distinct bucket of the
-// wave) plus the counts of that bucket in the earlier waves.
+// The launch order of the tiles: a counting sort by decreasing cost in one
+// workgroup (bucket b holds cost kHaloMaxCost - b). Tiles of equal cost are
+// placed by atomics, in no fixed order: the order only schedules the
+// gather-GEMM's workgroups, each of which computes its own rows the same way
+// wherever it runs.
 constexpr int kOrderThreads = 1024;
 constexpr int kOrderWaves = kOrderThreads / 64;
 constexpr int kOrderBuckets = 1024;
 static_assert(kHaloMaxCost < kOrderBuckets && kOrderBuckets == kOrderThreads, "cost buckets");
-__global__ __launch_bounds__(kOrderThreads) void halo_order(const unsigned char* __restrict__ plan, int64_t tiles,
+__global__ __launch_bounds__(kOrderThreads) void halo_order(const uint16_t* __restrict__ costs, int64_t tiles,
                                                             int32_t* __restrict__ order) {
   __shared__ uint32_t cnt[kOrderBuckets];
-  __shared__ uint16_t wc[kOrderWaves][kOrderBuckets];
   __shared__ uint32_t wsum[kOrderWaves];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const unsigned long long lt = (1ull << lane) - 1ull;
   cnt[tid] = 0u;
-  for (int w = 0; w < kOrderWaves; ++w) wc[w][tid] = 0;
   __syncthreads();
-  auto bucket_of = [&](int64_t t) {
-    return kHaloMaxCost - int(reinterpret_cast<const HaloHeader*>(plan + t * int64_t(kPlanBytes) + kPlanHdr)->cost);
-  };
-  for (int64_t t = tid; t < tiles; t += kOrderThreads) atomicAdd(&cnt[bucket_of(t)], 1u);
+  for (int64_t t = tid; t < tiles; t += kOrderThreads) atomicAdd(&cnt[kHaloMaxCost - int(costs[t])], 1u);
   __syncthreads();
   {  // exclusive scan of the bucket counts
     const uint32_t own = cnt[tid];
@@ -273,49 +295,24 @@ __global__ __launch_bounds__(kOrderThreads) void halo_order(const unsigned char*
     cnt[tid] = before + x - own;
   }
   __syncthreads();
-  for (int64_t t0 = 0; t0 < tiles; t0 += kOrderThreads) {
-    const int64_t t = t0 + tid;
-    const int b = t < tiles ? bucket_of(t) : -1;
-    uint32_t rank = 0;
-    unsigned long long todo = __ballot(b >= 0);
-    while (todo) {  // one round per distinct bucket of the wave (wave-uniform)
-      const int leader = __ffsll(todo) - 1;
-      const int bl = __shfl(b, leader, 64);
-      const unsigned long long same = __ballot(b == bl);
-      if (b == bl) rank = uint32_t(__popcll(same & lt));
-      if (lane == leader) wc[wave][bl] = uint16_t(__popcll(same));
-      todo &= ~same;
-    }
-    __syncthreads();
-    if (b >= 0) {
-      for (int w = 0; w < wave; ++w) rank += wc[w][b];
-      order[cnt[b] + rank] = int32_t(t);
-    }
-    __syncthreads();
-    uint32_t add = 0;
-    for (int w = 0; w < kOrderWaves; ++w) {
-      add += wc[w][tid];
-      wc[w][tid] = 0;
-    }
-    cnt[tid] += add;
-    __syncthreads();
-  }
+  for (int64_t t = tid; t < tiles; t += kOrderThreads)
+    order[atomicAdd(&cnt[kHaloMaxCost - int(costs[t])], 1u)] = int32_t(t);
 }
 
 }  // namespace
 
-hipError_t launch_halo_order(const unsigned char* plan, int64_t tiles, int32_t* order, hipStream_t st) {
+hipError_t launch_halo_order(const uint16_t* costs, int64_t tiles, int32_t* order, hipStream_t st) {
   if (tiles <= 0) return hipSuccess;
-  halo_order<<<1, kOrderThreads, 0, st>>>(plan, tiles, order);
+  halo_order<<<1, kOrderThreads, 0, st>>>(costs, tiles, order);
   return hipGetLastError();
 }
 
 hipError_t launch_halo_plan(const int32_t* srows, const uint32_t* mask, const int32_t* nbr, int64_t n,
-                            unsigned char* plan, hipStream_t st) {
+                            unsigned char* plan, uint16_t* costs, hipStream_t st) {
   const int64_t tiles = halo_tiles(n);
   if (tiles <= 0) return hipSuccess;
   if (tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
-  halo_plan<<<unsigned(tiles), kPlanThreads, 0, st>>>(srows, mask, nbr, n, plan);
+  halo_plan<<<unsigned(tiles), kPlanThreads, 0, st>>>(srows, mask, nbr, n, plan, costs);
   return hipGetLastError();
 }
 

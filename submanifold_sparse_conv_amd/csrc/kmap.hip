@@ -321,8 +321,8 @@ __global__ __launch_bounds__(kGroupThreads) void group_rows(const int32_t* __res
 }  // namespace
 
 hipError_t launch_kmap(const uint64_t* skeys, int64_t n, const TableRef& t, const DenseRef* dense, int32_t* nbr,
-                       uint32_t* mask, int32_t* grows, uint32_t* gmask, unsigned char* plan, int32_t* order,
-                       hipStream_t st) {
+                       uint32_t* mask, int32_t* grows, uint32_t* gmask, unsigned char* plan, uint16_t* costs,
+                       int32_t* order, hipStream_t st) {
   if (n > 0) {
     const unsigned grid = unsigned((n + kThreads - 1) / kThreads);
     if (dense != nullptr)
@@ -333,9 +333,9 @@ hipError_t launch_kmap(const uint64_t* skeys, int64_t n, const TableRef& t, cons
                                                                                          grows, gmask);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const hipError_t e2 = launch_halo_plan(t.srows, mask, nbr, n, plan, st);
+    const hipError_t e2 = launch_halo_plan(t.srows, mask, nbr, n, plan, costs, st);
     if (e2 != hipSuccess) return e2;
-    return launch_halo_order(plan, halo_tiles(n), order, st);
+    return launch_halo_order(costs, halo_tiles(n), order, st);
   }
   return hipGetLastError();
 }

@@ -76,23 +76,24 @@ struct HaloHeader {
   int32_t nh;         // halo rows (slots 1 .. nh); -1: the halo does not fit, gather from global memory
   uint32_t tmask;     // taps some row of the tile has
   uint16_t fm[27];    // bit b: 32-row block b (rows 32b .. 32b + 31) has tap k
-  uint16_t cost;      // work estimate: (block, tap) pairs that multiply, x 3 when nh < 0
 };
 inline int64_t halo_tiles(int64_t n) { return (n + kHaloTM - 1) / kHaloTM; }
+// A tile's work estimate (written by the plan, one uint16 per tile): the
+// (32-row block, tap) pairs that multiply, three times that when nh < 0.
 constexpr int kHaloMaxCost = 3 * 27 * (kHaloTM / 32);
 // The tiles in the gather-GEMM's launch order: decreasing cost (ties in tile
 // order), so that the hardware's in-order dispatch of workgroups to free slots
 // runs the longest tiles first and the shortest fill the end.
-hipError_t launch_halo_order(const unsigned char* plan, int64_t tiles, int32_t* order, hipStream_t st);
+hipError_t launch_halo_order(const uint16_t* costs, int64_t tiles, int32_t* order, hipStream_t st);
 
 // dense: the hash's occupancy bitmap when it was built in a known grid (the
 // block records are read from it instead of the table), else null. plan:
 // halo_tiles(n) records of kPlanBytes.
 hipError_t launch_kmap(const uint64_t* skeys, int64_t n, const TableRef& t, const DenseRef* dense, int32_t* nbr,
-                       uint32_t* mask, int32_t* grows, uint32_t* gmask, unsigned char* plan, int32_t* order,
-                       hipStream_t st);
+                       uint32_t* mask, int32_t* grows, uint32_t* gmask, unsigned char* plan, uint16_t* costs,
+                       int32_t* order, hipStream_t st);
 hipError_t launch_halo_plan(const int32_t* srows, const uint32_t* mask, const int32_t* nbr, int64_t n,
-                            unsigned char* plan, hipStream_t st);
+                            unsigned char* plan, uint16_t* costs, hipStream_t st);
 
 // Forward kernels. `srows` is the row order of the tiles (position -> caller
 // row), `mask` the 27-bit neighbour mask of the voxel at each position.
