@@ -921,17 +921,28 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_halo(const RowsArgs p, const 
     bare_barrier();
     const int32_t* const s_rows = reinterpret_cast<const int32_t*>(s_rowb);
     // Halo rows of chunk c: slot q*16 + lane/4, piece lane&3 (slot 0 and the
-    // slots past the halo read the zero block).
+    // slots past the halo read the zero block). The caller rows are read from
+    // LDS first, all together, then the copies are issued.
+    constexpr int QW = ((kHaloCap + 15) / 16 + 3) / 4;  // copy rounds per wave
     auto fill_halo = [&](int c) {
       const int nq = (nh + 1 + 15) >> 4;
-      for (int q = wave; q < nq; q += 4) {
-        const int slot = q * 16 + (lane >> 2);
-        const int ch = c * KC + (((lane & 3) ^ ((slot >> 2) & 3)) << 3);
-        const bool ok = slot >= 1 && slot <= nh;
-        const void* g = ok ? static_cast<const void*>(static_cast<const uint16_t*>(p.x) +
-                                                      int64_t(s_rows[slot]) * c_in + ch)
-                           : static_cast<const void*>(p.zeros);
-        copy16_to_lds(g, s_halo + q * 1024);
+      int32_t rr[QW];
+#pragma unroll
+      for (int i = 0; i < QW; ++i) {
+        const int slot = (wave + 4 * i) * 16 + (lane >> 2);
+        rr[i] = slot >= 1 && slot <= nh ? s_rows[slot] : -1;
+      }
+#pragma unroll
+      for (int i = 0; i < QW; ++i) {
+        const int q = wave + 4 * i;
+        if (q < nq) {
+          const int slot = q * 16 + (lane >> 2);
+          const int ch = c * KC + (((lane & 3) ^ ((slot >> 2) & 3)) << 3);
+          const void* g = rr[i] >= 0 ? static_cast<const void*>(static_cast<const uint16_t*>(p.x) +
+                                                                 int64_t(rr[i]) * c_in + ch)
+                                     : static_cast<const void*>(p.zeros);
+          copy16_to_lds(g, s_halo + q * 1024);
+        }
       }
     };
     // LDS offsets of this lane's four rows (128 rh + 32 blk + lane % 32) at tap k
@@ -949,7 +960,10 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_halo(const RowsArgs p, const 
     // Registers: A and B fragments in two sets used by alternate stages. A
     // stage multiplies on its set while the next stage's A fragments (read one
     // stage ahead, within a chunk) and the B fragments of the stage after next
-    // land in the other set; `so` holds the slots of the next stage's tap.
+    // land in the other set. The slot offsets of a tap are read three stages
+    // ahead into one of two registers (by stage parity), so the next stage's A
+    // reads wait only for an offset read issued before the previous stage's
+    // A reads, not for those reads themselves (LDS reads return in order).
     uint4 b0[2][CB], b1[2][CB];
     hvec a0[2][RB], a1[2][RB];
     load_b(0, b0);
@@ -958,16 +972,16 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_halo(const RowsArgs p, const 
     __builtin_amdgcn_s_waitcnt(0);
     bare_barrier();  // chunk 0's halo has landed
     load_a(read_slots(0), a0);
-    uint2 so = read_slots(1);
+    uint2 sa = read_slots(1), sb = read_slots(2);  // slots of stages 1 and 2
     // Stage st = 27 c + k. Two stages per iteration (nst is even), so that
     // each stage's register sets are fixed; the stage's loads are issued
     // unconditionally (clamped past the end, read again after a halo refill)
     // so that the waits the compiler places before the multiplies stay exact.
     int c = 0, k = 0;
-    auto stage = [&](int st, uint4 (&bc)[2][CB], hvec (&ac)[2][RB], hvec (&an)[2][RB]) {
+    auto stage = [&](int st, uint4 (&bc)[2][CB], hvec (&ac)[2][RB], hvec (&an)[2][RB], uint2& so) {
       const uint32_t bm = uint32_t((k < 16 ? bml >> (4 * k) : bmh >> (4 * (k - 16))) & 15u);
       load_a(so, an);                               // the next stage (same chunk unless k == 26)
-      so = read_slots(k < 25 ? k + 2 : k - 25);     // the stage after next
+      so = read_slots(k < 24 ? k + 3 : k - 24);     // three stages ahead
       mma_stage(bm, ac, bc);
       load_b(st + 2 < nst ? st + 2 : st, bc);       // the stage after next
       if (k == 26) {
@@ -988,8 +1002,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_halo(const RowsArgs p, const 
       }
     };
     for (int st = 0; st < nst; st += 2) {
-      stage(st, b0, a0, a1);
-      stage(st + 1, b1, a1, a0);
+      stage(st, b0, a0, a1, sa);
+      stage(st + 1, b1, a1, a0, sb);
     }
   } else {
     // Too many distinct neighbours: A fragments straight from global memory.
