@@ -680,8 +680,9 @@ __device__ __forceinline__ void store_tile32(const RowsArgs& p, const f32x16 (&a
 // different bank groups whenever their numbers differ mod 16. A tile whose halo
 // does not fit (nh < 0: sparse sets, up to 27 distinct neighbours per voxel)
 // gathers its A fragments from global memory in the same order, so its
-// results are the same bits. Shapes: halo_shape (c_in % 32 == 0, c_out % 128
-// == 0).
+// results are the same bits. Shapes: halo_shape (c_in a multiple of 64 up to
+// 256; c_out 64, 128 or 256). For c_out 64 the item is 256 x 64 and the four
+// waves take 64 rows x 64 columns each (template WR = 4).
 //
 // Work items: blockIdx -> (row tile, column tile) in the plan's launch order;
 // when the last round of workgroups would hold few items (split > 0), each of
@@ -699,7 +700,7 @@ constexpr int kHaloParts = kHaloTM / 32;  // one part per 32-row block
 constexpr int kPartNbrAt = 3 * 4 * 16 * 64 + 16 * (32 * 4 + 8);
 
 // One 32-row block of an item (rows 32 blk .. + 31 of the tile, columns
-// n0 .. n0 + 127), for the last, short round: the four waves split the input
+// n0 .. n0 + 32 CB - 1), for the last, short round: the four waves split the input
 // channels (wave w takes the 32-channel chunks w, w + 4, ...), gather their A
 // fragments straight from global memory with the loads three taps ahead, and
 // their partial sums meet in LDS, added in chunk order, before wave 0's
@@ -708,10 +709,11 @@ constexpr int kPartNbrAt = 3 * 4 * 16 * 64 + 16 * (32 * 4 + 8);
 // are added in another order than a whole item's: results equal to rounding,
 // and the same bits run to run (the split depends only on the sizes and the
 // device).
-template <class H>
+template <class H, int CB>
 __device__ __forceinline__ void halo_part(const RowsArgs& p, const unsigned char* rec, int blk, int n0, float* s_red) {
   typedef typename H::vec hvec;
-  constexpr int CB = 4, D = 3;  // 27 taps = 9 x D: a tap's load set is k % D in every chunk
+  static_assert(CB == 2 || CB == 4, "64 or 128 columns");
+  constexpr int D = 3;  // 27 taps = 9 x D: a tap's load set is k % D in every chunk
   const int c_in = p.c_in, c_out = p.c_out;
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hw = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -817,11 +819,15 @@ __device__ __forceinline__ void halo_part(const RowsArgs& p, const unsigned char
   }
 }
 
-template <bool F16>
+template <bool F16, int WR>
 __global__ __launch_bounds__(kThreads, 2) void fwd_halo(const RowsArgs p, const HaloLaunch hl) {
   typedef Half<F16> H;
   typedef typename H::vec hvec;
-  constexpr int TM = kHaloTM, TN = 128, RB = 4, CB = 2;
+  // WR row groups of waves: 2 (2 x 2 waves, 128 rows x 64 columns each, a
+  // 128-column item) or 4 (4 x 1 waves, 64 rows x 64 columns, a 64-column item)
+  static_assert(WR == 2 || WR == 4, "wave arrangements");
+  constexpr int TM = kHaloTM, RB = 8 / WR, CB = 2, TN = 32 * CB * (4 / WR);
+  constexpr int WROWS = TM / WR;  // rows per wave
   constexpr int KC = kHaloKC, ROWB = kHaloRowBytes;
   constexpr int HBYTES = kHaloCap * ROWB;
   constexpr int SLOTQ = (kPlanSlotBytes + 1023) / 1024, ROWQ = (kHaloCap * 4 + 1023) / 1024;
@@ -846,21 +852,22 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_halo(const RowsArgs p, const 
   const int rt = p.order[item / p.n_tiles_n];
   const unsigned char* const rec = p.plan + int64_t(rt) * kPlanBytes;
   if (part >= 0) {
-    halo_part<H>(p, rec, part, (item % p.n_tiles_n) * TN, reinterpret_cast<float*>(s_lds));
+    halo_part<H, TN / 32>(p, rec, part, (item % p.n_tiles_n) * TN, reinterpret_cast<float*>(s_lds));
     return;
   }
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hw = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int rh = wave >> 1, chf = wave & 1;
-  const int n0 = (item % p.n_tiles_n) * TN + 64 * chf;  // this wave's first column
+  const int rh = wave / (4 / WR), chf = wave % (4 / WR);
+  const int r0 = WROWS * rh;                                // this wave's first row
+  const int n0 = (item % p.n_tiles_n) * TN + 32 * CB * chf;  // this wave's first column
   const HaloHeader* const hdr = reinterpret_cast<const HaloHeader*>(rec + kPlanHdr);
   const int nh = hdr->nh;
-  // This wave's block masks (its four 32-row blocks), 4 bits per tap.
+  // This wave's block masks (its RB 32-row blocks), 4 bits per tap.
   uint64_t bml = 0, bmh = 0;
   {
 #pragma unroll
     for (int k = 0; k < 27; ++k) {
-      const uint64_t f = (hdr->fm[k] >> (4 * rh)) & 15u;
+      const uint64_t f = (hdr->fm[k] >> (RB * rh)) & ((1u << RB) - 1u);
       if (k < 16) bml |= f << (4 * k);
       else bmh |= f << (4 * (k - 16));
     }
@@ -868,10 +875,10 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_halo(const RowsArgs p, const 
   const int nchunks = c_in / KC;  // even (halo_shape)
 
   // crow[q]: caller row of this wave's row 64 q + lane (-1: not stored).
-  int32_t crow[2];
+  int32_t crow[(RB + 1) / 2];
 #pragma unroll
-  for (int q = 0; q < 2; ++q)
-    crow[q] = reinterpret_cast<const int32_t*>(rec + kPlanCrow)[128 * rh + 64 * q + lane];
+  for (int q = 0; q < (RB + 1) / 2; ++q)
+    crow[q] = reinterpret_cast<const int32_t*>(rec + kPlanCrow)[r0 + 64 * q + lane];
   f32x16 acc[RB][CB];
 #pragma unroll
   for (int b = 0; b < RB; ++b)
@@ -945,12 +952,18 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_halo(const RowsArgs p, const 
         }
       }
     };
-    // LDS offsets of this lane's four rows (128 rh + 32 blk + lane % 32) at tap k
-    const unsigned char* const slot_lane = s_slotb + (128 * rh + l32 * 4) * 2;
-    auto read_slots = [&](int k) { return *reinterpret_cast<const uint2*>(slot_lane + k * TM * 2); };
+    // LDS offsets of this lane's RB rows (r0 + 32 blk + lane % 32) at tap k
+    const unsigned char* const slot_lane = s_slotb + (128 * (r0 >> 7) + l32 * 4 + ((r0 >> 5) & 3)) * 2;
+    auto read_slots = [&](int k) {
+      if constexpr (RB == 4) return *reinterpret_cast<const uint2*>(slot_lane + k * TM * 2);
+      else return uint2{*reinterpret_cast<const uint32_t*>(slot_lane + k * TM * 2), 0u};
+    };
     const uint32_t pa = uint32_t(hw) << 4;  // piece 2 s + hw: offset ^ (pa + 32 s)
     auto load_a = [&](uint2 so, hvec (&a)[2][RB]) {
-      const uint32_t o[RB] = {so.x & 0xFFFFu, so.x >> 16, so.y & 0xFFFFu, so.y >> 16};
+      const uint32_t o4[4] = {so.x & 0xFFFFu, so.x >> 16, so.y & 0xFFFFu, so.y >> 16};
+      uint32_t o[RB];
+#pragma unroll
+      for (int blk = 0; blk < RB; ++blk) o[blk] = o4[blk];
 #pragma unroll
       for (int s = 0; s < 2; ++s)
 #pragma unroll
@@ -1007,9 +1020,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_halo(const RowsArgs p, const 
     }
   } else {
     // Too many distinct neighbours: A fragments straight from global memory.
-    // Row 128 rh + 32 blk + lane % 32: caller row and mask.
-    const int32_t* const pc = reinterpret_cast<const int32_t*>(rec + kPlanCrow) + 128 * rh;
-    const uint32_t* const pm = reinterpret_cast<const uint32_t*>(rec + kPlanMask) + 128 * rh;
+    // Row r0 + 32 blk + lane % 32: caller row and mask.
+    const int32_t* const pc = reinterpret_cast<const int32_t*>(rec + kPlanCrow) + r0;
+    const uint32_t* const pm = reinterpret_cast<const uint32_t*>(rec + kPlanMask) + r0;
     int32_t rr[RB];
     uint32_t rm[RB];
 #pragma unroll
@@ -1059,9 +1072,9 @@ int halo_slots() {
   return slots[dev];
 }
 
-template <bool F16>
+template <bool F16, int WR>
 hipError_t launch_halo(const ConvArgs& a, const uint16_t* wp, const uint16_t* zeros, hipStream_t st) {
-  constexpr int TM = kHaloTM, TN = 128;
+  constexpr int TM = kHaloTM, TN = 64 * (4 / WR);
   const int64_t mt = (a.n + TM - 1) / TM;
   const int nt = (a.c_out + TN - 1) / TN;
   const int64_t items = mt * nt;
@@ -1076,7 +1089,7 @@ hipError_t launch_halo(const ConvArgs& a, const uint16_t* wp, const uint16_t* ze
   }
   RowsArgs p{a.nbr, a.plan, a.order, a.srows, a.mask, a.n, a.x, wp, zeros, a.y, a.epi.bias, a.epi.residual,
              a.epi.act, a.y_dtype == TR_SC_F32 ? 1 : 0, a.c_in, a.c_out, nt};
-  fwd_halo<F16><<<unsigned(hl.full + kHaloParts * hl.split), kThreads, 0, st>>>(p, hl);
+  fwd_halo<F16, WR><<<unsigned(hl.full + kHaloParts * hl.split), kThreads, 0, st>>>(p, hl);
   return hipGetLastError();
 }
 
@@ -1122,7 +1135,8 @@ hipError_t dispatch(const ConvArgs& a, const uint16_t* p, const uint16_t* zeros,
   // Wide layers: 64-row waves halve the LDS reads of weight fragments per
   // multiply (the weight slice is read once per wave). Narrow layers: 32-row
   // waves give twice the workgroups and a third wave per SIMD.
-  if (halo_shape(a.c_in, a.c_out)) return launch_halo<F16>(a, p, zeros, st);
+  if (halo_shape(a.c_in, a.c_out))
+    return a.c_out == 64 ? launch_halo<F16, 4>(a, p, zeros, st) : launch_halo<F16, 2>(a, p, zeros, st);
   if (a.c_out >= 128 && a.c_in >= 256) return launch_rows<4, 8, F16, 1>(a, p, zeros, st);
   if (a.c_out >= 128) return launch_rows<2, 8, F16, 1>(a, p, zeros, st);
   // 64-wide layers over a large voxel set (a decoder level): rows through LDS
