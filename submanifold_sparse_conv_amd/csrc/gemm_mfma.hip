@@ -681,8 +681,9 @@ __device__ __forceinline__ void store_tile32(const RowsArgs& p, const f32x16 (&a
 // does not fit (nh < 0: sparse sets, up to 27 distinct neighbours per voxel)
 // gathers its A fragments from global memory in the same order, so its
 // results are the same bits. Shapes: halo_shape (c_in a multiple of 64 up to
-// 256; c_out 64, 128 or 256). For c_out 64 the item is 256 x 64 and the four
-// waves take 64 rows x 64 columns each (template WR = 4).
+// 256; c_out 32, 64, 128 or 256). For c_out 64 (32) the item is 256 x 64
+// (256 x 32) and the four waves take 64 rows x 64 (32) columns each (template
+// WR = 4, CB = 2 or 1).
 //
 // Work items: blockIdx -> (row tile, column tile) in the plan's launch order;
 // when the last round of workgroups would hold few items (split > 0), each of
@@ -712,7 +713,7 @@ constexpr int kPartNbrAt = 3 * 4 * 16 * 64 + 16 * (32 * 4 + 8);
 template <class H, int CB>
 __device__ __forceinline__ void halo_part(const RowsArgs& p, const unsigned char* rec, int blk, int n0, float* s_red) {
   typedef typename H::vec hvec;
-  static_assert(CB == 2 || CB == 4, "64 or 128 columns");
+  static_assert(CB == 1 || CB == 2 || CB == 4, "32, 64 or 128 columns");
   constexpr int D = 3;  // 27 taps = 9 x D: a tap's load set is k % D in every chunk
   const int c_in = p.c_in, c_out = p.c_out;
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hw = lane >> 5;
@@ -819,14 +820,15 @@ __device__ __forceinline__ void halo_part(const RowsArgs& p, const unsigned char
   }
 }
 
-template <bool F16, int WR>
+template <bool F16, int WR, int CB>
 __global__ __launch_bounds__(kThreads, 2) void fwd_halo(const RowsArgs p, const HaloLaunch hl) {
   typedef Half<F16> H;
   typedef typename H::vec hvec;
-  // WR row groups of waves: 2 (2 x 2 waves, 128 rows x 64 columns each, a
-  // 128-column item) or 4 (4 x 1 waves, 64 rows x 64 columns, a 64-column item)
-  static_assert(WR == 2 || WR == 4, "wave arrangements");
-  constexpr int TM = kHaloTM, RB = 8 / WR, CB = 2, TN = 32 * CB * (4 / WR);
+  // WR row groups of waves, CB 32-column blocks per wave: WR 2, CB 2 (2 x 2
+  // waves, 128 rows x 64 columns each, a 128-column item); WR 4 (4 x 1 waves,
+  // 64 rows x 32 CB columns each, a 32 CB-column item)
+  static_assert((WR == 2 && CB == 2) || (WR == 4 && (CB == 1 || CB == 2)), "wave arrangements");
+  constexpr int TM = kHaloTM, RB = 8 / WR, TN = 32 * CB * (4 / WR);
   constexpr int WROWS = TM / WR;  // rows per wave
   constexpr int KC = kHaloKC, ROWB = kHaloRowBytes;
   constexpr int HBYTES = kHaloCap * ROWB;
@@ -1072,9 +1074,9 @@ int halo_slots() {
   return slots[dev];
 }
 
-template <bool F16, int WR>
+template <bool F16, int WR, int CB>
 hipError_t launch_halo(const ConvArgs& a, const uint16_t* wp, const uint16_t* zeros, hipStream_t st) {
-  constexpr int TM = kHaloTM, TN = 64 * (4 / WR);
+  constexpr int TM = kHaloTM, TN = 32 * CB * (4 / WR);
   const int64_t mt = (a.n + TM - 1) / TM;
   const int nt = (a.c_out + TN - 1) / TN;
   const int64_t items = mt * nt;
@@ -1089,7 +1091,7 @@ hipError_t launch_halo(const ConvArgs& a, const uint16_t* wp, const uint16_t* ze
   }
   RowsArgs p{a.nbr, a.plan, a.order, a.srows, a.mask, a.n, a.x, wp, zeros, a.y, a.epi.bias, a.epi.residual,
              a.epi.act, a.y_dtype == TR_SC_F32 ? 1 : 0, a.c_in, a.c_out, nt};
-  fwd_halo<F16, WR><<<unsigned(hl.full + kHaloParts * hl.split), kThreads, 0, st>>>(p, hl);
+  fwd_halo<F16, WR, CB><<<unsigned(hl.full + kHaloParts * hl.split), kThreads, 0, st>>>(p, hl);
   return hipGetLastError();
 }
 
@@ -1135,8 +1137,11 @@ hipError_t dispatch(const ConvArgs& a, const uint16_t* p, const uint16_t* zeros,
   // Wide layers: 64-row waves halve the LDS reads of weight fragments per
   // multiply (the weight slice is read once per wave). Narrow layers: 32-row
   // waves give twice the workgroups and a third wave per SIMD.
-  if (halo_shape(a.c_in, a.c_out))
-    return a.c_out == 64 ? launch_halo<F16, 4>(a, p, zeros, st) : launch_halo<F16, 2>(a, p, zeros, st);
+  if (halo_shape(a.c_in, a.c_out)) {
+    if (a.c_out == 32) return launch_halo<F16, 4, 1>(a, p, zeros, st);
+    if (a.c_out == 64) return launch_halo<F16, 4, 2>(a, p, zeros, st);
+    return launch_halo<F16, 2, 2>(a, p, zeros, st);
+  }
   if (a.c_out >= 128 && a.c_in >= 256) return launch_rows<4, 8, F16, 1>(a, p, zeros, st);
   if (a.c_out >= 128) return launch_rows<2, 8, F16, 1>(a, p, zeros, st);
   // 64-wide layers over a large voxel set (a decoder level): rows through LDS

@@ -171,12 +171,13 @@ def test_forward_large_64wide_all_rows(c_in, c_out):
     assert err <= TOL["bf16"]
 
 
-@pytest.mark.parametrize("c_in,c_out", [(128, 128), (256, 256), (64, 128)])
+@pytest.mark.parametrize("c_in,c_out", [(128, 128), (256, 256), (64, 128), (64, 64), (128, 32)])
 def test_forward_split_last_round(c_in, c_out):
     # 532 tiles of 256 voxels over surface shells: on a 256-CU device (512
     # workgroup slots of the tile kernel) the last round holds 20 items (40 at
-    # 256 output channels), each run as eight K-split 32-row parts; sampled
-    # rows (about 1 in 17) against the oracle, the split tiles' included
+    # 256 output channels), each run as eight K-split 32-row parts (of 128, 64
+    # or 32 columns); sampled rows (about 1 in 17) against the oracle, the
+    # split tiles' included
     n = 532 * 256 - 37
     rng = np.random.default_rng(c_in * 7 + c_out)
     occ = W.ellipsoid_object(rng, 192, n, 10 * n)
@@ -187,9 +188,9 @@ def test_forward_split_last_round(c_in, c_out):
     say(f"[split last round] n={wl.n} c={c_in}->{c_out} bf16")
     c, x, w = to_dev(wl)
     _, m, y = run_all(c, x, w)
-    nbr = m.nbr.cpu().numpy()
+    nbr = oracle.kernel_map(coords)
     rows = sample_rows(wl.n, 8000, seed=c_in + c_out)
-    np.testing.assert_array_equal(nbr[rows], oracle.kernel_map(coords)[rows])
+    np.testing.assert_array_equal(m.nbr.cpu().numpy()[rows], nbr[rows])
     ref = oracle.forward(nbr, wl.x, wl.w, rows=rows)
     err = max_rel(y.float().cpu().numpy()[rows], ref)
     say(f"    max_rel={err:.3e}")
