@@ -131,7 +131,7 @@ hipError_t launch_pack_weights(const void* w, void* wp, int c_in, int c_out, hip
 // -- one contiguous kilobyte per fragment, the stages of the gather-GEMM
 // (chunk-major, taps in order) at a constant stride.
 inline bool halo_shape(int c_in, int c_out) {
-  return c_in % 64 == 0 && c_in <= 256 && (c_out == 32 || c_out == 64 || c_out == 128 || c_out == 256);
+  return c_in % 64 == 0 && c_in <= 1024 && (c_out == 32 || c_out == 64 || (c_out % 128 == 0 && c_out <= 1024));
 }
 __host__ __device__ inline int64_t frag_weight_offset(int c_in, int c_out) {  // in halves
   return packed_weight_elems(c_in, c_out) + 128;  // after the 256-byte zero block
