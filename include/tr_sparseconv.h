@@ -189,10 +189,14 @@ int tr_sparseconv_forward(const tr_sc_kmap* m, const void* x, const void* w, voi
  * harnesses that forbid allocation). Same arguments, result bits and errors as
  * tr_sparseconv_forward, without the workspace: the packed weights go to a
  * scratch array inside the library, 8 MiB per GPU, held until the process
- * ends; the call itself allocates nothing. Limit: half-precision weights need
- * 27 * c_in * c_out * 2 + 256 bytes <= 8 MiB (c_in * c_out <= 155,339, e.g.
- * 384 x 384), else TR_SC_ERR_WORKSPACE and nothing is enqueued (fp32 reads w in
- * place and has no limit). Every call on one GPU shares that GPU's array:
+ * ends; the call itself allocates nothing. Limit: the packed half-precision
+ * weights, tr_sparseconv_packed_weights_bytes(c_in, c_out, dtype), must fit in
+ * 8 MiB: 27 * c_in * c_out * 2 + 256 bytes, plus a second copy of the
+ * 27 * c_in * c_out * 2 bytes in the halo kernel's fragment order for its
+ * shapes (c_in a multiple of 64 up to 1024; c_out 32, 64 or a multiple of 128
+ * up to 1024). E.g. 256 x 256 (7.1 MB) or 392 x 392 (8.3 MB) fit, 384 x 384
+ * (15.9 MB) does not; else TR_SC_ERR_WORKSPACE and nothing is enqueued (fp32
+ * reads w in place and has no limit). Every call on one GPU shares that GPU's array:
  * calls that overlap in time on one GPU (two streams or threads) race; `stream`
  * must belong to the current device. */
 int tr_sparseconv_forward_noalloc(const tr_sc_kmap* m, const void* x, const void* w, void* y,

@@ -516,7 +516,7 @@ int tr_sparseconv_forward_noalloc(const tr_sc_kmap* m, const void* x, const void
   if (need > kNoAllocScratchBytes)
     return fail(TR_SC_ERR_WORKSPACE,
                 "forward_noalloc: packed weights of %zu bytes exceed the %zu-byte scratch array "
-                "(27 * c_in * c_out * 2 + 256 bytes must fit)",
+                "(the packed weights, tr_sparseconv_packed_weights_bytes, must fit)",
                 need, kNoAllocScratchBytes);
   if (m->n == 0) return TR_SC_OK;
   if (w == nullptr) return fail(TR_SC_ERR_INVALID_ARG, "forward_noalloc: NULL tensor");

@@ -40,24 +40,26 @@ def call_both(coords, c_in, c_out, dtype, seed):
     return wl.n
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
-def test_noalloc_matches_forward_twice(dtype):
+@pytest.mark.parametrize("dtype,c1,c2", [("bf16", (64, 64), (32, 16)), ("f16", (64, 64), (32, 16)),
+                                         ("f32", (8, 8), (3, 5)),
+                                         ("bf16", (128, 128), (64, 32))])  # both halo shapes
+def test_noalloc_matches_forward_twice(dtype, c1, c2):
     rng = np.random.default_rng(91)
     big = W.make("S", with_values=False).coords
     small = W.random_sparse(rng, 700, D=12, B=1)
-    c1 = (64, 64) if dtype != "f32" else (8, 8)
-    c2 = (32, 16) if dtype != "f32" else (3, 5)
     say(f"[noalloc] {dtype}: n={len(big)} c={c1} then n={len(small)} c={c2}")
     call_both(big, c1[0], c1[1], dtype, 5)
     call_both(small, c2[0], c2[1], dtype, 6)
 
 
 def test_noalloc_wide_and_binding():
-    # the largest half shape in range, through the Python binding
+    # the largest shapes in range (a row-gather shape and a halo shape, whose
+    # packing holds a second, fragment-ordered copy), through the Python binding
     rng = np.random.default_rng(92)
     coords = W.random_sparse(rng, 3000, D=16, B=1)
-    say(f"[noalloc] 384 x 384 bf16, n={len(coords)}")
-    call_both(coords, 384, 384, "bf16", 7)
+    say(f"[noalloc] 392 x 392 and 256 x 256 bf16, n={len(coords)}")
+    call_both(coords, 392, 392, "bf16", 7)
+    call_both(coords, 256, 256, "bf16", 9)
     wl = W.custom(coords, 64, 32, "bf16", 8)
     x = torch.from_numpy(wl.x).to(DEV).bfloat16()
     w = torch.from_numpy(wl.w).to(DEV).bfloat16()
