@@ -40,14 +40,12 @@ __global__ __launch_bounds__(kThreads) void pack_weights(const uint16_t* __restr
 // multiples of 8 and 16-byte aligned arrays: a thread moves two 8-channel
 // pieces in, through a 64 x 66 LDS tile (4-byte words, rows 132 bytes apart so
 // that the column reads spread over the banks), and two pieces out.
-__global__ __launch_bounds__(kThreads) void pack_weights_v8(const uint16_t* __restrict__ w,
-                                                            uint16_t* __restrict__ wp, int c_in,
-                                                            int c_out, uint16_t* __restrict__ zeros) {
-  __shared__ uint32_t t[64 * 33];
-  if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && threadIdx.x < 16)
+__device__ __forceinline__ void pack_tile_v8(const uint16_t* __restrict__ w, uint16_t* __restrict__ wp, int c_in,
+                                             int c_out, uint16_t* __restrict__ zeros, int bx, int by, int k,
+                                             uint32_t* t) {
+  if (bx == 0 && by == 0 && k == 0 && threadIdx.x < 16)
     reinterpret_cast<uint4*>(zeros)[threadIdx.x] = make_uint4(0u, 0u, 0u, 0u);
-  const int k = blockIdx.z;
-  const int ci0 = blockIdx.y * 64, co0 = blockIdx.x * 64;
+  const int ci0 = by * 64, co0 = bx * 64;
   const uint16_t* src = w + int64_t(k) * c_in * c_out;
   uint16_t* dst = wp + int64_t(k) * c_in * c_out;
 #pragma unroll
@@ -75,6 +73,52 @@ __global__ __launch_bounds__(kThreads) void pack_weights_v8(const uint16_t* __re
       *reinterpret_cast<uint4*>(dst + int64_t(co) * c_in + ci) = make_uint4(o[0], o[1], o[2], o[3]);
     }
   }
+}
+
+__global__ __launch_bounds__(kThreads) void pack_weights_v8(const uint16_t* __restrict__ w,
+                                                            uint16_t* __restrict__ wp, int c_in,
+                                                            int c_out, uint16_t* __restrict__ zeros) {
+  __shared__ uint32_t t[64 * 33];
+  pack_tile_v8(w, wp, c_in, c_out, zeros, blockIdx.x, blockIdx.y, blockIdx.z, t);
+}
+
+// Fragment piece e of the halo kernel's weight copy (one lane of one
+// fragment, 8 input channels of one output column) gathered from w
+// [27][c_in][c_out]: 8 two-byte loads, consecutive lanes on consecutive columns.
+__device__ __forceinline__ uint4 frag_piece_from_w(const uint16_t* __restrict__ w, int c_in, int c_out, int64_t e) {
+  const int ncb = c_out / 32;
+  const int lane = int(e & 63);
+  int64_t f = e >> 6;
+  const int cb = int(f % ncb);
+  f /= ncb;
+  const int s = int(f & 1);
+  f >>= 1;
+  const int k = int(f % 27);
+  const int c = int(f / 27);
+  const int col = cb * 32 + (lane & 31);
+  const int ci = c * 32 + s * 16 + (lane >> 5) * 8;
+  const uint16_t* src = w + (int64_t(k) * c_in + ci) * c_out + col;
+  uint32_t o[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) o[u] = uint32_t(src[(2 * u) * int64_t(c_out)]) | (uint32_t(src[(2 * u + 1) * int64_t(c_out)]) << 16);
+  return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+// Both layouts of a halo shape in one launch: the first nv8 workgroups pack
+// [27][c_out][c_in] tiles as pack_weights_v8, the rest write the fragment
+// copy straight from w.
+__global__ __launch_bounds__(kThreads) void pack_weights_v8_frag(const uint16_t* __restrict__ w,
+                                                                 uint16_t* __restrict__ wp, int c_in, int c_out,
+                                                                 uint16_t* __restrict__ zeros, uint4* __restrict__ wf,
+                                                                 int nbx, int nby, int nv8, int64_t total) {
+  __shared__ uint32_t t[64 * 33];
+  const int b = blockIdx.x;
+  if (b < nv8) {
+    pack_tile_v8(w, wp, c_in, c_out, zeros, b % nbx, (b / nbx) % nby, b / (nbx * nby), t);
+    return;
+  }
+  for (int64_t e = int64_t(b - nv8) * kThreads + threadIdx.x; e < total; e += int64_t(gridDim.x - nv8) * kThreads)
+    wf[e] = frag_piece_from_w(w, c_in, c_out, e);
 }
 
 // Fragment-order copy: thread = one lane of one fragment, 16 bytes in and out
@@ -116,6 +160,15 @@ hipError_t launch_pack_weights(const void* w, void* wp, int c_in, int c_out, hip
   uint16_t* zeros = dst + packed_weight_elems(c_in, c_out);
   const bool v8 = c_in % 8 == 0 && c_out % 8 == 0 && reinterpret_cast<uintptr_t>(w) % 16 == 0 &&
                   reinterpret_cast<uintptr_t>(wp) % 16 == 0;
+  if (v8 && halo_shape(c_in, c_out)) {
+    const int nbx = int(grid.x), nby = int(grid.y), nv8 = nbx * nby * 27;
+    const int64_t total = int64_t(27) * c_in * c_out / 8;  // 16-byte fragment pieces
+    const int64_t nf = (total + kThreads - 1) / kThreads;
+    pack_weights_v8_frag<<<unsigned(nv8 + (nf < 2048 ? nf : 2048)), kThreads, 0, st>>>(
+        src, dst, c_in, c_out, zeros, reinterpret_cast<uint4*>(dst + frag_weight_offset(c_in, c_out)), nbx, nby, nv8,
+        total);
+    return hipGetLastError();
+  }
   if (v8)
     pack_weights_v8<<<grid, kThreads, 0, st>>>(src, dst, c_in, c_out, zeros);
   else
