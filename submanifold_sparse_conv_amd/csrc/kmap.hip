@@ -16,6 +16,7 @@
 // rows of nbr are written back in caller order through LDS so that
 // consecutive lanes store consecutive words.
 #include "common.h"
+#include "halo_plan.h"
 #include "launch.h"
 
 namespace trsc {
@@ -48,11 +49,14 @@ __device__ inline uint32_t cell_x(int x) { return (uint32_t(x & 1) << 2) | (uint
 __device__ inline uint32_t cell_y(int y) { return (uint32_t(y & 1) << 1) | (uint32_t(y >> 1) << 4); }
 __device__ inline uint32_t cell_z(int z) { return uint32_t(z & 1) | (uint32_t(z >> 1) << 3); }
 
-// Each wave works alone (no workgroup barrier): its LDS region first holds,
-// for each lane, the {bitmap, start} record of each of the 8 blocks around the
-// voxel (record j of lane l at j * 64 + l), which turns the per-tap choice of
-// block into one indexed LDS read; the same bytes then stage the wave's 64 x
-// 27 output rows and their caller rows for the write-back.
+// Each wave works alone until its rows are written (no workgroup barrier): its
+// LDS region first holds, for each lane, the {bitmap, start} record of each of
+// the 8 blocks around the voxel (record j of lane l at j * 64 + l), which turns
+// the per-tap choice of block into one indexed LDS read; the same bytes then
+// stage the wave's 64 x 27 output rows and their caller rows for the
+// write-back. A workgroup's 256 voxels are one tile of the halo gather-GEMM:
+// once every wave is done, the workgroup builds the tile's plan from the
+// neighbour rows it holds in registers (halo_plan.h), in the same LDS.
 //
 // DENSE: the hash was built in a known grid, and the block records come from
 // its occupancy bitmap instead of the table: the word of a neighbour block is
@@ -62,11 +66,17 @@ __device__ inline uint32_t cell_z(int z) { return uint32_t(z & 1) | (uint32_t(z 
 template <bool DENSE>
 __global__ __launch_bounds__(kThreads) void kmap_kernel(const uint64_t* __restrict__ skeys, int64_t n,
                                                         TableRef t, DenseRef d, int32_t* __restrict__ nbr,
-                                                        uint32_t* __restrict__ mask_out) {
+                                                        uint32_t* __restrict__ mask_out,
+                                                        unsigned char* __restrict__ plan,
+                                                        uint16_t* __restrict__ costs) {
   constexpr int kWaves = kThreads / 64;
+  static_assert(kThreads == kPlanThreads, "a workgroup's voxels are one halo tile");
   static_assert(64 * 27 * 4 + 64 * 4 <= 8 * 64 * 16, "staged rows fit in the record region");
-  __shared__ uint4 lds[kWaves][8 * 64];
-  __shared__ uint32_t s_cpre[kThreads];  // DENSE: first sorted position of each bitmap chunk
+  // LDS: the waves' record regions and the bitmap chunk prefixes, then the plan
+  constexpr int kMapLds = kWaves * 8 * 64 * 16 + kThreads * 4;
+  __shared__ __attribute__((aligned(16))) unsigned char s_u[kMapLds > kPlanLdsBytes ? kMapLds : kPlanLdsBytes];
+  uint4 (*const lds)[8 * 64] = reinterpret_cast<uint4 (*)[8 * 64]>(s_u);
+  uint32_t* const s_cpre = reinterpret_cast<uint32_t*>(s_u + kWaves * 8 * 64 * 16);  // DENSE: first sorted position of each bitmap chunk
   if constexpr (DENSE) {
     if (int(threadIdx.x) < d.nchunks) s_cpre[threadIdx.x] = d.cpre[threadIdx.x];
     __syncthreads();
@@ -75,14 +85,19 @@ __global__ __launch_bounds__(kThreads) void kmap_kernel(const uint64_t* __restri
   uint4* rec = lds[wave];
   int32_t* res = reinterpret_cast<int32_t*>(lds[wave]);  // [64][27]: odd stride, conflict-free
   int32_t* rows = res + 64 * 27;
-  const int64_t base = int64_t(xcd_remap(blockIdx.x, gridDim.x)) * kThreads + wave * 64;
-  if (base >= n) return;
+  const int64_t tile = xcd_remap(blockIdx.x, gridDim.x);
+  const int64_t base = tile * kThreads + wave * 64;
   const int64_t s = base + lane;
   const uint32_t tmask = t.hdr->cap_mask, tshift = t.hdr->shift;
   int32_t got[27];
+  uint32_t msk = 0;
+  int32_t me = -1;
+#pragma unroll
+  for (int k = 0; k < 27; ++k) got[k] = -1;
+  if (base < n) {
   if (s < n) {
     const uint64_t key = skeys[s];
-    const int32_t me = t.srows[s];
+    me = t.srows[s];
     const uint64_t bkey = key >> 6;
     // In-block coordinates (0..3) and, per axis, the side on which the 3x3x3
     // neighbourhood leaves the block (0: stays inside).
@@ -181,7 +196,7 @@ __global__ __launch_bounds__(kThreads) void kmap_kernel(const uint64_t* __restri
     const uint32_t cx[3] = {cell_x((lx + 3) & 3), cell_x(lx), cell_x((lx + 1) & 3)};
     const uint32_t cy[3] = {cell_y((ly + 3) & 3), cell_y(ly), cell_y((ly + 1) & 3)};
     const uint32_t cz[3] = {cell_z((lz + 3) & 3), cell_z(lz), cell_z((lz + 1) & 3)};
-    uint32_t msk = 0;
+    msk = 0;
     int32_t spos[27];
 #pragma unroll
     for (int k = 0; k < 27; ++k) {
@@ -226,6 +241,11 @@ __global__ __launch_bounds__(kThreads) void kmap_kernel(const uint64_t* __restri
     const int v = e / 27;
     nbr[int64_t(rows[v]) * 27 + (e - v * 27)] = res[e];
   }
+  }
+  // the tile's plan, once every wave has read its staged rows
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __syncthreads();
+  halo_plan_tile(tile, s < n, msk, me, got, plan, costs, s_u);
 }
 
 constexpr int kGroupThreads = 1024;
@@ -325,16 +345,15 @@ hipError_t launch_kmap(const uint64_t* skeys, int64_t n, const TableRef& t, cons
                        int32_t* order, hipStream_t st) {
   if (n > 0) {
     const unsigned grid = unsigned((n + kThreads - 1) / kThreads);
+    static_assert(kThreads == kHaloTM, "one workgroup per halo tile");
     if (dense != nullptr)
-      kmap_kernel<true><<<grid, kThreads, 0, st>>>(skeys, n, t, *dense, nbr, mask);
+      kmap_kernel<true><<<grid, kThreads, 0, st>>>(skeys, n, t, *dense, nbr, mask, plan, costs);
     else
-      kmap_kernel<false><<<grid, kThreads, 0, st>>>(skeys, n, t, DenseRef{}, nbr, mask);
+      kmap_kernel<false><<<grid, kThreads, 0, st>>>(skeys, n, t, DenseRef{}, nbr, mask, plan, costs);
     group_rows<<<unsigned((n + kGroupWindow - 1) / kGroupWindow), kGroupThreads, 0, st>>>(t.srows, mask, n,
                                                                                          grows, gmask);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const hipError_t e2 = launch_halo_plan(t.srows, mask, nbr, n, plan, costs, st);
-    if (e2 != hipSuccess) return e2;
     return launch_halo_order(costs, halo_tiles(n), order, st);
   }
   return hipGetLastError();

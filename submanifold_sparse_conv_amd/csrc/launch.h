@@ -92,8 +92,6 @@ hipError_t launch_halo_order(const uint16_t* costs, int64_t tiles, int32_t* orde
 hipError_t launch_kmap(const uint64_t* skeys, int64_t n, const TableRef& t, const DenseRef* dense, int32_t* nbr,
                        uint32_t* mask, int32_t* grows, uint32_t* gmask, unsigned char* plan, uint16_t* costs,
                        int32_t* order, hipStream_t st);
-hipError_t launch_halo_plan(const int32_t* srows, const uint32_t* mask, const int32_t* nbr, int64_t n,
-                            unsigned char* plan, uint16_t* costs, hipStream_t st);
 
 // Forward kernels. `srows` is the row order of the tiles (position -> caller
 // row), `mask` the 27-bit neighbour mask of the voxel at each position.
