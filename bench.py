@@ -30,7 +30,7 @@ PEAK_FP32_VECTOR_TFLOPS = 157.3  # MI355X fp32 vector (256 CUs, 2.4 GHz)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fwd_mfma.json")
 # the gather-GEMM kernel and the headers it includes: counters taken on other sources are stale
 GEMM_SOURCES = [os.path.join(ROOT, "submanifold_sparse_conv_amd", "csrc", f)
-                for f in ("gemm_mfma.hip", "common.h", "launch.h", "halo_plan.hip")]
+                for f in ("gemm_mfma.hip", "common.h", "launch.h", "halo_plan.h")]
 
 WORKLOAD_NAMES = {
     "T": "16^3 sphere shell (radius 6, thickness 1), C 8->8 fp32",

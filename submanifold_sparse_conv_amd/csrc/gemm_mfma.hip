@@ -11,6 +11,12 @@
 // voxel's caller index. No atomics, fixed (tap, channel) order: results are
 // the same bit for bit on every run.
 //
+// Two families of kernels. fwd_halo (below, the shapes of halo_shape: half
+// features, C_in a multiple of 64 up to 1024, C_out 32, 64 or a multiple of
+// 128) stages each 256-voxel tile's distinct neighbour rows in LDS once per
+// 32-channel chunk and reads every tap's operand from there, following a plan
+// the kernel map builds per tile. fwd_rows / fwd_lds take the other shapes:
+//
 // K loop: the taps some row of the tile needs (OR of the rows' 27-bit
 // neighbour masks), each split into 64-channel chunks ("stages"). Each of the
 // four waves owns 16*FM whole rows of the tile and all TN columns, so every
@@ -653,7 +659,7 @@ __device__ __forceinline__ void store_tile32(const RowsArgs& p, const f32x16 (&a
 // from global memory. Over a thin surface the halo holds ~1.75 rows per voxel
 // against ~17.7 gathered ones. The plan (tile order, halo rows, the LDS
 // offset of every (row, tap)'s row, which 32-row blocks have which taps) comes
-// from the kernel map (halo_plan).
+// from the kernel map (halo_plan.h).
 //
 // Matrix instruction v_mfma_f32_32x32x16 (bf16 / fp16): on gfx950 it sustains
 // ~97 % of the matrix peak from two waves per SIMD, where 16x16x32 stays near
