@@ -72,7 +72,8 @@ def run_case(coords, c_in, c_out, w_t, x_t, y_t, act, use_bias, use_res, seed, r
 
 EPILOGUES = [("none", False, False), ("relu", True, False), ("silu", True, True), ("none", False, True)]
 TYPES = [(w, x, y) for w in ("bf16", "f16") for x in (w, "f32") for y in (w, "f32")]
-SHAPES = [(64, 64), (32, 96), (16, 8), (128, 136), (64, 24)]  # one shape per output-tile width
+SHAPES = [(64, 64), (32, 96), (16, 8), (128, 136), (64, 24),  # one shape per output-tile width
+          (64, 32), (128, 128)]  # the halo kernel's 32- and 128-column items
 
 
 @pytest.mark.parametrize("w_t,x_t,y_t", TYPES)
