@@ -50,10 +50,13 @@ __device__ inline int slot_index(int r) { return (r >> 7) * 128 + (r & 31) * 4 +
 // The plan of tile `tile` (items tile * kHaloTM + tid): thread tid brings its item's
 // validity, 27-bit neighbour mask m, caller row cr and the caller rows of its
 // 27 neighbours jv (-1: absent). Every thread of the 256-thread workgroup
-// calls it; `lds` is kPlanLdsBytes of LDS no other code uses meanwhile.
+// calls it; `lds` is kPlanLdsBytes of LDS no other code uses meanwhile. The
+// tile order is also the row order of the row-gather kernels and the weight
+// gradient: grows / gmask at the tile's positions.
 __device__ __forceinline__ void halo_plan_tile(int64_t tile, bool valid, uint32_t m, int32_t cr,
                                                const int32_t (&jv)[27], unsigned char* __restrict__ plan,
-                                               uint16_t* __restrict__ costs, unsigned char* lds) {
+                                               uint16_t* __restrict__ costs, int32_t* __restrict__ grows,
+                                               uint32_t* __restrict__ gmask, unsigned char* lds) {
   int32_t* const tab = reinterpret_cast<int32_t*>(lds + kPlanTabAt);
   int16_t* const s_slot = reinterpret_cast<int16_t*>(lds + kPlanSlotAt);
   uint32_t (*const cnt)[256] = reinterpret_cast<uint32_t (*)[256]>(lds + kPlanCntAt);
@@ -114,6 +117,10 @@ __device__ __forceinline__ void halo_plan_tile(int64_t tile, bool valid, uint32_
   const int sx = slot_index(r);
   reinterpret_cast<int32_t*>(rec + kPlanCrow)[r] = cr;
   reinterpret_cast<uint32_t*>(rec + kPlanMask)[r] = m;
+  if (valid) {  // valid items take the tile's first positions: t0 + r < n
+    grows[tile * kHaloTM + r] = cr;
+    gmask[tile * kHaloTM + r] = m;
+  }
   s_pmask[r] = m;
 
   // (2) The item's neighbours inserted into the table: every first probe

@@ -68,7 +68,8 @@ __global__ __launch_bounds__(kThreads) void kmap_kernel(const uint64_t* __restri
                                                         TableRef t, DenseRef d, int32_t* __restrict__ nbr,
                                                         uint32_t* __restrict__ mask_out,
                                                         unsigned char* __restrict__ plan,
-                                                        uint16_t* __restrict__ costs) {
+                                                        uint16_t* __restrict__ costs, int32_t* __restrict__ grows,
+                                                        uint32_t* __restrict__ gmask) {
   constexpr int kWaves = kThreads / 64;
   static_assert(kThreads == kPlanThreads, "a workgroup's voxels are one halo tile");
   static_assert(64 * 27 * 4 + 64 * 4 <= 8 * 64 * 16, "staged rows fit in the record region");
@@ -245,97 +246,7 @@ __global__ __launch_bounds__(kThreads) void kmap_kernel(const uint64_t* __restri
   // the tile's plan, once every wave has read its staged rows
   __builtin_amdgcn_s_waitcnt(0xC07F);
   __syncthreads();
-  halo_plan_tile(tile, s < n, msk, me, got, plan, costs, s_u);
-}
-
-constexpr int kGroupThreads = 1024;
-
-// Row order of the gather-GEMM: inside each window of kGroupWindow Morton-
-// consecutive voxels, a stable counting sort by octant pattern. Tiles of
-// consecutive rows then hold voxels on the same side of the surface, whose
-// neighbour masks overlap more, so fewer taps are multiplied by zero rows.
-// (Which tile a voxel lands in does not change its output row.)
-__global__ __launch_bounds__(kGroupThreads) void group_rows(const int32_t* __restrict__ srows,
-                                                            const uint32_t* __restrict__ mask, int64_t n,
-                                                            int32_t* __restrict__ grows,
-                                                            uint32_t* __restrict__ gmask) {
-  constexpr int WAVES = kGroupThreads / 64;
-  constexpr int PER = kGroupWindow / kGroupThreads;
-  static_assert(PER * kGroupThreads == kGroupWindow, "window = whole passes of the workgroup");
-  // cnt[it][wave][d]: keys with pattern d among the lanes of (item it, wave);
-  // turned in place into their first output position.
-  __shared__ uint32_t cnt[PER][WAVES][256];
-  __shared__ uint32_t s_tmp[4];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t w0 = int64_t(blockIdx.x) * kGroupWindow;
-  const int64_t w1 = w0 + kGroupWindow < n ? w0 + kGroupWindow : n;
-  // The window's masks and rows, loaded once (all loads in flight together).
-  uint32_t mv[PER];
-  int32_t rv[PER];
-#pragma unroll
-  for (int it = 0; it < PER; ++it) {
-    const int64_t t = w0 + it * kGroupThreads + tid;
-    mv[it] = t < w1 ? mask[t] : 0u;
-    rv[it] = t < w1 ? srows[t] : 0;
-  }
-  for (int q = tid; q < PER * WAVES * 256; q += kGroupThreads) (&cnt[0][0][0])[q] = 0u;
-  __syncthreads();
-  // Rank every item among the equal patterns of its (item, wave) with ballots;
-  // the first lane of each pattern stores the count.
-  const unsigned long long lt = (1ull << lane) - 1ull;
-  uint32_t dg[PER], rank[PER];
-#pragma unroll
-  for (int it = 0; it < PER; ++it) {
-    const bool valid = w0 + it * kGroupThreads + tid < w1;
-    const uint32_t d = octant_key(mv[it]);
-    unsigned long long peers = __ballot(valid);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const bool bit = (d >> j) & 1u;
-      const unsigned long long bal = __ballot(bit);
-      peers &= bit ? bal : ~bal;
-    }
-    dg[it] = d;
-    rank[it] = valid ? __popcll(peers & lt) : ~0u;
-    if (valid && (peers & lt) == 0) cnt[it][wave][d] = __popcll(peers);
-  }
-  __syncthreads();
-  // Thread d < 256 owns pattern d: its total, the exclusive scan of the totals
-  // over the patterns (four waves), then its positions in (item, wave) order.
-  uint32_t tot = 0, excl = 0;
-  if (tid < 256) {
-#pragma unroll
-    for (int it = 0; it < PER; ++it)
-      for (int w = 0; w < WAVES; ++w) tot += cnt[it][w][tid];
-    uint32_t x = tot;
-    for (int o = 1; o < 64; o <<= 1) {
-      const uint32_t y = __shfl_up(x, o, 64);
-      if (lane >= o) x += y;
-    }
-    excl = x - tot;
-    if (lane == 63) s_tmp[wave] = x;
-  }
-  __syncthreads();
-  if (tid < 256) {
-    uint32_t run = excl;
-    for (int w = 0; w < wave; ++w) run += s_tmp[w];
-#pragma unroll
-    for (int it = 0; it < PER; ++it)
-      for (int w = 0; w < WAVES; ++w) {
-        const uint32_t v = cnt[it][w][tid];
-        cnt[it][w][tid] = run;
-        run += v;
-      }
-  }
-  __syncthreads();
-#pragma unroll
-  for (int it = 0; it < PER; ++it) {
-    if (rank[it] != ~0u) {
-      const uint32_t pos = cnt[it][wave][dg[it]] + rank[it];
-      grows[w0 + pos] = rv[it];
-      gmask[w0 + pos] = mv[it];
-    }
-  }
+  halo_plan_tile(tile, s < n, msk, me, got, plan, costs, grows, gmask, s_u);
 }
 
 }  // namespace
@@ -347,11 +258,9 @@ hipError_t launch_kmap(const uint64_t* skeys, int64_t n, const TableRef& t, cons
     const unsigned grid = unsigned((n + kThreads - 1) / kThreads);
     static_assert(kThreads == kHaloTM, "one workgroup per halo tile");
     if (dense != nullptr)
-      kmap_kernel<true><<<grid, kThreads, 0, st>>>(skeys, n, t, *dense, nbr, mask, plan, costs);
+      kmap_kernel<true><<<grid, kThreads, 0, st>>>(skeys, n, t, *dense, nbr, mask, plan, costs, grows, gmask);
     else
-      kmap_kernel<false><<<grid, kThreads, 0, st>>>(skeys, n, t, DenseRef{}, nbr, mask, plan, costs);
-    group_rows<<<unsigned((n + kGroupWindow - 1) / kGroupWindow), kGroupThreads, 0, st>>>(t.srows, mask, n,
-                                                                                         grows, gmask);
+      kmap_kernel<false><<<grid, kThreads, 0, st>>>(skeys, n, t, DenseRef{}, nbr, mask, plan, costs, grows, gmask);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     return launch_halo_order(costs, halo_tiles(n), order, st);

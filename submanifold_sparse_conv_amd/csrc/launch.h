@@ -43,9 +43,8 @@ hipError_t launch_dense_hash(const int32_t* coords, int64_t n, int g, int batch,
                              hipStream_t st);
 
 // Kernel map (nbr, caller order; mask, Morton order) and the gather-GEMM row
-// order: grows / gmask = Morton order regrouped inside windows of kGroupWindow
-// voxels by the octant pattern of the neighbour mask.
-constexpr int kGroupWindow = 4096;
+// order: grows / gmask = Morton order regrouped inside each kHaloTM-voxel tile
+// by the octant pattern of the neighbour mask (the halo plan's tile order).
 
 // Halo plan of the gather-GEMM over tiles of kHaloTM Morton-consecutive voxels:
 // per tile, the rows in tile order (octant-regrouped inside the tile), the
