@@ -155,7 +155,10 @@ size_t tr_sparseconv_kmap_workspace_bytes(int64_t n);
  *           neighbour of voxel i at tap k, or -1. nbr[i*27 + 13] = i.
  *           Owned by the caller; the kernel map reads it in every forward.
  * workspace device buffer >= tr_sparseconv_kmap_workspace_bytes(n) bytes
- *           (per-voxel neighbour masks in Morton order); must outlive the handle.
+ *           (per-voxel neighbour masks in Morton order, the gather-GEMM's row
+ *           order, and per tile of 256 Morton-consecutive voxels the plan of
+ *           the halo gather-GEMM: 20,480 bytes, plus the tiles' launch order);
+ *           must outlive the handle.
  * out       receives a new handle (release with tr_sparseconv_kmap_destroy). */
 int tr_sparseconv_build_kernel_map(const tr_sc_hash* h, int32_t* nbr, void* workspace,
                                    size_t ws_bytes, void* stream, tr_sc_kmap** out);
