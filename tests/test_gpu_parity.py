@@ -172,21 +172,24 @@ def test_forward_large_64wide_all_rows(c_in, c_out):
     assert err <= TOL["bf16"]
 
 
-@pytest.mark.parametrize("c_in,c_out", [(128, 128), (256, 256), (64, 128), (64, 64), (128, 32)])
-def test_forward_split_last_round(c_in, c_out):
-    # 532 tiles of 256 voxels over surface shells: on a 256-CU device (512
-    # workgroup slots of the tile kernel) the last round holds 20 items (40 at
-    # 256 output channels), each run as eight K-split 32-row parts (of 128, 64
-    # or 32 columns); sampled rows (about 1 in 17) against the oracle, the
-    # split tiles' included
-    n = 532 * 256 - 37
+@pytest.mark.parametrize("c_in,c_out,tiles", [(128, 128, 532), (256, 256, 532), (64, 128, 532), (64, 64, 532),
+                                               (128, 32, 532), (128, 128, 600), (256, 256, 600), (64, 128, 600)])
+def test_forward_split_last_round(c_in, c_out, tiles):
+    # tiles of 256 voxels over surface shells. On a 256-CU device (512
+    # workgroup slots of the tile kernel), at 532 tiles the last round holds 20
+    # items (40 at 256 output channels), each run as eight K-split 32-row parts
+    # (of 128, 64 or 32 columns); at 600 tiles it holds 88 (176) 128-column
+    # items, too many for their parts to fit at once, so they run whole.
+    # Sampled rows (about 1 in 17) against the oracle, the last round's tiles
+    # included
+    n = tiles * 256 - 37
     rng = np.random.default_rng(c_in * 7 + c_out)
     occ = W.ellipsoid_object(rng, 192, n, 10 * n)
     coords = np.argwhere(occ).astype(np.int32)
     coords = coords[rng.permutation(len(coords))[:n]]
     coords = np.concatenate([np.zeros((n, 1), np.int32), coords], axis=1)
     wl = W.custom(coords, c_in, c_out, "bf16", seed=c_in + c_out)
-    say(f"[split last round] n={wl.n} c={c_in}->{c_out} bf16")
+    say(f"[split last round] n={wl.n} tiles={tiles} c={c_in}->{c_out} bf16")
     c, x, w = to_dev(wl)
     _, m, y = run_all(c, x, w)
     nbr = oracle.kernel_map(coords)
